@@ -1,0 +1,191 @@
+"""Benchmark of the GDN spec-verify layer step on one MI355X.
+
+One step = one gdn_spec_attention call (conv + ring roll, gates, norms, the
+gated delta rule with per-token state snapshots) over the Qwen3-Next-shaped
+batch: 64 spec rows, K=3 tokens each, 16 k-heads / 32 v-heads, dk=dv=128,
+fp32 states in a 512-slot pool.  Steps cycle over several independent layers
+(each with its own pools and inputs, as consecutive GDN layers of a model
+have), so no step finds the previous step's states in the last-level cache.
+
+Prints one JSON line: tokens/s, us per layer, achieved HBM bandwidth of the
+kernel against the 8 TB/s MI355X peak, and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN layer tokens/sec + us/layer + % HBM peak, spec verify K=3, batch 64"
+HBM_PEAK_GBS = 8000.0
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_gdn_rows_qwen3next_k3_b64.json")
+
+
+def algorithmic_bytes(case) -> int:
+    """Bytes the spec step must move, counted from the batch's metadata."""
+    d, sp = case["dims"], case["spec"]
+    Hk, Hv, dk, dv, W, L = d["Hk"], d["Hv"], d["dk"], d["dv"], d["W"], d["L"]
+    C = 2 * Hk * dk + Hv * dv
+    T = sp["num_spec_tokens"]
+    tile = Hv * dv * dk * 4
+    total = T * C * 2 + 2 * T * Hv * 2 + T * Hv * dv * 2      # qkv, a+b, out
+    total += C * W * 2 + 2 * Hv * 4                            # conv weight, A_log, dt_bias
+    sq, ssi, nacc = sp["spec_query_start_loc"], sp["spec_state_indices"], sp["num_accepted_tokens"]
+    for b in range(sp["num_spec_decodes"]):
+        Tb = int(sq[b + 1] - sq[b])
+        n = int(nacc[b])
+        cs = int(sp["spec_cache_indices"][b]) if sp.get("spec_cache_indices") is not None \
+            else int(ssi[b][0])
+        if cs > 0:
+            read_cols = set(range(n - 1, n - 1 + W - 1)) | set(range(n, n + max(L - Tb, 0)))
+            total += (len(read_cols) + L) * C * 2               # ring read + rewrite
+        if ssi[b][n - 1] > 0:
+            total += tile                                       # state load
+        total += sum(tile for t in range(Tb) if ssi[b][t] > 0)  # per-token stores
+    total += 4 * (sp["num_spec_decodes"] + 1) + 4 * ssi.size + 4 * sp["num_spec_decodes"]
+    if sp.get("spec_token_indx") is not None:
+        total += 4 * T
+    return int(total)
+
+
+def cpu_baseline(case, rows=16):
+    """The oracle (single-threaded C, fp64) on the first ``rows`` spec rows."""
+    import oracle  # test infrastructure: the baseline leg only
+    from tests.gpu_util import sub_spec
+    from tests.helpers import clone
+    sp = sub_spec(case["spec"], list(range(rows)))
+    c = clone(case)
+    out = np.zeros((case["num_actual_tokens"], case["dims"]["Hv"], case["dims"]["dv"]), np.uint16)
+    t0 = time.perf_counter()
+    oracle.spec_step(case["dims"], c, sp, out)
+    dt = time.perf_counter() - t0
+    return {"value": sp["num_spec_tokens"] / dt, "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{rows} of {case['spec']['num_spec_decodes']} spec rows "
+                      f"({sp['num_spec_tokens']} tokens) of the same batch, one thread, "
+                      f"{dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--workload", default="qwen3next_k3_b64")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the GDN step shards heads and rows with no "
+              "exchange, so there is no multi-GPU path to time here", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import speculative_decoding_causal_amd as gdn
+    import synth
+    from tests.gpu_util import bf, f32, i32
+
+    case = synth.make_case(args.workload, seed=args.seed)
+    d, sp = case["dims"], case["spec"]
+    cfg = gdn.GdnConfig(d["Hk"], d["Hv"], d["dk"], d["dv"], d["W"], d["activation"],
+                        d["use_qk_l2norm"], d["eps"], d["scale"])
+    dev = torch.device("cuda:0")
+    T = sp["num_spec_tokens"]
+    meta = dict(sqsl=i32(sp["spec_query_start_loc"]), ssi=i32(sp["spec_state_indices"]),
+                nacc=i32(sp["num_accepted_tokens"]), tix=i32(sp.get("spec_token_indx")),
+                cache=i32(sp.get("spec_cache_indices")))
+    conv0, ssm0 = bf(case["conv_state"]), f32(case["ssm_state"])
+    w, A_log, dt_bias = bf(case["conv_weight"]), f32(case["A_log"]), f32(case["dt_bias"])
+    layers = []
+    g = torch.Generator(device="cpu").manual_seed(args.seed)
+    for li in range(args.layers):
+        perm = torch.randperm(case["num_actual_tokens"], generator=g)
+        qkv = bf(case["mixed_qkv"])[perm.to(dev)].contiguous()
+        layers.append(dict(qkv=qkv, a=bf(case["a"]), b=bf(case["b"]),
+                           conv=conv0.clone(), ssm=ssm0.clone(),
+                           out=torch.empty(case["num_actual_tokens"], d["Hv"], d["dv"],
+                                           dtype=torch.bfloat16, device=dev)))
+    del conv0, ssm0
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        L = layers[i % len(layers)]
+        gdn.gdn_spec_attention(cfg, L["qkv"], L["a"], L["b"], w, None, A_log, dt_bias,
+                               L["conv"], L["ssm"], meta["sqsl"], meta["ssi"], meta["nacc"],
+                               L["out"], spec_cache_indices=meta["cache"],
+                               spec_token_indx=meta["tix"], num_spec_tokens=T, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(args.warmup + i)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_per_step = total_ms / args.steps
+    avg_launch_s = float(launch_ms.mean()) * 1e-3
+    nbytes = algorithmic_bytes(case)
+    achieved = nbytes / avg_launch_s / 1e9
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        with open(PROFILE_TRAFFIC) as f:
+            traffic = json.load(f).get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "us_per_layer": ms_per_step * 1e3,
+        "hbm_frac_of_peak": achieved / HBM_PEAK_GBS,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "spec_rows": sp["num_spec_decodes"], "K": sp["K"],
+                   "tokens_per_step": T, "num_k_heads": d["Hk"], "num_v_heads": d["Hv"],
+                   "head_k_dim": d["dk"], "head_v_dim": d["dv"], "conv_width": d["W"],
+                   "state_len": d["L"], "num_slots": d["num_slots"],
+                   "layers_cycled": args.layers, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "gdn_rows_kernel<128,128>",
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": avg_launch_s * 1e6,
+                     "p10_launch_us": float(np.percentile(launch_ms, 10)) * 1e3,
+                     "p90_launch_us": float(np.percentile(launch_ms, 90)) * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,263 @@
+/*
+ * gdn.h - C ABI of the MI355X (gfx950) Gated DeltaNet attention step with
+ * speculative-decoding support.
+ *
+ * The step has two stages per token:
+ *   1. a depthwise causal conv1d of width W over the packed projections
+ *      mixed_qkv = [q (Hk*dk) | k (Hk*dk) | v (Hv*dv)], reading W-1 samples of
+ *      history from a per-sequence conv-state ring and rolling that ring;
+ *   2. the gated delta rule (Yang, Kautz, Hatamizadeh, "Gated Delta
+ *      Networks", ICLR 2025) on an fp32 state S in R^{dv x dk} per v-head:
+ *        alpha = exp(-exp(A_log) * softplus(a + dt_bias)),  beta = sigmoid(b)
+ *        S <- alpha S ;  u = beta (v - S k) ;  S <- S + u k^T ;  o = scale S q
+ *      with q and k L2-normalised over dk (optional) and v-head h reading
+ *      k-head h / (Hv/Hk).
+ *
+ * Speculative-decoding semantics follow three web pages:
+ *   [P1] "[GDN] Spec-decoding-aware attention kernel" (vllm-xpu-kernels
+ *        pull request 336), sections "Problem" and "Changes";
+ *   [P2] "[XE2] Support MTP of QWEN model" (vllm-xpu-kernels pull request
+ *        368): the overview (spec/non-spec token streams, token_indx
+ *        remapping), the automated review of the interface (optional tensors
+ *        checked before use) and the squashed commit message (ragged spec
+ *        rows; the conservation check is kept, the rectangular one dropped);
+ *   [P3] "[Bugfix] Align Qwen GDN gates with speculative tokens" (vLLM pull
+ *        request 51812), "Purpose": gates are read through the same indices
+ *        as mixed_qkv.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers, row-major and contiguous.
+ *    bf16 values are passed as their 16-bit patterns (gdn_bf16).  Integers
+ *    are int32; has_initial_state is one byte per row.
+ *  - The caller owns every buffer, including the workspace.  The library
+ *    keeps no pointer after returning and allocates no device memory.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    with no host synchronisation; faults inside kernels surface at the
+ *    caller's next synchronisation.
+ *  - Every call validates its host-side arguments BEFORE enqueuing anything:
+ *    on error it returns a negative status, touches no buffer, and
+ *    gdn_last_error() describes the problem.  Metadata VALUES that live in
+ *    device memory (slots, n_acc, token rows) are not read by the host; the
+ *    kernels clamp them so that out-of-range values never cause an
+ *    out-of-range access (results are then unspecified).  gdn_check_metadata_host
+ *    checks them on host copies.
+ *  - Pools: conv_state [num_slots, state_len, C] bf16 (channel-contiguous
+ *    ring, column 0 oldest); ssm_state [num_slots, Hv, dv, dk] fp32.  A slot
+ *    value <= 0 is NULL_BLOCK_ID / pad slot: nothing is read (zeros are used)
+ *    and nothing is written [P1 "Changes"; P2 review thread].  Rows of one
+ *    call must use disjoint slots.
+ *  - core_attn_out [num_actual_tokens, Hv, dv] bf16: only rows named by a
+ *    token_indx (or the identity mapping) are written.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t gdn_bf16;
+typedef void* gdn_stream_t; /* hipStream_t */
+
+/* Status codes. */
+enum {
+  GDN_OK = 0,
+  GDN_ERR_NULL = -1,             /* a required pointer is NULL */
+  GDN_ERR_DIMS = -2,             /* inconsistent sizes or counts */
+  GDN_ERR_SPEC_PAIR = -3,        /* only one of spec_state_indices /
+                                    num_accepted_tokens given [P1 "Changes"] */
+  GDN_ERR_MISSING_OPTIONAL = -4, /* an optional tensor needed by the batch is
+                                    absent [P2 interface review] */
+  GDN_ERR_CONSERVATION = -5,     /* non-spec + spec tokens != num_actual_tokens
+                                    [P2 commit message] */
+  GDN_ERR_WORKSPACE = -6,        /* workspace NULL or too small */
+  GDN_ERR_HIP = -7,              /* a HIP launch failed */
+  GDN_ERR_UNSUPPORTED = -8,      /* shape outside what the kernels support */
+  GDN_ERR_METADATA = -9          /* gdn_check_metadata_host found a violation */
+};
+
+/* Layer shape.  Supported by the kernels: head_k_dim == head_v_dim in
+ * {16, 32, 64, 128}; 1 <= conv_width <= 4; conv_width-1 <= state_len <= 16;
+ * num_v_heads a multiple of num_k_heads with (Hv/Hk)*head_v_dim <= 1024. */
+typedef struct gdn_dims {
+  int32_t num_k_heads;   /* Hk */
+  int32_t num_v_heads;   /* Hv */
+  int32_t head_k_dim;    /* dk */
+  int32_t head_v_dim;    /* dv */
+  int32_t conv_width;    /* W */
+  int32_t state_len;     /* L: ring columns per conv slot (the pool's dim 1) */
+  int32_t num_slots;     /* slots in each pool (dim 0) */
+  int32_t activation;    /* conv activation: 0 identity, 1 SiLU */
+  int32_t use_qk_l2norm; /* 1: q, k <- x / sqrt(sum x^2 + l2norm_eps) */
+  float l2norm_eps;
+  float scale;           /* multiplies q after normalisation (o = scale S q) */
+} gdn_dims;
+
+/* Largest tokens per row in a spec call (K) and per decode row. */
+#define GDN_MAX_ROW_TOKENS 16
+
+/*
+ * gdn_spec_attention - one spec-verify step over `num_spec_decodes` rows.
+ *
+ * Row b owns tokens [spec_query_start_loc[b], spec_query_start_loc[b+1]) of
+ * the spec token stream, 1 <= T_b <= max_spec_len (ragged rows allowed; no
+ * rectangular assumption [P2 commit message]).  Stream token j lives at
+ * global row spec_token_indx[j] (identity when NULL) of mixed_qkv, a, b and
+ * core_attn_out [P2 overview; P3 "Purpose"].
+ *
+ * Conv [P1 "Changes"]: slot cs = spec_cache_indices[b] (NULL -> column 0 of
+ * spec_state_indices, the column-0 contract).  With n = num_accepted_tokens[b]
+ * the window is ring columns n-1 .. n+W-3 followed by the row's inputs; the
+ * ring becomes columns n .. n+L-T_b-1 of the pre-state followed by the T_b
+ * inputs (stage, then roll; sole writer per slot and channel).
+ * SSM [P1 "Changes"]: initial state from slot spec_state_indices[b][n-1];
+ * the state after token t is stored to spec_state_indices[b][t].
+ * Preconditions (unchecked on device): 1 <= n <= T_b, n+W-2 <= L.
+ *
+ *   mixed_qkv      [num_actual_tokens, C]  C = 2*Hk*dk + Hv*dv
+ *   a, b           [num_actual_tokens, Hv]
+ *   conv_weight    [C, W]; conv_bias [C] or NULL
+ *   A_log, dt_bias [Hv] fp32
+ *   spec_state_indices [num_spec_decodes, max_spec_len] (row stride max_spec_len)
+ *   num_accepted_tokens [num_spec_decodes]
+ *   num_spec_tokens = spec_query_start_loc[num_spec_decodes] (host copy)
+ *
+ * num_spec_decodes == 0 is a no-op that returns GDN_OK.
+ */
+int gdn_spec_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
+                       const gdn_bf16* a, const gdn_bf16* b,
+                       const gdn_bf16* conv_weight, const gdn_bf16* conv_bias,
+                       const float* A_log, const float* dt_bias,
+                       gdn_bf16* conv_state, float* ssm_state,
+                       int32_t num_actual_tokens, int32_t num_spec_decodes,
+                       int32_t num_spec_tokens, int32_t max_spec_len,
+                       const int32_t* spec_query_start_loc,
+                       const int32_t* spec_cache_indices,
+                       const int32_t* spec_state_indices,
+                       const int32_t* num_accepted_tokens,
+                       const int32_t* spec_token_indx,
+                       gdn_bf16* core_attn_out, gdn_stream_t stream);
+
+/*
+ * gdn_attention - a whole layer step over a batch that may mix non-spec rows
+ * (decodes, then prefills) and spec rows [P2 overview: the two token
+ * streams; P1 "Changes": the spec tensors are optional and absent means the
+ * non-spec behaviour].
+ *
+ * Non-spec rows: num_decodes one-token rows first, then num_prefills rows;
+ * row i owns non-spec stream tokens [query_start_loc[i], query_start_loc[i+1])
+ * at global rows non_spec_token_indx[j] (identity when NULL).  Slot
+ * c = non_spec_state_indices[i] serves both pools; the history is read when
+ * has_initial_state[i] != 0 (all rows when NULL) and c > 0.  The conv window
+ * is the ring tail, the ring rolls by T_i, and only the final state is stored
+ * (when c > 0).  Prefill rows run the chunked form of the recurrence.
+ *
+ * Spec rows: exactly as gdn_spec_attention.  spec_state_indices and
+ * num_accepted_tokens must be given together or not at all (GDN_ERR_SPEC_PAIR).
+ *
+ * Checks: num_non_spec_tokens + num_spec_tokens == num_actual_tokens
+ * (GDN_ERR_CONSERVATION); when both streams are non-empty both token_indx
+ * tensors are required.  Prefill rows need a workspace of
+ * gdn_workspace_bytes(dims, num_non_spec_tokens, num_prefills) bytes.
+ */
+int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
+                  const gdn_bf16* a, const gdn_bf16* b,
+                  const gdn_bf16* conv_weight, const gdn_bf16* conv_bias,
+                  const float* A_log, const float* dt_bias,
+                  gdn_bf16* conv_state, float* ssm_state,
+                  int32_t num_actual_tokens,
+                  int32_t num_decodes, int32_t num_prefills,
+                  int32_t num_non_spec_tokens,
+                  const int32_t* query_start_loc,
+                  const int32_t* non_spec_state_indices,
+                  const uint8_t* has_initial_state,
+                  const int32_t* non_spec_token_indx,
+                  int32_t num_spec_decodes, int32_t num_spec_tokens,
+                  int32_t max_spec_len,
+                  const int32_t* spec_query_start_loc,
+                  const int32_t* spec_cache_indices,
+                  const int32_t* spec_state_indices,
+                  const int32_t* num_accepted_tokens,
+                  const int32_t* spec_token_indx,
+                  gdn_bf16* core_attn_out, void* workspace,
+                  size_t workspace_bytes, gdn_stream_t stream);
+
+/* Bytes of workspace gdn_attention needs for a batch whose non-spec stream
+ * has at most max_non_spec_tokens tokens, of which max_prefill_rows rows are
+ * prefills.  0 when no prefill row is present. */
+size_t gdn_workspace_bytes(const gdn_dims* dims, int32_t max_non_spec_tokens,
+                           int32_t max_prefill_rows);
+
+/*
+ * Row batch for the stage entry points.  kind = GDN_ROWS_SPEC uses the spec
+ * fields (state_indices is [num_rows, max_row_tokens], num_accepted_tokens,
+ * cache_indices optional); kind = GDN_ROWS_NON_SPEC uses cache_indices and
+ * has_initial_state (optional), one state store per row.  Stage entry
+ * points take rows of at most GDN_MAX_ROW_TOKENS tokens.
+ */
+enum { GDN_ROWS_NON_SPEC = 0, GDN_ROWS_SPEC = 1 };
+typedef struct gdn_rows {
+  int32_t kind;
+  int32_t num_rows;
+  int32_t num_tokens;       /* = query_start_loc[num_rows] */
+  int32_t max_row_tokens;   /* spec: row stride of state_indices */
+  const int32_t* query_start_loc;
+  const int32_t* cache_indices;
+  const int32_t* state_indices;
+  const int32_t* num_accepted_tokens;
+  const uint8_t* has_initial_state;
+  const int32_t* token_indx;
+} gdn_rows;
+
+/* Stage entry points (the conv and the delta rule as separate ops).
+ * gdn_conv_only runs the conv with the rows' window rule, rolls the rings and
+ * writes the fp32 conv output of each token to conv_out[global row][C].
+ * gdn_delta_rule_only reads conv_out at the same rows and runs gates, norms
+ * and the recurrence with the rows' slot rule.  Calling the two in order
+ * gives bit-for-bit the result of the fused entry points. */
+int gdn_conv_only(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
+                  const gdn_bf16* conv_weight, const gdn_bf16* conv_bias,
+                  gdn_bf16* conv_state, int32_t num_actual_tokens,
+                  const gdn_rows* rows, float* conv_out, gdn_stream_t stream);
+int gdn_delta_rule_only(const gdn_dims* dims, const float* conv_out,
+                        const gdn_bf16* a, const gdn_bf16* b,
+                        const float* A_log, const float* dt_bias,
+                        float* ssm_state, int32_t num_actual_tokens,
+                        const gdn_rows* rows, gdn_bf16* core_attn_out,
+                        gdn_stream_t stream);
+
+/*
+ * gdn_check_metadata_host - validate metadata VALUES on host copies of the
+ * tensors (same meaning as in gdn_attention; any group may be absent by
+ * passing 0 rows).  Checks: query_start_loc starts at 0 and is
+ * non-decreasing; decode rows hold one token; spec rows hold 1..max_spec_len
+ * tokens; 1 <= n_acc <= T_b and n_acc + W - 2 <= state_len; slots
+ * < num_slots; token rows in [0, num_actual_tokens) and distinct across both
+ * streams; slots of different rows disjoint.  Returns GDN_OK or
+ * GDN_ERR_METADATA (with gdn_last_error() naming the first violation).
+ */
+int gdn_check_metadata_host(const gdn_dims* dims, int32_t num_actual_tokens,
+                            int32_t num_decodes, int32_t num_prefills,
+                            const int32_t* query_start_loc,
+                            const int32_t* non_spec_state_indices,
+                            const int32_t* non_spec_token_indx,
+                            int32_t num_spec_decodes, int32_t max_spec_len,
+                            const int32_t* spec_query_start_loc,
+                            const int32_t* spec_cache_indices,
+                            const int32_t* spec_state_indices,
+                            const int32_t* num_accepted_tokens,
+                            const int32_t* spec_token_indx);
+
+/* Human-readable status; never NULL. */
+const char* gdn_status_string(int status);
+/* Message of the last failing call on this thread ("" if none). */
+const char* gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

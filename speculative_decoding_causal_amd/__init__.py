@@ -1,0 +1,348 @@
+"""MI355X-native Gated DeltaNet attention step with speculative decoding.
+
+Thin ctypes binding over ``libgdn.so`` (HIP kernels for gfx950 behind a C
+ABI declared in ``include/gdn.h``).  This module only marshals arguments:
+dtype / contiguity / device checks, sizes derived from tensor shapes, the
+current HIP stream.  Every step of the computation runs in the library's
+kernels; there is no CPU fallback, and importing fails loudly when the
+library has not been built.
+
+Entry points (same names as the C ABI):
+  gdn_spec_attention, gdn_attention, gdn_workspace_bytes, gdn_conv_only,
+  gdn_delta_rule_only, gdn_check_metadata_host, gdn_status_string,
+  gdn_last_error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with "
+        "`python speculative_decoding_causal_amd/build.py` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+GDN_OK = 0
+GDN_ERR_NULL = -1
+GDN_ERR_DIMS = -2
+GDN_ERR_SPEC_PAIR = -3
+GDN_ERR_MISSING_OPTIONAL = -4
+GDN_ERR_CONSERVATION = -5
+GDN_ERR_WORKSPACE = -6
+GDN_ERR_HIP = -7
+GDN_ERR_UNSUPPORTED = -8
+GDN_ERR_METADATA = -9
+GDN_ROWS_NON_SPEC = 0
+GDN_ROWS_SPEC = 1
+MAX_ROW_TOKENS = 16
+
+EXPORTED_SYMBOLS = (
+    "gdn_spec_attention", "gdn_attention", "gdn_workspace_bytes",
+    "gdn_conv_only", "gdn_delta_rule_only", "gdn_check_metadata_host",
+    "gdn_status_string", "gdn_last_error",
+)
+
+
+class GdnDims(ctypes.Structure):
+    _fields_ = [
+        ("num_k_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
+        ("head_k_dim", ctypes.c_int32), ("head_v_dim", ctypes.c_int32),
+        ("conv_width", ctypes.c_int32), ("state_len", ctypes.c_int32),
+        ("num_slots", ctypes.c_int32), ("activation", ctypes.c_int32),
+        ("use_qk_l2norm", ctypes.c_int32), ("l2norm_eps", ctypes.c_float),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class GdnRows(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32), ("num_rows", ctypes.c_int32),
+        ("num_tokens", ctypes.c_int32), ("max_row_tokens", ctypes.c_int32),
+        ("query_start_loc", ctypes.c_void_p), ("cache_indices", ctypes.c_void_p),
+        ("state_indices", ctypes.c_void_p), ("num_accepted_tokens", ctypes.c_void_p),
+        ("has_initial_state", ctypes.c_void_p), ("token_indx", ctypes.c_void_p),
+    ]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_lib.gdn_spec_attention.argtypes = [ctypes.POINTER(GdnDims)] + [_P] * 9 + [_I] * 4 + [_P] * 6 + [_P]
+_lib.gdn_spec_attention.restype = ctypes.c_int
+_lib.gdn_attention.argtypes = ([ctypes.POINTER(GdnDims)] + [_P] * 9 + [_I] * 4 + [_P] * 4 +
+                               [_I] * 3 + [_P] * 5 + [_P, _P, ctypes.c_size_t, _P])
+_lib.gdn_attention.restype = ctypes.c_int
+_lib.gdn_workspace_bytes.argtypes = [ctypes.POINTER(GdnDims), _I, _I]
+_lib.gdn_workspace_bytes.restype = ctypes.c_size_t
+_lib.gdn_conv_only.argtypes = [ctypes.POINTER(GdnDims), _P, _P, _P, _P, _I,
+                               ctypes.POINTER(GdnRows), _P, _P]
+_lib.gdn_conv_only.restype = ctypes.c_int
+_lib.gdn_delta_rule_only.argtypes = [ctypes.POINTER(GdnDims), _P, _P, _P, _P, _P, _P, _I,
+                                     ctypes.POINTER(GdnRows), _P, _P]
+_lib.gdn_delta_rule_only.restype = ctypes.c_int
+_lib.gdn_check_metadata_host.argtypes = [ctypes.POINTER(GdnDims), _I, _I, _I, _P, _P, _P,
+                                         _I, _I, _P, _P, _P, _P, _P]
+_lib.gdn_check_metadata_host.restype = ctypes.c_int
+_lib.gdn_status_string.argtypes = [ctypes.c_int]
+_lib.gdn_status_string.restype = ctypes.c_char_p
+_lib.gdn_last_error.argtypes = []
+_lib.gdn_last_error.restype = ctypes.c_char_p
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = gdn_last_error()
+        super().__init__(f"{where}: {gdn_status_string(status)} ({status}): {msg}")
+
+
+def gdn_status_string(status: int) -> str:
+    return _lib.gdn_status_string(int(status)).decode()
+
+
+def gdn_last_error() -> str:
+    return _lib.gdn_last_error().decode()
+
+
+@dataclass
+class GdnConfig:
+    """Layer shape; ``state_len`` and ``num_slots`` come from the pools."""
+    num_k_heads: int
+    num_v_heads: int
+    head_k_dim: int
+    head_v_dim: int
+    conv_width: int = 4
+    activation: int = 1          # 0 identity, 1 SiLU
+    use_qk_l2norm: int = 1
+    l2norm_eps: float = 1e-6
+    scale: float | None = None   # default head_k_dim ** -0.5
+
+    @property
+    def conv_dim(self) -> int:
+        return 2 * self.num_k_heads * self.head_k_dim + self.num_v_heads * self.head_v_dim
+
+    def dims(self, conv_state: torch.Tensor | None = None,
+             state_len: int | None = None, num_slots: int | None = None) -> GdnDims:
+        if conv_state is not None:
+            num_slots, state_len = int(conv_state.shape[0]), int(conv_state.shape[1])
+        scale = self.head_k_dim ** -0.5 if self.scale is None else self.scale
+        return GdnDims(self.num_k_heads, self.num_v_heads, self.head_k_dim,
+                       self.head_v_dim, self.conv_width, int(state_len),
+                       int(num_slots), self.activation, self.use_qk_l2norm,
+                       float(self.l2norm_eps), float(scale))
+
+
+def _ptr(t, dtype=None, name="tensor", device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the kernels read device memory)")
+    return t.data_ptr()
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_I32 = torch.int32
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check_pools(cfg: GdnConfig, conv_state, ssm_state):
+    if conv_state.dim() != 3 or conv_state.shape[2] != cfg.conv_dim:
+        raise ValueError(f"conv_state must be [num_slots, state_len, {cfg.conv_dim}]")
+    want = (conv_state.shape[0], cfg.num_v_heads, cfg.head_v_dim, cfg.head_k_dim)
+    if tuple(ssm_state.shape) != want:
+        raise ValueError(f"ssm_state must be {list(want)}, got {list(ssm_state.shape)}")
+
+
+def _host_count(x, given):
+    if given is not None:
+        return int(given)
+    return int(x[-1].item())  # synchronises; pass the count to avoid it
+
+
+def gdn_spec_attention(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias,
+                       A_log, dt_bias, conv_state, ssm_state,
+                       spec_query_start_loc, spec_state_indices,
+                       num_accepted_tokens, core_attn_out,
+                       spec_cache_indices=None, spec_token_indx=None,
+                       num_spec_tokens: int | None = None, stream=None) -> None:
+    """One spec-verify step (see ``include/gdn.h``); pools are updated in
+    place and ``core_attn_out`` [num_actual_tokens, Hv, dv] is written at the
+    rows named by ``spec_token_indx``."""
+    dev = mixed_qkv.device
+    _check_pools(cfg, conv_state, ssm_state)
+    dims = cfg.dims(conv_state)
+    Ns = int(spec_query_start_loc.shape[0]) - 1 if spec_query_start_loc is not None else 0
+    K = int(spec_state_indices.shape[1]) if spec_state_indices is not None else 1
+    T = _host_count(spec_query_start_loc, num_spec_tokens) if Ns > 0 else 0
+    rc = _lib.gdn_spec_attention(
+        ctypes.byref(dims), _ptr(mixed_qkv, _BF16, "mixed_qkv", dev), _ptr(a, _BF16, "a", dev),
+        _ptr(b, _BF16, "b", dev), _ptr(conv_weight, _BF16, "conv_weight", dev),
+        _ptr(conv_bias, _BF16, "conv_bias", dev), _ptr(A_log, torch.float32, "A_log", dev),
+        _ptr(dt_bias, torch.float32, "dt_bias", dev), _ptr(conv_state, _BF16, "conv_state", dev),
+        _ptr(ssm_state, torch.float32, "ssm_state", dev), int(mixed_qkv.shape[0]), Ns, T, K,
+        _ptr(spec_query_start_loc, _I32, "spec_query_start_loc", dev),
+        _ptr(spec_cache_indices, _I32, "spec_cache_indices", dev),
+        _ptr(spec_state_indices, _I32, "spec_state_indices", dev),
+        _ptr(num_accepted_tokens, _I32, "num_accepted_tokens", dev),
+        _ptr(spec_token_indx, _I32, "spec_token_indx", dev),
+        _ptr(core_attn_out, _BF16, "core_attn_out", dev), _stream(stream))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_spec_attention")
+
+
+def gdn_workspace_bytes(cfg: GdnConfig, state_len: int, num_slots: int,
+                        max_non_spec_tokens: int, max_prefill_rows: int) -> int:
+    dims = cfg.dims(state_len=state_len, num_slots=num_slots)
+    return int(_lib.gdn_workspace_bytes(ctypes.byref(dims), int(max_non_spec_tokens),
+                                        int(max_prefill_rows)))
+
+
+def gdn_attention(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias, A_log,
+                  dt_bias, conv_state, ssm_state, core_attn_out, *,
+                  num_decodes=0, num_prefills=0, num_non_spec_tokens=0,
+                  query_start_loc=None, non_spec_state_indices=None,
+                  has_initial_state=None, non_spec_token_indx=None,
+                  spec_query_start_loc=None, spec_state_indices=None,
+                  num_accepted_tokens=None, spec_cache_indices=None,
+                  spec_token_indx=None, num_spec_tokens=None, workspace=None,
+                  stream=None) -> None:
+    """A layer step over a batch of non-spec rows (decodes, then prefills)
+    and spec rows.  ``workspace`` (uint8 device tensor) is needed when
+    ``num_prefills > 0``; size it with ``gdn_workspace_bytes``."""
+    dev = mixed_qkv.device
+    _check_pools(cfg, conv_state, ssm_state)
+    dims = cfg.dims(conv_state)
+    Ns = int(spec_query_start_loc.shape[0]) - 1 if spec_query_start_loc is not None else 0
+    K = int(spec_state_indices.shape[1]) if spec_state_indices is not None else 1
+    Ts = _host_count(spec_query_start_loc, num_spec_tokens) if Ns > 0 else 0
+    ws_ptr = _ptr(workspace, None, "workspace", dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib.gdn_attention(
+        ctypes.byref(dims), _ptr(mixed_qkv, _BF16, "mixed_qkv", dev), _ptr(a, _BF16, "a", dev),
+        _ptr(b, _BF16, "b", dev), _ptr(conv_weight, _BF16, "conv_weight", dev),
+        _ptr(conv_bias, _BF16, "conv_bias", dev), _ptr(A_log, torch.float32, "A_log", dev),
+        _ptr(dt_bias, torch.float32, "dt_bias", dev), _ptr(conv_state, _BF16, "conv_state", dev),
+        _ptr(ssm_state, torch.float32, "ssm_state", dev), int(mixed_qkv.shape[0]),
+        int(num_decodes), int(num_prefills), int(num_non_spec_tokens),
+        _ptr(query_start_loc, _I32, "query_start_loc", dev),
+        _ptr(non_spec_state_indices, _I32, "non_spec_state_indices", dev),
+        _ptr(has_initial_state, (torch.uint8, torch.bool), "has_initial_state", dev),
+        _ptr(non_spec_token_indx, _I32, "non_spec_token_indx", dev),
+        Ns, Ts, K,
+        _ptr(spec_query_start_loc, _I32, "spec_query_start_loc", dev),
+        _ptr(spec_cache_indices, _I32, "spec_cache_indices", dev),
+        _ptr(spec_state_indices, _I32, "spec_state_indices", dev),
+        _ptr(num_accepted_tokens, _I32, "num_accepted_tokens", dev),
+        _ptr(spec_token_indx, _I32, "spec_token_indx", dev),
+        _ptr(core_attn_out, _BF16, "core_attn_out", dev), ws_ptr, ctypes.c_size_t(ws_bytes),
+        _stream(stream))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_attention")
+
+
+def _rows(kind, query_start_loc, num_tokens, max_row_tokens, cache_indices=None,
+          state_indices=None, num_accepted_tokens=None, has_initial_state=None,
+          token_indx=None, dev=None) -> GdnRows:
+    n = int(query_start_loc.shape[0]) - 1
+    return GdnRows(int(kind), n, int(num_tokens), int(max_row_tokens),
+                   _ptr(query_start_loc, _I32, "query_start_loc", dev),
+                   _ptr(cache_indices, _I32, "cache_indices", dev),
+                   _ptr(state_indices, _I32, "state_indices", dev),
+                   _ptr(num_accepted_tokens, _I32, "num_accepted_tokens", dev),
+                   _ptr(has_initial_state, (torch.uint8, torch.bool), "has_initial_state", dev),
+                   _ptr(token_indx, _I32, "token_indx", dev))
+
+
+def gdn_conv_only(cfg: GdnConfig, mixed_qkv, conv_weight, conv_bias, conv_state,
+                  conv_out, kind, query_start_loc, num_tokens, max_row_tokens,
+                  cache_indices=None, state_indices=None, num_accepted_tokens=None,
+                  has_initial_state=None, token_indx=None, stream=None) -> None:
+    dev = mixed_qkv.device
+    dims = cfg.dims(conv_state)
+    rows = _rows(kind, query_start_loc, num_tokens, max_row_tokens, cache_indices,
+                 state_indices, num_accepted_tokens, has_initial_state, token_indx, dev)
+    rc = _lib.gdn_conv_only(ctypes.byref(dims), _ptr(mixed_qkv, _BF16, "mixed_qkv", dev),
+                            _ptr(conv_weight, _BF16, "conv_weight", dev),
+                            _ptr(conv_bias, _BF16, "conv_bias", dev),
+                            _ptr(conv_state, _BF16, "conv_state", dev), int(mixed_qkv.shape[0]),
+                            ctypes.byref(rows), _ptr(conv_out, torch.float32, "conv_out", dev),
+                            _stream(stream))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_conv_only")
+
+
+def gdn_delta_rule_only(cfg: GdnConfig, conv_out, a, b, A_log, dt_bias, ssm_state,
+                        core_attn_out, kind, query_start_loc, num_tokens, max_row_tokens,
+                        cache_indices=None, state_indices=None, num_accepted_tokens=None,
+                        has_initial_state=None, token_indx=None, state_len=None,
+                        stream=None) -> None:
+    dev = conv_out.device
+    dims = cfg.dims(state_len=state_len if state_len is not None else cfg.conv_width - 1,
+                    num_slots=int(ssm_state.shape[0]))
+    rows = _rows(kind, query_start_loc, num_tokens, max_row_tokens, cache_indices,
+                 state_indices, num_accepted_tokens, has_initial_state, token_indx, dev)
+    rc = _lib.gdn_delta_rule_only(
+        ctypes.byref(dims), _ptr(conv_out, torch.float32, "conv_out", dev),
+        _ptr(a, _BF16, "a", dev), _ptr(b, _BF16, "b", dev),
+        _ptr(A_log, torch.float32, "A_log", dev), _ptr(dt_bias, torch.float32, "dt_bias", dev),
+        _ptr(ssm_state, torch.float32, "ssm_state", dev), int(conv_out.shape[0]),
+        ctypes.byref(rows), _ptr(core_attn_out, _BF16, "core_attn_out", dev), _stream(stream))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_delta_rule_only")
+
+
+def _np_ptr(x):
+    if x is None:
+        return None
+    x = np.ascontiguousarray(x, dtype=np.int32)
+    return x, x.ctypes.data
+
+
+def gdn_check_metadata_host(cfg: GdnConfig, state_len: int, num_slots: int,
+                            num_actual_tokens: int, *, num_decodes=0, num_prefills=0,
+                            query_start_loc=None, non_spec_state_indices=None,
+                            non_spec_token_indx=None, spec_query_start_loc=None,
+                            spec_cache_indices=None, spec_state_indices=None,
+                            num_accepted_tokens=None, spec_token_indx=None) -> int:
+    """Check metadata values on host (numpy) copies; returns the status and
+    raises nothing (``gdn_last_error()`` explains a failure)."""
+    dims = cfg.dims(state_len=state_len, num_slots=num_slots)
+    keep = []
+
+    def p(x):
+        r = _np_ptr(x)
+        if r is None:
+            return None
+        keep.append(r[0])
+        return r[1]
+
+    Ns = 0 if spec_query_start_loc is None else len(spec_query_start_loc) - 1
+    K = 1 if spec_state_indices is None else np.asarray(spec_state_indices).shape[1]
+    return int(_lib.gdn_check_metadata_host(
+        ctypes.byref(dims), int(num_actual_tokens), int(num_decodes), int(num_prefills),
+        p(query_start_loc), p(non_spec_state_indices), p(non_spec_token_indx), int(Ns), int(K),
+        p(spec_query_start_loc), p(spec_cache_indices), p(spec_state_indices),
+        p(num_accepted_tokens), p(spec_token_indx)))

@@ -1,0 +1,65 @@
+// Device helpers shared by the HIP kernels: bf16 conversion, lane
+// reductions, gates.  gfx950 (CDNA4, wave64) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+__device__ __forceinline__ float bf2f(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// DPP lane moves within a row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF,
+                                      0xF, false));
+}
+
+// Sum over groups of LPR consecutive lanes (LPR in 1,2,4,8,16); every lane
+// of a group ends with the same bits (each step adds a commutative pair).
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (LPR >= 2) v += dpp_mov<0xB1>(v);   // quad_perm 1,0,3,2
+  if constexpr (LPR >= 4) v += dpp_mov<0x4E>(v);   // quad_perm 2,3,0,1
+  if constexpr (LPR >= 8) v += dpp_mov<0x141>(v);  // row_half_mirror
+  if constexpr (LPR >= 16) v += dpp_mov<0x140>(v); // row_mirror
+  return v;
+}
+
+// Butterfly sum over the 64 lanes of a wave; all lanes get the same bits.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Decay alpha = exp(-exp(A_log) * softplus(a + dt_bias)) and write strength
+// beta = sigmoid(b) of one (token, v-head).
+__device__ __forceinline__ void gate_pair(float a, float b, float A_log,
+                                          float dt_bias, float* alpha,
+                                          float* beta) {
+  float x = a + dt_bias;
+  float sp = x > 20.f ? x : log1pf(expf(x));
+  *alpha = expf(-expf(A_log) * sp);
+  *beta = 1.f / (1.f + expf(-b));
+}
+
+__device__ __forceinline__ float silu(float x) { return x / (1.f + expf(-x)); }
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) {
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
+}  // namespace gdn

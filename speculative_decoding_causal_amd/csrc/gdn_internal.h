@@ -1,0 +1,86 @@
+// Internal interface between the C-ABI layer (gdn_api.cpp) and the HIP
+// kernels.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kThreads = 256;        // threads per workgroup (4 wave64)
+constexpr int kMaxRowTokens = 16;    // tokens per row in the fused kernel
+constexpr int kMaxStateLen = 16;
+constexpr int kMaxWidth = 4;
+
+enum RowKind : int { kNonSpec = 0, kSpec = 1 };
+enum Stage : int { kFused = 0, kConvOnly = 1, kDeltaOnly = 2 };
+
+// Everything one launch of the row kernel needs, passed by value.
+struct RowArgs {
+  // shape
+  int Hk, Hv, G, C, L, W, num_slots, act, l2norm;
+  float eps, scale;
+  int num_actual_tokens;
+  // layer tensors
+  const uint16_t* qkv;
+  const uint16_t* a;
+  const uint16_t* b;
+  const uint16_t* conv_w;
+  const uint16_t* conv_b;
+  const float* A_log;
+  const float* dt_bias;
+  uint16_t* conv_pool;
+  float* ssm_pool;
+  uint16_t* out;
+  float* y;  // conv output, [num_actual_tokens, C] (stage entry points)
+  // rows
+  int kind;
+  int num_rows;
+  int num_tokens;      // tokens of the stream the rows index
+  int row_stride;      // spec: row stride of ssi
+  int max_row_tokens;  // tokens processed per row at most (LDS sizing)
+  const int* qsl;
+  const int* cache_idx;
+  const int* ssi;
+  const int* nacc;
+  const uint8_t* his;
+  const int* tix;
+  int stage;
+};
+
+// Rows of at most kMaxRowTokens tokens (spec rows and decodes), one
+// workgroup per (row, k-head): conv + ring roll, gates, norms, recurrence.
+hipError_t launch_rows(const RowArgs& a, int dk, int dv, hipStream_t s);
+size_t rows_lds_bytes(const RowArgs& a, int dk, int dv);
+
+// Long non-spec rows (prefills): conv over the whole row into a workspace,
+// then the delta rule over the row.
+struct PrefillArgs {
+  int Hk, Hv, G, C, L, W, num_slots, act, l2norm;
+  float eps, scale;
+  int num_actual_tokens;
+  const uint16_t* qkv;
+  const uint16_t* a;
+  const uint16_t* b;
+  const uint16_t* conv_w;
+  const uint16_t* conv_b;
+  const float* A_log;
+  const float* dt_bias;
+  uint16_t* conv_pool;
+  float* ssm_pool;
+  uint16_t* out;
+  int num_rows;        // prefill rows
+  int stream_tokens;   // tokens of the non-spec stream (workspace capacity)
+  int max_row_len;     // upper bound on tokens per prefill row
+  const int* qsl;      // [num_rows+1], non-spec stream indices
+  const int* cache_idx;
+  const uint8_t* his;
+  const int* tix;
+  void* workspace;
+};
+size_t prefill_workspace_bytes(int Hk, int Hv, int dk, int dv,
+                               int stream_tokens, int rows);
+hipError_t launch_prefill(const PrefillArgs& a, int dk, int dv, hipStream_t s);
+
+}  // namespace gdn

@@ -1,0 +1,318 @@
+// Non-spec prefill rows (rows of any length).
+//
+// Three launches on the caller's stream:
+//   1. conv_prefill: one thread per (channel, 64-token segment of a row)
+//      slides the width-W window along the row and writes the fp32 conv
+//      output to the workspace at the token's non-spec stream index.  The
+//      thread of segment 0 is the only one that reads the ring history (the
+//      window of the row's first tokens) and it alone rolls the ring by T
+//      afterwards, so reads of the pre-state precede the writes.
+//   2. prep_prefill: per token, the q/k L2 norms (wave reductions, q scaled)
+//      are applied in place in the workspace, k.q is kept, and the gates of
+//      every v-head are evaluated at the token's global row.
+//   3. delta_prefill: one workgroup per (row, v-head, block of 32 state rows)
+//      carries its state rows in VGPRs across the whole row; the per-token
+//      operands are staged in LDS 32 tokens at a time.  The final state is
+//      stored to the row's slot.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kSeg = 64;    // tokens per conv thread
+constexpr int kChunk = 32;  // tokens staged per LDS refill in the recurrence
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+struct WsLayout {
+  size_t y, kq, ga, gb, total;
+};
+
+WsLayout ws_layout(int Hk, int Hv, int dk, int dv, int stream_tokens) {
+  const size_t C = 2ull * Hk * dk + (size_t)Hv * dv;
+  const size_t n = stream_tokens > 0 ? (size_t)stream_tokens : 0;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  WsLayout w;
+  size_t o = 0;
+  w.y = o;  o += al(n * C * 4);
+  w.kq = o; o += al(n * Hk * 4);
+  w.ga = o; o += al(n * Hv * 4);
+  w.gb = o; o += al(n * Hv * 4);
+  w.total = o;
+  return w;
+}
+
+__device__ __forceinline__ int slot_or_null(int s, int num_slots) {
+  return (s > 0 && s < num_slots) ? s : 0;
+}
+
+struct PrefillRow {
+  int j0, T, slot;
+  bool init;
+};
+
+__device__ __forceinline__ PrefillRow prefill_row(const PrefillArgs& p, int row) {
+  PrefillRow r;
+  r.j0 = clampi(p.qsl[row], 0, p.stream_tokens);
+  int j1 = clampi(p.qsl[row + 1], r.j0, p.stream_tokens);
+  r.T = j1 - r.j0;
+  r.slot = slot_or_null(p.cache_idx[row], p.num_slots);
+  r.init = (p.his ? p.his[row] != 0 : true) && r.slot > 0;
+  return r;
+}
+
+__device__ __forceinline__ int global_row(const PrefillArgs& p, int j) {
+  int r = p.tix ? p.tix[j] : j;
+  return (r >= 0 && r < p.num_actual_tokens) ? r : -1;
+}
+
+__global__ void __launch_bounds__(kThreads)
+conv_prefill_kernel(PrefillArgs p, float* __restrict__ y) {
+  const int C = p.C, L = p.L, W = p.W;
+  const int c = blockIdx.y * kThreads + threadIdx.x;
+  if (c >= C) return;
+  const PrefillRow pr = prefill_row(p, blockIdx.z);
+  const int base = blockIdx.x * kSeg;
+  if (base >= pr.T) return;
+  const int end = min(pr.T, base + kSeg);
+  const uint16_t* ring = p.conv_pool + (size_t)pr.slot * L * C + c;
+
+  // Input at row position t; t < 0 reads ring column L + t (history).
+  auto xin = [&](int t) -> uint16_t {
+    if (t >= 0) {
+      int r = global_row(p, pr.j0 + t);
+      return r >= 0 ? p.qkv[(size_t)r * C + c] : (uint16_t)0;
+    }
+    return pr.init ? ring[(size_t)(L + t) * C] : (uint16_t)0;
+  };
+
+  float w[kMaxWidth];
+#pragma unroll
+  for (int m = 0; m < kMaxWidth; ++m) w[m] = m < W ? bf2f(p.conv_w[(size_t)c * W + m]) : 0.f;
+  const float wlast = bf2f(p.conv_w[(size_t)c * W + W - 1]);
+  const float bias = p.conv_b ? bf2f(p.conv_b[c]) : 0.f;
+  float win[kMaxWidth];  // win[m] = input at t - (W-1) + m, m < W-1
+#pragma unroll
+  for (int m = 0; m < kMaxWidth - 1; ++m)
+    win[m] = m < W - 1 ? bf2f(xin(base - (W - 1) + m)) : 0.f;
+  for (int t = base; t < end; ++t) {
+    const float xt = bf2f(xin(t));
+    float acc = bias;
+#pragma unroll
+    for (int m = 0; m < kMaxWidth - 1; ++m)
+      if (m < W - 1) acc = fmaf(w[m], win[m], acc);
+    acc = fmaf(wlast, xt, acc);
+    if (p.act) acc = silu(acc);
+    y[(size_t)(pr.j0 + t) * C + c] = acc;
+#pragma unroll
+    for (int m = 0; m < kMaxWidth - 2; ++m)
+      if (m < W - 2) win[m] = win[m + 1];
+    if (W >= 2) {
+#pragma unroll
+      for (int m = 0; m < kMaxWidth - 1; ++m)
+        if (m == W - 2) win[m] = xt;
+    }
+  }
+  // Roll: new column l <- (history ++ inputs)[T + l].  Column T + l is read
+  // before column l is written, and only this thread touches the channel.
+  if (blockIdx.x == 0 && pr.slot > 0) {
+    uint16_t* wr = p.conv_pool + (size_t)pr.slot * L * C + c;
+    for (int l = 0; l < L; ++l) {
+      int src = pr.T + l;
+      uint16_t v = src < L ? (pr.init ? wr[(size_t)src * C] : (uint16_t)0) : xin(src - L);
+      wr[(size_t)l * C] = v;
+    }
+  }
+}
+
+template <int DK>
+__global__ void __launch_bounds__(kThreads)
+prep_prefill_kernel(PrefillArgs p, float* __restrict__ y, float* __restrict__ kq,
+                    float* __restrict__ ga, float* __restrict__ gb) {
+  const int j = blockIdx.x;
+  const int lo = clampi(p.qsl[0], 0, p.stream_tokens);
+  const int hi = clampi(p.qsl[p.num_rows], lo, p.stream_tokens);
+  if (j < lo || j >= hi) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int Hk = p.Hk, C = p.C;
+  float* yj = y + (size_t)j * C;
+  for (int i = wv; i < Hk; i += kThreads / 64) {
+    float* q = yj + i * DK;
+    float* k = yj + Hk * DK + i * DK;
+    float sq = 0.f, sk = 0.f;
+    for (int c = lane; c < DK; c += 64) {
+      sq = fmaf(q[c], q[c], sq);
+      sk = fmaf(k[c], k[c], sk);
+    }
+    sq = wave_sum(sq);
+    sk = wave_sum(sk);
+    const float iq = p.l2norm ? 1.f / sqrtf(sq + p.eps) : 1.f;
+    const float ik = p.l2norm ? 1.f / sqrtf(sk + p.eps) : 1.f;
+    float dot = 0.f;
+    for (int c = lane; c < DK; c += 64) {
+      float qq = q[c] * iq * p.scale;
+      float kk = k[c] * ik;
+      q[c] = qq;
+      k[c] = kk;
+      dot = fmaf(kk, qq, dot);
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) kq[(size_t)j * Hk + i] = dot;
+  }
+  const int r = global_row(p, j);
+  for (int h = tid; h < p.Hv; h += kThreads) {
+    float av = r >= 0 ? bf2f(p.a[(size_t)r * p.Hv + h]) : 0.f;
+    float bv = r >= 0 ? bf2f(p.b[(size_t)r * p.Hv + h]) : 0.f;
+    gate_pair(av, bv, p.A_log[h], p.dt_bias[h], &ga[(size_t)j * p.Hv + h],
+              &gb[(size_t)j * p.Hv + h]);
+  }
+}
+
+template <int DK, int DV>
+__global__ void __launch_bounds__(kThreads)
+delta_prefill_kernel(PrefillArgs p, const float* __restrict__ y,
+                     const float* __restrict__ kqv, const float* __restrict__ gav,
+                     const float* __restrict__ gbv) {
+  constexpr int LPR = DK / 16;
+  constexpr int RPW = 64 / LPR;
+  constexpr int RB = (kThreads / 64) * RPW;  // state rows per workgroup
+  __shared__ __align__(16) float ks[kChunk][DK];
+  __shared__ __align__(16) float qs[kChunk][DK];
+  __shared__ float vsh[kChunk][RB];
+  __shared__ float obs[kChunk][RB];
+  __shared__ float al[kChunk], be[kChunk], kqs[kChunk];
+  __shared__ int rows[kChunk];
+
+  const int h = blockIdx.y;
+  const int rb0 = blockIdx.x * RB;
+  if (rb0 >= DV) return;
+  const PrefillRow pr = prefill_row(p, blockIdx.z);
+  if (pr.T <= 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int jl = lane % LPR, gl = lane / LPR;
+  const int Hk = p.Hk, Hv = p.Hv, C = p.C;
+  const int ih = h / p.G;
+  const int rho = rb0 + wv * RPW + gl;  // this lane group's state row
+  const bool live = rho < DV;
+  const size_t tile = ((size_t)pr.slot * Hv + h) * DV * DK + (size_t)(live ? rho : 0) * DK;
+
+  v4f S[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+    S[n] = (pr.init && live)
+               ? *reinterpret_cast<const v4f*>(p.ssm_pool + tile + (n * LPR + jl) * 4)
+               : v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = 0; c0 < pr.T; c0 += kChunk) {
+    const int n_t = min(kChunk, pr.T - c0);
+    __syncthreads();
+    for (int idx = tid; idx < n_t * DK; idx += kThreads) {
+      int t = idx / DK, c = idx - t * DK;
+      const float* yj = y + (size_t)(pr.j0 + c0 + t) * C;
+      ks[t][c] = yj[Hk * DK + ih * DK + c];
+      qs[t][c] = yj[ih * DK + c];
+    }
+    for (int idx = tid; idx < n_t * RB; idx += kThreads) {
+      int t = idx / RB, rr = idx - t * RB;
+      vsh[t][rr] = (rb0 + rr < DV)
+                       ? y[(size_t)(pr.j0 + c0 + t) * C + 2 * Hk * DK + h * DV + rb0 + rr]
+                       : 0.f;
+    }
+    if (tid < n_t) {
+      const size_t j = (size_t)(pr.j0 + c0 + tid);
+      al[tid] = gav[j * Hv + h];
+      be[tid] = gbv[j * Hv + h];
+      kqs[tid] = kqv[j * Hk + ih];
+      rows[tid] = global_row(p, (int)j);
+    }
+    __syncthreads();
+    for (int t = 0; t < n_t; ++t) {
+      v4f kv[4], qv[4];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        kv[n] = *reinterpret_cast<const v4f*>(&ks[t][(n * LPR + jl) * 4]);
+        qv[n] = *reinterpret_cast<const v4f*>(&qs[t][(n * LPR + jl) * 4]);
+      }
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        a0 = fmaf(S[n].x, kv[n].x, a0); a1 = fmaf(S[n].x, qv[n].x, a1);
+        a0 = fmaf(S[n].y, kv[n].y, a0); a1 = fmaf(S[n].y, qv[n].y, a1);
+        a0 = fmaf(S[n].z, kv[n].z, a0); a1 = fmaf(S[n].z, qv[n].z, a1);
+        a0 = fmaf(S[n].w, kv[n].w, a0); a1 = fmaf(S[n].w, qv[n].w, a1);
+      }
+      const float pk = group_sum<LPR>(a0), pq = group_sum<LPR>(a1);
+      const float alpha = al[t], beta = be[t];
+      const float vr = live ? vsh[t][rho - rb0] : 0.f;
+      const float u = beta * (vr - alpha * pk);
+      const float o = fmaf(alpha, pq, u * kqs[t]);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        S[n].x = fmaf(u, kv[n].x, alpha * S[n].x);
+        S[n].y = fmaf(u, kv[n].y, alpha * S[n].y);
+        S[n].z = fmaf(u, kv[n].z, alpha * S[n].z);
+        S[n].w = fmaf(u, kv[n].w, alpha * S[n].w);
+      }
+      if (jl == 0 && live) obs[t][rho - rb0] = o;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < n_t * RB; idx += kThreads) {
+      int t = idx / RB, rr = idx - t * RB;
+      int r = rows[t];
+      if (r >= 0 && rb0 + rr < DV)
+        p.out[((size_t)r * Hv + h) * DV + rb0 + rr] = f2bf(obs[t][rr]);
+    }
+  }
+  if (pr.slot > 0 && live) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+      *reinterpret_cast<v4f*>(p.ssm_pool + tile + (n * LPR + jl) * 4) = S[n];
+  }
+}
+
+template <int DK, int DV>
+hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t s) {
+  const WsLayout w = ws_layout(a.Hk, a.Hv, DK, DV, a.stream_tokens);
+  char* ws = static_cast<char*>(a.workspace);
+  float* y = reinterpret_cast<float*>(ws + w.y);
+  float* kq = reinterpret_cast<float*>(ws + w.kq);
+  float* ga = reinterpret_cast<float*>(ws + w.ga);
+  float* gb = reinterpret_cast<float*>(ws + w.gb);
+  const int segs = (a.max_row_len + kSeg - 1) / kSeg;
+  if (segs <= 0) return hipSuccess;
+  dim3 g1(segs, (a.C + kThreads - 1) / kThreads, a.num_rows);
+  hipLaunchKernelGGL(conv_prefill_kernel, g1, dim3(kThreads), 0, s, a, y);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(prep_prefill_kernel<DK>, dim3(a.stream_tokens), dim3(kThreads), 0, s,
+                     a, y, kq, ga, gb);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int RB = (kThreads / 64) * (64 / (DK / 16));
+  dim3 g3((DV + RB - 1) / RB, a.Hv, a.num_rows);
+  hipLaunchKernelGGL((delta_prefill_kernel<DK, DV>), g3, dim3(kThreads), 0, s, a, y, kq, ga, gb);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t prefill_workspace_bytes(int Hk, int Hv, int dk, int dv, int stream_tokens,
+                               int rows) {
+  if (rows <= 0) return 0;
+  return ws_layout(Hk, Hv, dk, dv, stream_tokens).total;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int dk, int dv, hipStream_t s) {
+  if (a.num_rows <= 0 || a.stream_tokens <= 0) return hipSuccess;
+  if (dk != dv) return hipErrorInvalidValue;
+  switch (dk) {
+    case 16: return launch_prefill_typed<16, 16>(a, s);
+    case 32: return launch_prefill_typed<32, 32>(a, s);
+    case 64: return launch_prefill_typed<64, 64>(a, s);
+    case 128: return launch_prefill_typed<128, 128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gdn

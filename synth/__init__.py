@@ -24,7 +24,9 @@ Shapes and value distributions (one record per workload):
 
 Common to all: mixed_qkv, a, b ~ N(0, 1) rounded to bf16; conv weight
 ~ N(0, 0.5) bf16; no conv bias; A_log ~ U(ln 1, ln 16) and dt_bias ~ N(0, 0.1)
-in fp32; SSM pool ~ N(0, 0.1) fp32; conv pool ~ N(0, 1) bf16; SiLU; q/k
+in fp32; SSM pool ~ N(0, 0.1) fp32 and conv pool ~ N(0, 1) bf16 on the
+slots the batch references (other slots hold the constant 0.5, a canary that
+must survive the step); SiLU; q/k
 L2-normalised with eps 1e-6; scale = dk^-1/2; n_acc ~ U{1..K}.  L is the
 smallest ring that keeps the window n_acc-1 in range: W-1 + K-1.  Slot 0 is
 always the NULL block.  Random numbers come from numpy's PCG64 seeded per
@@ -98,12 +100,49 @@ def _params(rng, d, T):
     )
 
 
-def _pools(rng, d):
+CANARY_SSM = np.float32(0.5)       # value of pool slots no row references
+CANARY_CONV = np.uint16(0x3F00)     # bf16 0.5
+
+
+def _pools(rng, d, slots=None):
+    """SSM pool ~ N(0, 0.1) fp32 and conv pool ~ N(0, 1) bf16 on ``slots``
+    (all slots when None); every other slot holds the canary value."""
     S, L, C = d["num_slots"], d["L"], conv_dim(d["Hk"], d["Hv"], d["dk"], d["dv"])
-    ssm = rng.standard_normal((S, d["Hv"], d["dv"], d["dk"]), dtype=np.float32)
-    ssm *= np.float32(0.1)
-    conv = to_bf16(rng.standard_normal((S, L, C), dtype=np.float32))
+    shape = (S, d["Hv"], d["dv"], d["dk"])
+    if slots is None:
+        ssm = rng.standard_normal(shape, dtype=np.float32)
+        ssm *= np.float32(0.1)
+        conv = to_bf16(rng.standard_normal((S, L, C), dtype=np.float32))
+        return dict(ssm_state=ssm, conv_state=conv)
+    slots = np.unique(np.asarray(list(slots), np.int64))
+    slots = slots[(slots >= 0) & (slots < S)]
+    ssm = np.full(shape, CANARY_SSM, np.float32)
+    conv = np.full((S, L, C), CANARY_CONV, np.uint16)
+    n = len(slots)
+    if n:
+        v = rng.standard_normal((n,) + shape[1:], dtype=np.float32)
+        v *= np.float32(0.1)
+        ssm[slots] = v
+        conv[slots] = to_bf16(rng.standard_normal((n, L, C), dtype=np.float32))
     return dict(ssm_state=ssm, conv_state=conv)
+
+
+def referenced_slots(case, rows=None) -> np.ndarray:
+    """Slots the batch's rows read or write (spec rows ``rows`` only, when
+    given); slot 0 (NULL) excluded."""
+    out = []
+    sp = case.get("spec")
+    if sp is not None:
+        ssi = sp["spec_state_indices"]
+        sel = range(sp["num_spec_decodes"]) if rows is None else rows
+        for b in sel:
+            out.extend(ssi[b].tolist())
+            if sp.get("spec_cache_indices") is not None:
+                out.append(int(sp["spec_cache_indices"][b]))
+    ns = case.get("nonspec")
+    if ns is not None and rows is None:
+        out.extend(ns["cache_indices"].tolist())
+    return np.array(sorted(set(s for s in out if s > 0)), np.int64)
 
 
 def _spec_meta(rng, Ns, K, slot_lo, slot_hi, null_p=0.0, force_nacc1=False,
@@ -156,10 +195,12 @@ def compose_rows(rng, row_kinds, row_lens, keep_first_nonspec=True):
 
 
 def make_case(name: str, seed: int = 0, permute_tokens: bool = False,
-              with_pools: bool = True, **over) -> dict:
+              with_pools: bool = True, fill="touched", **over) -> dict:
     """Build one workload.  Returns a dict with ``dims``, the parameter and
     input arrays, the pools, and ``spec`` / ``nonspec`` metadata (either may
-    be None)."""
+    be None).  ``fill`` picks the pool slots that get random values:
+    "touched" (every slot the batch references), "all", or a list of spec
+    row indices whose slots (plus every non-spec slot) are filled."""
     cfg = dict(CONFIGS[name])
     cfg.update(over)
     rng = np.random.default_rng(seed)
@@ -205,5 +246,12 @@ def make_case(name: str, seed: int = 0, permute_tokens: bool = False,
         case["spec"] = spec
         case["nonspec"] = nonspec
     if with_pools:
-        case.update(_pools(rng, d))
+        if isinstance(fill, str) and fill == "all":
+            slots = None
+        elif isinstance(fill, str) and fill == "touched":
+            slots = referenced_slots(case)
+        else:
+            slots = np.union1d(referenced_slots(case, rows=list(fill)),
+                               referenced_slots(dict(nonspec=case["nonspec"])))
+        case.update(_pools(rng, d, slots))
     return case

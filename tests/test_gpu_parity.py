@@ -1,0 +1,157 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on seeded
+synthetic workloads: the tiny and small spec batches, the Qwen3-Next-shaped
+K=3 batch-64 verify step (identity and permuted token_indx), the deep K=4
+batch-256 step (rows sampled for the oracle), ragged and edge-case batches,
+and the mixed batch (spec rows + decodes + two 1024-token prefills in a
+shuffled token order).  Bit-exact on the conv ring and slot bookkeeping;
+bf16 outputs within 2e-2; fp32 states within 1e-3 relative per tile."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import synth
+from tests import helpers
+from tests.gpu_util import (Gpu, assert_out_close, assert_states_close, gpu_available,
+                            OUT_CANARY, say, spec_rows_of, sub_spec)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU and libgdn.so")]
+
+
+def check_spec_case(case, sample_rows=None):
+    """Run the whole batch on the GPU; the oracle runs every row (or the
+    sampled rows) and the two are compared on those rows and their slots."""
+    sp = case["spec"]
+    rows = list(range(sp["num_spec_decodes"])) if sample_rows is None else list(sample_rows)
+    ref_spec = sp if sample_rows is None else sub_spec(sp, rows)
+    out_ref, conv_ref, ssm_ref, _ = helpers.run_spec(case, ref_spec)
+    g = Gpu(case)
+    say(f"spec {case.get('name')} rows={sp['num_spec_decodes']} T={sp['num_spec_tokens']}")
+    g.spec()
+    glob, slots = spec_rows_of(sp, rows)
+    out = g.host_out()
+    assert_out_close(out, out_ref, glob)
+    if sample_rows is None:
+        rest = np.setdiff1d(np.arange(len(out)), glob)
+        assert (out[rest] == OUT_CANARY).all(), "rows outside token_indx were written"
+    conv_slots = slots
+    np.testing.assert_array_equal(g.host_conv(conv_slots), conv_ref[conv_slots])
+    assert_states_close(g.host_ssm(slots), ssm_ref[slots])
+    # a few slots nobody names keep their bytes
+    free = np.setdiff1d(np.arange(1, case["dims"]["num_slots"]),
+                        synth.referenced_slots(case))[:8]
+    if len(free):
+        np.testing.assert_array_equal(g.host_conv(free), case["conv_state"][free])
+        np.testing.assert_array_equal(g.host_ssm(free), case["ssm_state"][free])
+    np.testing.assert_array_equal(g.host_conv([0]), case["conv_state"][[0]])
+    np.testing.assert_array_equal(g.host_ssm([0]), case["ssm_state"][[0]])
+    return g
+
+
+@pytest.mark.parametrize("name,seed", [("tiny", 0), ("tiny", 1), ("small", 0), ("small", 1)])
+def test_spec_small_workloads(name, seed):
+    check_spec_case(synth.make_case(name, seed=seed))
+
+
+@pytest.mark.parametrize("permute", [False, True])
+def test_spec_qwen3next_k3_b64(permute):
+    check_spec_case(synth.make_case("qwen3next_k3_b64", seed=3, permute_tokens=permute))
+
+
+def test_spec_deep_k4_b256_sampled():
+    rows = list(range(0, 256, 11))
+    case = synth.make_case("deep_k4_b256", seed=4, fill=rows)
+    nacc = case["spec"]["num_accepted_tokens"]
+    one = int(np.argmax(nacc == 1))
+    if one not in rows:
+        rows.append(one)
+        case = synth.make_case("deep_k4_b256", seed=4, fill=rows)
+    check_spec_case(case, sample_rows=rows)
+
+
+@pytest.mark.parametrize("lens", [[3, 1, 2, 3, 1, 1, 2, 3, 2], [1] * 7, [4, 4, 1, 3]])
+def test_spec_ragged_rows(lens):
+    # Short rows (a request that accepted no draft gets fewer tokens; no
+    # rectangular assumption) with the tail row shorter than K.
+    K = max(lens)
+    case = synth.make_case("small", seed=7, K=K, Ns=len(lens), lens=lens, null_p=0.0,
+                           Hv=32, num_slots=64)
+    check_spec_case(case)
+
+
+@pytest.mark.parametrize("rung", ["K1_full", "K4_full", "K3_nacc1", "K4_min1_max1"])
+def test_spec_page_rungs(rung):
+    # The acceptance rungs the replay harness reports (spec-decoding kernel
+    # page, "Test Result"): fully accepted K=1 and K=4, n_acc=1 with K=3,
+    # and a K=4 batch where every row has n_acc=1.
+    K = {"K1_full": 1, "K4_full": 4, "K3_nacc1": 3, "K4_min1_max1": 4}[rung]
+    case = synth.make_case("small", seed=11, K=K, Ns=12, Hv=32, num_slots=128, null_p=0.0)
+    sp = case["spec"]
+    if rung.endswith("full"):
+        sp["num_accepted_tokens"][:] = K
+    else:
+        sp["num_accepted_tokens"][:] = 1
+    check_spec_case(case)
+
+
+def test_spec_null_slots_everywhere():
+    case = synth.make_case("small", seed=12, null_p=0.6)
+    check_spec_case(case)
+
+
+def test_spec_unmapped_rows_untouched():
+    # num_actual_tokens larger than the spec stream: other rows keep their bytes.
+    case = synth.make_case("small", seed=13)
+    T = case["num_actual_tokens"]
+    extra = 5
+    for k in ("mixed_qkv", "a", "b"):
+        case[k] = np.concatenate([case[k], case[k][:extra]])
+    case["num_actual_tokens"] = T + extra
+    perm = np.random.default_rng(0).permutation(T + extra)[:T].astype(np.int32)
+    case["spec"]["spec_token_indx"] = perm
+    g = check_spec_case(case)
+    untouched = np.setdiff1d(np.arange(T + extra), perm)
+    assert (g.host_out()[untouched] == OUT_CANARY).all()
+
+
+def test_mixed_batch_parity():
+    case = synth.make_case("mixed", seed=5)
+    o1, r1, s1, _ = helpers.run_nonspec(case)
+    c = helpers.clone(case)
+    c["conv_state"], c["ssm_state"] = r1, s1
+    out_ref, conv_ref, ssm_ref, _ = helpers.run_spec(c, out=o1)
+    g = Gpu(case)
+    say("mixed: 32 spec rows + 32 decodes + 2x1024 prefill")
+    g.attention()
+    out = g.host_out()
+    assert_out_close(out, out_ref)
+    slots = synth.referenced_slots(case)
+    np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
+    assert_states_close(g.host_ssm(slots), ssm_ref[slots])
+    free = np.setdiff1d(np.arange(1, case["dims"]["num_slots"]), slots)[:8]
+    np.testing.assert_array_equal(g.host_ssm(free), case["ssm_state"][free])
+
+
+@pytest.mark.parametrize("lens,his", [([1, 1, 63, 64, 65], [1, 0, 1, 0, 1]),
+                                      ([1, 200, 7], [1, 1, 0])])
+def test_nonspec_prefill_lengths(lens, his):
+    # Prefill rows that end inside a 64-token segment, exactly on it and just
+    # past it, with and without an initial state; decodes first.
+    nd = sum(1 for l in lens if l == 1)
+    T = sum(lens)
+    case = helpers.small_case(seed=20, Hk=16, Hv=32, dk=128, dv=128, K=4, T=T,
+                              num_slots=16)
+    slots = list(range(3, 3 + len(lens)))
+    tix = np.random.default_rng(1).permutation(T).astype(np.int32)
+    ns = helpers.nonspec_meta(lens, slots, his=his, tix=tix, num_decodes=nd)
+    case["nonspec"] = ns
+    case["spec"] = None
+    case["name"] = "nonspec"
+    out_ref, conv_ref, ssm_ref, _ = helpers.run_nonspec(case)
+    g = Gpu(case)
+    say(f"non-spec rows {lens}")
+    g.attention()
+    assert_out_close(g.host_out(), out_ref)
+    np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
+    assert_states_close(g.host_ssm(slots), ssm_ref[slots])
