@@ -109,8 +109,156 @@ __host__ __device__ inline Lds lds_layout(int DK, int DV, int G, int L, int Tm) 
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-template <int DK, int DV, int R>
-__global__ void __launch_bounds__(kThreads)
+// For dk = 128: state rows per lane (R), threads per workgroup (T) and the
+// waves per SIMD the registers are fitted to (WPE), and whether snapshots
+// use non-temporal stores; all chosen by measurement on MI355X.
+#ifndef GDN_ROWS_R128
+#define GDN_ROWS_R128 4
+#endif
+#ifndef GDN_ROWS_T128
+#define GDN_ROWS_T128 512
+#endif
+#ifndef GDN_ROWS_WPE128
+#define GDN_ROWS_WPE128 4
+#endif
+#ifndef GDN_NT_STORE
+#define GDN_NT_STORE 1
+#endif
+
+__device__ __forceinline__ void store_row4(float* p, v4f v) {
+#if GDN_NT_STORE
+  __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p));
+#else
+  *reinterpret_cast<v4f*>(p) = v;
+#endif
+}
+
+// Load (or zero) the R state rows of one lane group: rows rho0 + s*RPW,
+// 16 columns each (four float4 at columns (n*LPR + jl)*4).
+template <int DK, int R, int LPR, int RPW>
+__device__ __forceinline__ void load_rows(v4f (&S)[R][4], const float* base, int rho0,
+                                          int jl, int NR, bool full) {
+  if (base == nullptr) {
+#pragma unroll
+    for (int s = 0; s < R; ++s)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) S[s][n] = v4f{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  if (full) {
+#pragma unroll
+    for (int s = 0; s < R; ++s)
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        S[s][n] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(
+            base + (size_t)(rho0 + s * RPW) * DK + (n * LPR + jl) * 4));
+  } else {
+#pragma unroll
+    for (int s = 0; s < R; ++s) {
+      const int rho = rho0 + s * RPW;
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        S[s][n] = rho < NR ? __builtin_nontemporal_load(reinterpret_cast<const v4f*>(
+                                 base + (size_t)rho * DK + (n * LPR + jl) * 4))
+                           : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
+// Inputs of one conv channel, gathered into registers in one batch: ring
+// columns (LM >= L), the row's inputs (KT >= T), taps and bias.
+template <int LM, int KT>
+struct ChanIn {
+  uint16_t h[LM];
+  uint16_t x[KT];
+  float w[kMaxWidth];
+  float bias;
+};
+
+template <int KT>
+__device__ __forceinline__ int pick(const int (&v)[KT], int j) {
+  int r = -1;
+#pragma unroll
+  for (int jj = 0; jj < KT; ++jj)
+    if (jj == j) r = v[jj];
+  return r;
+}
+
+__device__ __forceinline__ int channel_of(int pc, int ih, int Hk, int DK, int NR) {
+  if (pc < DK) return ih * DK + pc;
+  if (pc < 2 * DK) return Hk * DK + ih * DK + (pc - DK);
+  return 2 * Hk * DK + ih * NR + (pc - 2 * DK);
+}
+
+template <int LM, int KT>
+__device__ __forceinline__ void load_chan(ChanIn<LM, KT>& in, const RowArgs& p,
+                                          const RowPlan& rp, int c, const int (&rj)[KT]) {
+  const bool hist = rp.read_hist && rp.conv_slot > 0;
+  const uint16_t* ring = p.conv_pool + (size_t)rp.conv_slot * p.L * p.C + c;
+#pragma unroll
+  for (int l = 0; l < LM; ++l) in.h[l] = (hist && l < p.L) ? ring[(size_t)l * p.C] : (uint16_t)0;
+#pragma unroll
+  for (int j = 0; j < KT; ++j)
+    in.x[j] = rj[j] >= 0 ? p.qkv[(size_t)rj[j] * p.C + c] : (uint16_t)0;
+#pragma unroll
+  for (int m = 0; m < kMaxWidth; ++m)
+    in.w[m] = m < p.W ? bf2f(p.conv_w[(size_t)c * p.W + m]) : 0.f;
+  in.bias = p.conv_b ? bf2f(p.conv_b[c]) : 0.f;
+}
+
+// Stage one channel's pre-state and inputs in this thread's LDS column
+// zb[.][pc] (runtime window offsets are cheap there).
+template <int LM, int KT>
+__device__ __forceinline__ void stage_chan(const ChanIn<LM, KT>& in, int L, int T, int pc,
+                                           int NCH, uint16_t* zb) {
+#pragma unroll
+  for (int l = 0; l < LM; ++l)
+    if (l < L) zb[l * NCH + pc] = in.h[l];
+#pragma unroll
+  for (int j = 0; j < KT; ++j)
+    if (j < T) zb[(L + j) * NCH + pc] = in.x[j];
+}
+
+// Convolve one staged channel and roll its ring; every ring write follows
+// every read of the pre-state (all of it is in LDS by now).
+template <int KT>
+__device__ __forceinline__ void conv_chan(const float (&w)[kMaxWidth], float bias,
+                                          const RowArgs& p, const RowPlan& rp, int c, int pc,
+                                          int NCH, int T, const uint16_t* zb, float* dst,
+                                          int dstride, const int (&rj)[KT]) {
+  const int L = p.L, W = p.W;
+  for (int j = 0; j < T; ++j) {
+    float acc = bias;
+#pragma unroll
+    for (int m = 0; m < kMaxWidth; ++m) {
+      if (m < W) {
+        const int idx = j + m;
+        const int zi = idx < W - 1 ? rp.off + idx : L + idx - (W - 1);
+        acc = fmaf(w[m], bf2f(zb[zi * NCH + pc]), acc);
+      }
+    }
+    if (p.act) acc = silu(acc);
+    if (p.stage == kConvOnly) {
+      const int r = pick<KT>(rj, j);
+      if (r >= 0) p.y[(size_t)r * p.C + c] = acc;
+    } else {
+      dst[j * dstride] = acc;
+    }
+  }
+  if (rp.conv_slot > 0) {
+    uint16_t* wring = p.conv_pool + (size_t)rp.conv_slot * L * p.C + c;
+    for (int l = 0; l < L; ++l) {
+      const int src = l < L - T ? rp.shift + l : T + l;
+      wring[(size_t)l * p.C] = zb[src * NCH + pc];
+    }
+  }
+}
+
+// NT threads per workgroup, R state rows per lane; WPE waves per SIMD is the
+// occupancy the register budget is fitted to.  LM / KT bound state_len and
+// the tokens per row for the register gathers of the conv phase.
+template <int DK, int DV, int R, int NT, int WPE, int LM, int KT>
+__global__ void __launch_bounds__(NT, WPE)
 gdn_rows_kernel(RowArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int LPR = DK / 16;    // lanes per state row
@@ -119,7 +267,7 @@ gdn_rows_kernel(RowArgs p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int Hk = p.Hk, G = p.G, C = p.C, L = p.L, W = p.W;
+  const int Hk = p.Hk, G = p.G, C = p.C, L = p.L;
   const int row = blockIdx.x / Hk;
   const int ih = blockIdx.x - row * Hk;
   const int NCH = 2 * DK + G * DV;
@@ -142,9 +290,23 @@ gdn_rows_kernel(RowArgs p) {
   float* kq = reinterpret_cast<float*>(smem + lay.kq);
   uint16_t* zb = reinterpret_cast<uint16_t*>(smem + lay.zb);
 
+  // Global rows of the row's tokens (uniform scalar loads) and, in LDS for
+  // the later phases, rows and state-store slots.
+  int rj[KT];
+#pragma unroll
+  for (int j = 0; j < KT; ++j) {
+    int r = -1;
+    if (j < T) {
+      r = p.tix ? p.tix[rp.j0 + j] : rp.j0 + j;
+      if (r < 0 || r >= p.num_actual_tokens) r = -1;
+    }
+    rj[j] = r;
+  }
   if (tid < T) {
-    int r = p.tix ? p.tix[rp.j0 + tid] : rp.j0 + tid;
-    rows_s[tid] = (r >= 0 && r < p.num_actual_tokens) ? r : -1;
+    rows_s[tid] = rj[0];
+#pragma unroll
+    for (int j = 1; j < KT; ++j)
+      if (tid == j) rows_s[tid] = rj[j];
     int st;
     if (p.kind == kSpec)
       st = slot_or_null(p.ssi[(size_t)row * p.row_stride + tid], p.num_slots);
@@ -152,77 +314,94 @@ gdn_rows_kernel(RowArgs p) {
       st = (tid == T - 1) ? rp.conv_slot : 0;
     st_s[tid] = st;
   }
-  __syncthreads();
 
-  // ---- phase 1: conv (or load of a precomputed conv output) -------------
+  // The conv and gate inputs are gathered in one batch of loads (vector loads
+  // complete in order, so nothing slow may be issued ahead of them).
   const int stage = p.stage;
-  for (int pc = tid; pc < NCH; pc += kThreads) {
-    int c;
-    if (pc < DK) c = ih * DK + pc;
-    else if (pc < 2 * DK) c = Hk * DK + ih * DK + (pc - DK);
-    else c = 2 * Hk * DK + ih * NR + (pc - 2 * DK);
+  const bool conv_stage = stage != kDeltaOnly;
+  const bool have_chan = conv_stage && tid < NCH;
+  const int c0 = channel_of(tid, ih, Hk, DK, NR);
+  float w0[kMaxWidth], bias0 = 0.f;
+  {
+    ChanIn<LM, KT> in0;
+    if (have_chan) {
+      load_chan<LM, KT>(in0, p, rp, c0, rj);
+#pragma unroll
+      for (int m = 0; m < kMaxWidth; ++m) w0[m] = in0.w[m];
+      bias0 = in0.bias;
+    }
+    const bool have_gate0 = stage != kConvOnly && tid < T * G;
+    uint16_t gate_a = 0, gate_b = 0;
+    if (have_gate0) {
+      const int r = pick<KT>(rj, tid / G);
+      const int h = ih * G + tid % G;
+      if (r >= 0) {
+        gate_a = p.a[(size_t)r * p.Hv + h];
+        gate_b = p.b[(size_t)r * p.Hv + h];
+      }
+    }
+    if (have_chan) stage_chan<LM, KT>(in0, L, T, tid, NCH, zb);
+    if (have_gate0) {
+      ga[tid] = bf2f(gate_a);  // raw gate inputs; turned into alpha/beta below
+      gb[tid] = bf2f(gate_b);
+    }
+  }
+  // ---- phase 1: conv (or load of a precomputed conv output) -------------
+  for (int pc = tid; pc < NCH; pc += NT) {
+    const int c = pc == tid ? c0 : channel_of(pc, ih, Hk, DK, NR);
     float* dst;
     int dstride;
     if (pc < DK) { dst = qs + pc; dstride = DK; }
     else if (pc < 2 * DK) { dst = ks + (pc - DK); dstride = DK; }
     else { dst = vs + (pc - 2 * DK); dstride = NR; }
-
-    if (stage == kDeltaOnly) {
+    if (!conv_stage) {
       for (int j = 0; j < T; ++j) {
-        int r = rows_s[j];
+        const int r = pick<KT>(rj, j);
         dst[j * dstride] = r >= 0 ? p.y[(size_t)r * C + c] : 0.f;
       }
       continue;
     }
-    const bool hist = rp.read_hist && rp.conv_slot > 0;
-    const uint16_t* ring = p.conv_pool + (size_t)rp.conv_slot * L * C + c;
-    for (int l = 0; l < L; ++l) zb[l * NCH + pc] = hist ? ring[(size_t)l * C] : 0;
-    for (int j = 0; j < T; ++j) {
-      int r = rows_s[j];
-      zb[(L + j) * NCH + pc] = r >= 0 ? p.qkv[(size_t)r * C + c] : 0;
-    }
-    float w[kMaxWidth];
-#pragma unroll
-    for (int m = 0; m < kMaxWidth; ++m) w[m] = m < W ? bf2f(p.conv_w[(size_t)c * W + m]) : 0.f;
-    const float bias = p.conv_b ? bf2f(p.conv_b[c]) : 0.f;
-    for (int j = 0; j < T; ++j) {
-      float acc = bias;
-#pragma unroll
-      for (int m = 0; m < kMaxWidth; ++m) {
-        if (m < W) {
-          int idx = j + m;
-          int zi = idx < W - 1 ? rp.off + idx : L + idx - (W - 1);
-          acc = fmaf(w[m], bf2f(zb[zi * NCH + pc]), acc);
-        }
-      }
-      if (p.act) acc = silu(acc);
-      if (stage == kConvOnly) {
-        int r = rows_s[j];
-        if (r >= 0) p.y[(size_t)r * C + c] = acc;
-      } else {
-        dst[j * dstride] = acc;
-      }
-    }
-    if (rp.conv_slot > 0) {
-      uint16_t* wring = p.conv_pool + (size_t)rp.conv_slot * L * C + c;
-      for (int l = 0; l < L; ++l) {
-        int src = l < L - T ? rp.shift + l : T + l;
-        wring[(size_t)l * C] = zb[src * NCH + pc];
-      }
+    if (pc == tid) {
+      conv_chan<KT>(w0, bias0, p, rp, c, pc, NCH, T, zb, dst, dstride, rj);
+    } else {
+      ChanIn<LM, KT> in;
+      load_chan<LM, KT>(in, p, rp, c, rj);
+      stage_chan<LM, KT>(in, L, T, pc, NCH, zb);
+      conv_chan<KT>(in.w, in.bias, p, rp, c, pc, NCH, T, zb, dst, dstride, rj);
     }
   }
   if (stage == kConvOnly) return;
 
+  // The state rows (the bulk of the reads) are issued now and land while the
+  // gates and norms run.
+  const int jl = lane % LPR, gl = lane / LPR;
+  const size_t slot_stride = (size_t)p.Hv * DV * DK;
+  const size_t head_off = (size_t)ih * NR * DK;
+  const float* load_base =
+      rp.load_slot > 0 ? p.ssm_pool + (size_t)rp.load_slot * slot_stride + head_off : nullptr;
+  constexpr int kRowsPerWavePass = RPW * R;
+  constexpr int kRowsPerPass = (NT / 64) * kRowsPerWavePass;
+  v4f S[R][4];
+  {
+    const int r0 = wv * kRowsPerWavePass;
+    load_rows<DK, R, LPR, RPW>(S, load_base, r0 + gl, jl, NR, r0 + kRowsPerWavePass <= NR);
+  }
+
+
   // ---- phase 2: gates and q/k norms ---------------------------------------
-  for (int idx = tid; idx < T * G; idx += kThreads) {
-    int j = idx / G, g = idx - j * G, h = ih * G + g;
-    int r = rows_s[j];
-    float av = r >= 0 ? bf2f(p.a[(size_t)r * p.Hv + h]) : 0.f;
-    float bv = r >= 0 ? bf2f(p.b[(size_t)r * p.Hv + h]) : 0.f;
+  if (tid < T * G) {
+    const int h = ih * G + tid % G;
+    gate_pair(ga[tid], gb[tid], p.A_log[h], p.dt_bias[h], &ga[tid], &gb[tid]);
+  }
+  for (int idx = tid + NT; idx < T * G; idx += NT) {
+    const int j = idx / G, g = idx - j * G, h = ih * G + g;
+    const int r = pick<KT>(rj, j);
+    const float av = r >= 0 ? bf2f(p.a[(size_t)r * p.Hv + h]) : 0.f;
+    const float bv = r >= 0 ? bf2f(p.b[(size_t)r * p.Hv + h]) : 0.f;
     gate_pair(av, bv, p.A_log[h], p.dt_bias[h], &ga[idx], &gb[idx]);
   }
   __syncthreads();
-  for (int j = wv; j < T; j += kThreads / 64) {
+  for (int j = wv; j < T; j += NT / 64) {
     float sq = 0.f, sk = 0.f;
     for (int c = lane; c < DK; c += 64) {
       float q = qs[j * DK + c], k = ks[j * DK + c];
@@ -247,79 +426,92 @@ gdn_rows_kernel(RowArgs p) {
   __syncthreads();
 
   // ---- phase 3: recurrence over the state rows -----------------------------
-  const int jl = lane % LPR, gl = lane / LPR;
-  const size_t slot_stride = (size_t)p.Hv * DV * DK;
-  const size_t head_off = (size_t)ih * NR * DK;
-  for (int r0 = wv * RPW * R; r0 < NR; r0 += (kThreads / 64) * RPW * R) {
-    v4f S[R][4];
-    int rho[R];
-#pragma unroll
-    for (int s = 0; s < R; ++s) rho[s] = r0 + s * RPW + gl;
-    if (rp.load_slot > 0) {
-      const float* base = p.ssm_pool + (size_t)rp.load_slot * slot_stride + head_off;
-#pragma unroll
-      for (int s = 0; s < R; ++s)
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-          S[s][n] = rho[s] < NR
-                        ? *reinterpret_cast<const v4f*>(base + (size_t)rho[s] * DK + (n * LPR + jl) * 4)
-                        : v4f{0.f, 0.f, 0.f, 0.f};
-    } else {
-#pragma unroll
-      for (int s = 0; s < R; ++s)
-#pragma unroll
-        for (int n = 0; n < 4; ++n) S[s][n] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
+  for (int r0 = wv * kRowsPerWavePass; r0 < NR; r0 += kRowsPerPass) {
+    const bool full = r0 + kRowsPerWavePass <= NR;
+    const int rho0 = r0 + gl;
+    if (r0 != wv * kRowsPerWavePass) load_rows<DK, R, LPR, RPW>(S, load_base, rho0, jl, NR, full);
     for (int j = 0; j < T; ++j) {
-      v4f kv[4], qv[4];
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        kv[n] = *reinterpret_cast<const v4f*>(ks + j * DK + (n * LPR + jl) * 4);
-        qv[n] = *reinterpret_cast<const v4f*>(qs + j * DK + (n * LPR + jl) * 4);
-      }
       float pk[R], pq[R];
 #pragma unroll
-      for (int s = 0; s < R; ++s) {
-        float a0 = 0.f, a1 = 0.f;
+      for (int s = 0; s < R; ++s) { pk[s] = 0.f; pq[s] = 0.f; }
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          a0 = fmaf(S[s][n].x, kv[n].x, a0); a1 = fmaf(S[s][n].x, qv[n].x, a1);
-          a0 = fmaf(S[s][n].y, kv[n].y, a0); a1 = fmaf(S[s][n].y, qv[n].y, a1);
-          a0 = fmaf(S[s][n].z, kv[n].z, a0); a1 = fmaf(S[s][n].z, qv[n].z, a1);
-          a0 = fmaf(S[s][n].w, kv[n].w, a0); a1 = fmaf(S[s][n].w, qv[n].w, a1);
+      for (int n = 0; n < 4; ++n) {
+        const v4f kv = *reinterpret_cast<const v4f*>(ks + j * DK + (n * LPR + jl) * 4);
+        const v4f qv = *reinterpret_cast<const v4f*>(qs + j * DK + (n * LPR + jl) * 4);
+#pragma unroll
+        for (int s = 0; s < R; ++s) {
+          pk[s] = fmaf(S[s][n].x, kv.x, pk[s]); pq[s] = fmaf(S[s][n].x, qv.x, pq[s]);
+          pk[s] = fmaf(S[s][n].y, kv.y, pk[s]); pq[s] = fmaf(S[s][n].y, qv.y, pq[s]);
+          pk[s] = fmaf(S[s][n].z, kv.z, pk[s]); pq[s] = fmaf(S[s][n].z, qv.z, pq[s]);
+          pk[s] = fmaf(S[s][n].w, kv.w, pk[s]); pq[s] = fmaf(S[s][n].w, qv.w, pq[s]);
         }
-        pk[s] = group_sum<LPR>(a0);
-        pq[s] = group_sum<LPR>(a1);
+      }
+#pragma unroll
+      for (int s = 0; s < R; ++s) {
+        pk[s] = group_sum<LPR>(pk[s]);
+        pq[s] = group_sum<LPR>(pq[s]);
       }
       const float kqj = kq[j];
+      float al[R], u[R];
+      if constexpr (DV % kRowsPerWavePass == 0) {
+        // The wave's rows lie in one v-head: its gates are wave-uniform.
+        const int g = r0 / DV;
+        const float alw = __builtin_bit_cast(
+            float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ga[j * G + g])));
+        const float bew = __builtin_bit_cast(
+            float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gb[j * G + g])));
 #pragma unroll
-      for (int s = 0; s < R; ++s) {
-        const int rr = rho[s] < NR ? rho[s] : NR - 1;
-        const int g = rr / DV;
-        const float al = ga[j * G + g], be = gb[j * G + g];
-        const float vr = vs[j * NR + rr];
-        // S_new = al S + u k^T with u = be (v - al S k); o = S_new q.
-        const float u = be * (vr - al * pk[s]);
-        const float o = fmaf(al, pq[s], u * kqj);
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          S[s][n].x = fmaf(u, kv[n].x, al * S[s][n].x);
-          S[s][n].y = fmaf(u, kv[n].y, al * S[s][n].y);
-          S[s][n].z = fmaf(u, kv[n].z, al * S[s][n].z);
-          S[s][n].w = fmaf(u, kv[n].w, al * S[s][n].w);
+        for (int s = 0; s < R; ++s) {
+          const int rho = rho0 + s * RPW;
+          const float vr = vs[j * NR + (rho < NR ? rho : NR - 1)];
+          al[s] = alw;
+          // S_new = al S + u k^T with u = be (v - al S k); o = S_new q.
+          u[s] = bew * (vr - alw * pk[s]);
+          const float o = fmaf(alw, pq[s], u[s] * kqj);
+          if (jl == 0 && rho < NR) ob[j * NR + rho] = o;
         }
-        if (jl == 0 && rho[s] < NR) ob[j * NR + rho[s]] = o;
+      } else {
+#pragma unroll
+        for (int s = 0; s < R; ++s) {
+          const int rho = rho0 + s * RPW;
+          const int rr = rho < NR ? rho : NR - 1;
+          const int g = rr / DV;
+          al[s] = ga[j * G + g];
+          const float be = gb[j * G + g];
+          const float vr = vs[j * NR + rr];
+          u[s] = be * (vr - al[s] * pk[s]);
+          const float o = fmaf(al[s], pq[s], u[s] * kqj);
+          if (jl == 0 && rho < NR) ob[j * NR + rho] = o;
+        }
+      }
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const v4f kv = *reinterpret_cast<const v4f*>(ks + j * DK + (n * LPR + jl) * 4);
+#pragma unroll
+        for (int s = 0; s < R; ++s) {
+          S[s][n].x = fmaf(u[s], kv.x, al[s] * S[s][n].x);
+          S[s][n].y = fmaf(u[s], kv.y, al[s] * S[s][n].y);
+          S[s][n].z = fmaf(u[s], kv.z, al[s] * S[s][n].z);
+          S[s][n].w = fmaf(u[s], kv.w, al[s] * S[s][n].w);
+        }
       }
       const int st = st_s[j];
       if (st > 0) {
         float* base = p.ssm_pool + (size_t)st * slot_stride + head_off;
+        if (full) {
 #pragma unroll
-        for (int s = 0; s < R; ++s)
-          if (rho[s] < NR)
+          for (int s = 0; s < R; ++s)
 #pragma unroll
             for (int n = 0; n < 4; ++n)
-              __builtin_nontemporal_store(
-                  S[s][n], reinterpret_cast<v4f*>(base + (size_t)rho[s] * DK + (n * LPR + jl) * 4));
+              store_row4(base + (size_t)(rho0 + s * RPW) * DK + (n * LPR + jl) * 4, S[s][n]);
+        } else {
+#pragma unroll
+          for (int s = 0; s < R; ++s)
+            if (rho0 + s * RPW < NR)
+#pragma unroll
+              for (int n = 0; n < 4; ++n)
+                store_row4(base + (size_t)(rho0 + s * RPW) * DK + (n * LPR + jl) * 4, S[s][n]);
+        }
       }
     }
   }
@@ -327,17 +519,17 @@ gdn_rows_kernel(RowArgs p) {
 
   // ---- phase 4: outputs ----------------------------------------------------
   uint16_t* out = p.out;
-  for (int idx = tid; idx < T * NR; idx += kThreads) {
+  for (int idx = tid; idx < T * NR; idx += NT) {
     int j = idx / NR, rr = idx - j * NR;
     int r = rows_s[j];
     if (r >= 0) out[((size_t)r * p.Hv + ih * G) * DV + rr] = f2bf(ob[idx]);
   }
 }
 
-template <int DK, int DV, int R>
+template <int DK, int DV, int R, int NT, int WPE, int LM, int KT>
 hipError_t launch_typed(const RowArgs& a, hipStream_t s) {
   const Lds lay = lds_layout(DK, DV, a.G, a.L, a.max_row_tokens);
-  auto kern = gdn_rows_kernel<DK, DV, R>;
+  auto kern = gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT>;
   if (lay.total > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -345,8 +537,15 @@ hipError_t launch_typed(const RowArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   dim3 grid(static_cast<unsigned>(a.num_rows) * static_cast<unsigned>(a.Hk));
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lay.total, s, a);
+  hipLaunchKernelGGL(kern, grid, dim3(NT), lay.total, s, a);
   return hipGetLastError();
+}
+
+// Short rows on a short ring take the small register gathers.
+template <int DK, int DV, int R, int NT, int WPE>
+hipError_t launch_sized(const RowArgs& a, hipStream_t s) {
+  if (a.L <= 8 && a.max_row_tokens <= 4) return launch_typed<DK, DV, R, NT, WPE, 8, 4>(a, s);
+  return launch_typed<DK, DV, R, NT, WPE, kMaxStateLen, kMaxRowTokens>(a, s);
 }
 
 }  // namespace
@@ -359,10 +558,11 @@ hipError_t launch_rows(const RowArgs& a, int dk, int dv, hipStream_t s) {
   if (a.num_rows <= 0) return hipSuccess;
   if (dk != dv) return hipErrorInvalidValue;
   switch (dk) {
-    case 16: return launch_typed<16, 16, 1>(a, s);
-    case 32: return launch_typed<32, 32, 1>(a, s);
-    case 64: return launch_typed<64, 64, 2>(a, s);
-    case 128: return launch_typed<128, 128, 4>(a, s);
+    case 16: return launch_sized<16, 16, 1, 256, 4>(a, s);
+    case 32: return launch_sized<32, 32, 1, 256, 4>(a, s);
+    case 64: return launch_sized<64, 64, 2, 256, 4>(a, s);
+    case 128:
+      return launch_sized<128, 128, GDN_ROWS_R128, GDN_ROWS_T128, GDN_ROWS_WPE128>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
