@@ -109,9 +109,10 @@ __host__ __device__ inline Lds lds_layout(int DK, int DV, int G, int L, int Tm) 
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// For dk = 128: state rows per lane (R), threads per workgroup (T) and the
-// waves per SIMD the registers are fitted to (WPE), and whether snapshots
-// use non-temporal stores; all chosen by measurement on MI355X.
+// For dk = 128: state rows per lane (R), threads per workgroup (T), the
+// waves per SIMD the registers are fitted to (WPE), rows taken through all
+// tokens at a time (RB), and whether snapshots use non-temporal stores; all
+// chosen by measurement on MI355X.
 #ifndef GDN_ROWS_R128
 #define GDN_ROWS_R128 4
 #endif
@@ -120,6 +121,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 #endif
 #ifndef GDN_ROWS_WPE128
 #define GDN_ROWS_WPE128 4
+#endif
+#ifndef GDN_ROWS_RB128
+#define GDN_ROWS_RB128 4
 #endif
 #ifndef GDN_NT_STORE
 #define GDN_NT_STORE 1
@@ -257,9 +261,10 @@ __device__ __forceinline__ void conv_chan(const float (&w)[kMaxWidth], float bia
 // NT threads per workgroup, R state rows per lane; WPE waves per SIMD is the
 // occupancy the register budget is fitted to.  LM / KT bound state_len and
 // the tokens per row for the register gathers of the conv phase.
-template <int DK, int DV, int R, int NT, int WPE, int LM, int KT>
+template <int DK, int DV, int R, int NT, int WPE, int LM, int KT, int RB>
 __global__ void __launch_bounds__(NT, WPE)
 gdn_rows_kernel(RowArgs p) {
+  static_assert(R % RB == 0, "row batch");
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int LPR = DK / 16;    // lanes per state row
   constexpr int RPW = 64 / LPR;   // state rows per wave per sub-pass
@@ -426,91 +431,93 @@ gdn_rows_kernel(RowArgs p) {
   __syncthreads();
 
   // ---- phase 3: recurrence over the state rows -----------------------------
+  // Rows are taken RB at a time through all the row's tokens, so the first
+  // snapshots are stored as soon as those rows' loads have arrived.
   for (int r0 = wv * kRowsPerWavePass; r0 < NR; r0 += kRowsPerPass) {
     const bool full = r0 + kRowsPerWavePass <= NR;
     const int rho0 = r0 + gl;
     if (r0 != wv * kRowsPerWavePass) load_rows<DK, R, LPR, RPW>(S, load_base, rho0, jl, NR, full);
-    for (int j = 0; j < T; ++j) {
-      float pk[R], pq[R];
 #pragma unroll
-      for (int s = 0; s < R; ++s) { pk[s] = 0.f; pq[s] = 0.f; }
+    for (int sb = 0; sb < R; sb += RB) {
+      for (int j = 0; j < T; ++j) {
+        float pk[RB], pq[RB];
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const v4f kv = *reinterpret_cast<const v4f*>(ks + j * DK + (n * LPR + jl) * 4);
-        const v4f qv = *reinterpret_cast<const v4f*>(qs + j * DK + (n * LPR + jl) * 4);
+        for (int q = 0; q < RB; ++q) { pk[q] = 0.f; pq[q] = 0.f; }
 #pragma unroll
-        for (int s = 0; s < R; ++s) {
-          pk[s] = fmaf(S[s][n].x, kv.x, pk[s]); pq[s] = fmaf(S[s][n].x, qv.x, pq[s]);
-          pk[s] = fmaf(S[s][n].y, kv.y, pk[s]); pq[s] = fmaf(S[s][n].y, qv.y, pq[s]);
-          pk[s] = fmaf(S[s][n].z, kv.z, pk[s]); pq[s] = fmaf(S[s][n].z, qv.z, pq[s]);
-          pk[s] = fmaf(S[s][n].w, kv.w, pk[s]); pq[s] = fmaf(S[s][n].w, qv.w, pq[s]);
+        for (int n = 0; n < 4; ++n) {
+          const v4f kv = *reinterpret_cast<const v4f*>(ks + j * DK + (n * LPR + jl) * 4);
+          const v4f qv = *reinterpret_cast<const v4f*>(qs + j * DK + (n * LPR + jl) * 4);
+#pragma unroll
+          for (int q = 0; q < RB; ++q) {
+            const v4f x = S[sb + q][n];
+            pk[q] = fmaf(x.x, kv.x, pk[q]); pq[q] = fmaf(x.x, qv.x, pq[q]);
+            pk[q] = fmaf(x.y, kv.y, pk[q]); pq[q] = fmaf(x.y, qv.y, pq[q]);
+            pk[q] = fmaf(x.z, kv.z, pk[q]); pq[q] = fmaf(x.z, qv.z, pq[q]);
+            pk[q] = fmaf(x.w, kv.w, pk[q]); pq[q] = fmaf(x.w, qv.w, pq[q]);
+          }
         }
-      }
 #pragma unroll
-      for (int s = 0; s < R; ++s) {
-        pk[s] = group_sum<LPR>(pk[s]);
-        pq[s] = group_sum<LPR>(pq[s]);
-      }
-      const float kqj = kq[j];
-      float al[R], u[R];
-      if constexpr (DV % kRowsPerWavePass == 0) {
-        // The wave's rows lie in one v-head: its gates are wave-uniform.
-        const int g = r0 / DV;
-        const float alw = __builtin_bit_cast(
-            float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ga[j * G + g])));
-        const float bew = __builtin_bit_cast(
-            float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gb[j * G + g])));
-#pragma unroll
-        for (int s = 0; s < R; ++s) {
-          const int rho = rho0 + s * RPW;
-          const float vr = vs[j * NR + (rho < NR ? rho : NR - 1)];
-          al[s] = alw;
-          // S_new = al S + u k^T with u = be (v - al S k); o = S_new q.
-          u[s] = bew * (vr - alw * pk[s]);
-          const float o = fmaf(alw, pq[s], u[s] * kqj);
-          if (jl == 0 && rho < NR) ob[j * NR + rho] = o;
+        for (int q = 0; q < RB; ++q) {
+          pk[q] = group_sum<LPR>(pk[q]);
+          pq[q] = group_sum<LPR>(pq[q]);
         }
-      } else {
+        const float kqj = kq[j];
+        float al[RB], u[RB];
+        if constexpr (DV % kRowsPerWavePass == 0) {
+          // The wave's rows lie in one v-head: its gates are wave-uniform.
+          const int g = r0 / DV;
+          const float alw = __builtin_bit_cast(
+              float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ga[j * G + g])));
+          const float bew = __builtin_bit_cast(
+              float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gb[j * G + g])));
 #pragma unroll
-        for (int s = 0; s < R; ++s) {
-          const int rho = rho0 + s * RPW;
-          const int rr = rho < NR ? rho : NR - 1;
-          const int g = rr / DV;
-          al[s] = ga[j * G + g];
-          const float be = gb[j * G + g];
-          const float vr = vs[j * NR + rr];
-          u[s] = be * (vr - al[s] * pk[s]);
-          const float o = fmaf(al[s], pq[s], u[s] * kqj);
-          if (jl == 0 && rho < NR) ob[j * NR + rho] = o;
-        }
-      }
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const v4f kv = *reinterpret_cast<const v4f*>(ks + j * DK + (n * LPR + jl) * 4);
-#pragma unroll
-        for (int s = 0; s < R; ++s) {
-          S[s][n].x = fmaf(u[s], kv.x, al[s] * S[s][n].x);
-          S[s][n].y = fmaf(u[s], kv.y, al[s] * S[s][n].y);
-          S[s][n].z = fmaf(u[s], kv.z, al[s] * S[s][n].z);
-          S[s][n].w = fmaf(u[s], kv.w, al[s] * S[s][n].w);
-        }
-      }
-      const int st = st_s[j];
-      if (st > 0) {
-        float* base = p.ssm_pool + (size_t)st * slot_stride + head_off;
-        if (full) {
-#pragma unroll
-          for (int s = 0; s < R; ++s)
-#pragma unroll
-            for (int n = 0; n < 4; ++n)
-              store_row4(base + (size_t)(rho0 + s * RPW) * DK + (n * LPR + jl) * 4, S[s][n]);
+          for (int q = 0; q < RB; ++q) {
+            const int rho = rho0 + (sb + q) * RPW;
+            const float vr = vs[j * NR + (rho < NR ? rho : NR - 1)];
+            al[q] = alw;
+            // S_new = al S + u k^T with u = be (v - al S k); o = S_new q.
+            u[q] = bew * (vr - alw * pk[q]);
+            const float o = fmaf(alw, pq[q], u[q] * kqj);
+            if (jl == 0 && rho < NR) ob[j * NR + rho] = o;
+          }
         } else {
 #pragma unroll
-          for (int s = 0; s < R; ++s)
-            if (rho0 + s * RPW < NR)
+          for (int q = 0; q < RB; ++q) {
+            const int rho = rho0 + (sb + q) * RPW;
+            const int rr = rho < NR ? rho : NR - 1;
+            const int g = rr / DV;
+            al[q] = ga[j * G + g];
+            const float be = gb[j * G + g];
+            const float vr = vs[j * NR + rr];
+            u[q] = be * (vr - al[q] * pk[q]);
+            const float o = fmaf(al[q], pq[q], u[q] * kqj);
+            if (jl == 0 && rho < NR) ob[j * NR + rho] = o;
+          }
+        }
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const v4f kv = *reinterpret_cast<const v4f*>(ks + j * DK + (n * LPR + jl) * 4);
+#pragma unroll
+          for (int q = 0; q < RB; ++q) {
+            v4f& x = S[sb + q][n];
+            x.x = fmaf(u[q], kv.x, al[q] * x.x);
+            x.y = fmaf(u[q], kv.y, al[q] * x.y);
+            x.z = fmaf(u[q], kv.z, al[q] * x.z);
+            x.w = fmaf(u[q], kv.w, al[q] * x.w);
+          }
+        }
+        const int st = st_s[j];
+        if (st > 0) {
+          float* base = p.ssm_pool + (size_t)st * slot_stride + head_off;
+#pragma unroll
+          for (int q = 0; q < RB; ++q) {
+            const int rho = rho0 + (sb + q) * RPW;
+            if (full || rho < NR) {
 #pragma unroll
               for (int n = 0; n < 4; ++n)
-                store_row4(base + (size_t)(rho0 + s * RPW) * DK + (n * LPR + jl) * 4, S[s][n]);
+                store_row4(base + (size_t)rho * DK + (n * LPR + jl) * 4, S[sb + q][n]);
+            }
+          }
         }
       }
     }
@@ -529,7 +536,8 @@ gdn_rows_kernel(RowArgs p) {
 template <int DK, int DV, int R, int NT, int WPE, int LM, int KT>
 hipError_t launch_typed(const RowArgs& a, hipStream_t s) {
   const Lds lay = lds_layout(DK, DV, a.G, a.L, a.max_row_tokens);
-  auto kern = gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT>;
+  constexpr int RB = DK == 128 ? GDN_ROWS_RB128 : R;
+  auto kern = gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT, RB>;
   if (lay.total > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
