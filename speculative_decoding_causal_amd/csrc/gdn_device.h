@@ -56,6 +56,13 @@ __device__ __forceinline__ void gate_pair(float a, float b, float A_log,
   *beta = 1.f / (1.f + expf(-b));
 }
 
+// Log of the decay: log alpha = -exp(A_log) * softplus(a + dt_bias).
+__device__ __forceinline__ float gate_log(float a, float A_log, float dt_bias) {
+  const float x = a + dt_bias;
+  const float sp = x > 20.f ? x : log1pf(expf(x));
+  return -expf(A_log) * sp;
+}
+
 __device__ __forceinline__ float silu(float x) { return x / (1.f + expf(-x)); }
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) {

@@ -83,4 +83,16 @@ size_t prefill_workspace_bytes(int Hk, int Hv, int dk, int dv,
                                int stream_tokens, int rows);
 hipError_t launch_prefill(const PrefillArgs& a, int dk, int dv, hipStream_t s);
 
+// Per-token chunk quantities of the chunked prefill, indexed by non-spec
+// stream token and v-head: W [n, Hv, dk], U~ [n, Hv, dv], P [n, Hv, 64],
+// G [n, Hv] (cumulative log-decay inside the token's chunk).
+struct ChunkWs {
+  float* W;
+  float* U;
+  float* P;
+  float* G;
+};
+hipError_t launch_chunked(const PrefillArgs& a, int dk, int dv, const float* y, const float* glog,
+                          const float* gbeta, const ChunkWs& ws, hipStream_t s);
+
 }  // namespace gdn

@@ -9,11 +9,13 @@
 //      afterwards, so reads of the pre-state precede the writes.
 //   2. prep_prefill: per token, the q/k L2 norms (wave reductions, q scaled)
 //      are applied in place in the workspace, k.q is kept, and the gates of
-//      every v-head are evaluated at the token's global row.
-//   3. delta_prefill: one workgroup per (row, v-head, block of 32 state rows)
-//      carries its state rows in VGPRs across the whole row; the per-token
-//      operands are staged in LDS 32 tokens at a time.  The final state is
-//      stored to the row's slot.
+//      every v-head are evaluated at the token's global row (log-decay and
+//      beta).
+//   3. the chunked WY/UT recurrence on MFMA (gdn_chunk.hip) for head dims 64
+//      and 128; for smaller heads, delta_prefill: one workgroup per (row,
+//      v-head, block of state rows) carries its rows in VGPRs through the
+//      row, the per-token operands staged in LDS 32 tokens at a time.  The
+//      final state is stored to the row's slot.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -21,12 +23,13 @@ namespace gdn {
 namespace {
 
 constexpr int kSeg = 64;    // tokens per conv thread
+constexpr int kBatch = 16;  // tokens gathered per round of loads
 constexpr int kChunk = 32;  // tokens staged per LDS refill in the recurrence
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 struct WsLayout {
-  size_t y, kq, ga, gb, total;
+  size_t y, kq, ga, gb, W, U, P, G, total;
 };
 
 WsLayout ws_layout(int Hk, int Hv, int dk, int dv, int stream_tokens) {
@@ -39,6 +42,10 @@ WsLayout ws_layout(int Hk, int Hv, int dk, int dv, int stream_tokens) {
   w.kq = o; o += al(n * Hk * 4);
   w.ga = o; o += al(n * Hv * 4);
   w.gb = o; o += al(n * Hv * 4);
+  w.W = o;  o += al(n * Hv * dk * 4);
+  w.U = o;  o += al(n * Hv * dv * 4);
+  w.P = o;  o += al(n * Hv * 64 * 4);
+  w.G = o;  o += al(n * Hv * 4);
   w.total = o;
   return w;
 }
@@ -96,22 +103,32 @@ conv_prefill_kernel(PrefillArgs p, float* __restrict__ y) {
 #pragma unroll
   for (int m = 0; m < kMaxWidth - 1; ++m)
     win[m] = m < W - 1 ? bf2f(xin(base - (W - 1) + m)) : 0.f;
-  for (int t = base; t < end; ++t) {
-    const float xt = bf2f(xin(t));
-    float acc = bias;
+  // Inputs are gathered kBatch tokens at a time (one round of loads), then
+  // the window slides over them.
+  for (int t0 = base; t0 < end; t0 += kBatch) {
+    uint16_t xb[kBatch];
 #pragma unroll
-    for (int m = 0; m < kMaxWidth - 1; ++m)
-      if (m < W - 1) acc = fmaf(w[m], win[m], acc);
-    acc = fmaf(wlast, xt, acc);
-    if (p.act) acc = silu(acc);
-    y[(size_t)(pr.j0 + t) * C + c] = acc;
+    for (int i = 0; i < kBatch; ++i) xb[i] = (t0 + i < end) ? xin(t0 + i) : (uint16_t)0;
 #pragma unroll
-    for (int m = 0; m < kMaxWidth - 2; ++m)
-      if (m < W - 2) win[m] = win[m + 1];
-    if (W >= 2) {
+    for (int i = 0; i < kBatch; ++i) {
+      if (t0 + i < end) {
+        const float xt = bf2f(xb[i]);
+        float acc = bias;
 #pragma unroll
-      for (int m = 0; m < kMaxWidth - 1; ++m)
-        if (m == W - 2) win[m] = xt;
+        for (int m = 0; m < kMaxWidth - 1; ++m)
+          if (m < W - 1) acc = fmaf(w[m], win[m], acc);
+        acc = fmaf(wlast, xt, acc);
+        if (p.act) acc = silu(acc);
+        y[(size_t)(pr.j0 + t0 + i) * C + c] = acc;
+#pragma unroll
+        for (int m = 0; m < kMaxWidth - 2; ++m)
+          if (m < W - 2) win[m] = win[m + 1];
+        if (W >= 2) {
+#pragma unroll
+          for (int m = 0; m < kMaxWidth - 1; ++m)
+            if (m == W - 2) win[m] = xt;
+        }
+      }
     }
   }
   // Roll: new column l <- (history ++ inputs)[T + l].  Column T + l is read
@@ -164,8 +181,8 @@ prep_prefill_kernel(PrefillArgs p, float* __restrict__ y, float* __restrict__ kq
   for (int h = tid; h < p.Hv; h += kThreads) {
     float av = r >= 0 ? bf2f(p.a[(size_t)r * p.Hv + h]) : 0.f;
     float bv = r >= 0 ? bf2f(p.b[(size_t)r * p.Hv + h]) : 0.f;
-    gate_pair(av, bv, p.A_log[h], p.dt_bias[h], &ga[(size_t)j * p.Hv + h],
-              &gb[(size_t)j * p.Hv + h]);
+    ga[(size_t)j * p.Hv + h] = gate_log(av, p.A_log[h], p.dt_bias[h]);
+    gb[(size_t)j * p.Hv + h] = 1.f / (1.f + expf(-bv));
   }
 }
 
@@ -243,7 +260,7 @@ delta_prefill_kernel(PrefillArgs p, const float* __restrict__ y,
         a0 = fmaf(S[n].w, kv[n].w, a0); a1 = fmaf(S[n].w, qv[n].w, a1);
       }
       const float pk = group_sum<LPR>(a0), pq = group_sum<LPR>(a1);
-      const float alpha = al[t], beta = be[t];
+      const float alpha = expf(al[t]), beta = be[t];
       const float vr = live ? vsh[t][rho - rb0] : 0.f;
       const float u = beta * (vr - alpha * pk);
       const float o = fmaf(alpha, pq, u * kqs[t]);
@@ -289,10 +306,16 @@ hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t s) {
                      a, y, kq, ga, gb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int RB = (kThreads / 64) * (64 / (DK / 16));
-  dim3 g3((DV + RB - 1) / RB, a.Hv, a.num_rows);
-  hipLaunchKernelGGL((delta_prefill_kernel<DK, DV>), g3, dim3(kThreads), 0, s, a, y, kq, ga, gb);
-  return hipGetLastError();
+  if constexpr (DK >= 64) {
+    ChunkWs cw{reinterpret_cast<float*>(ws + w.W), reinterpret_cast<float*>(ws + w.U),
+               reinterpret_cast<float*>(ws + w.P), reinterpret_cast<float*>(ws + w.G)};
+    return launch_chunked(a, DK, DV, y, ga, gb, cw, s);
+  } else {
+    constexpr int RB = (kThreads / 64) * (64 / (DK / 16));
+    dim3 g3((DV + RB - 1) / RB, a.Hv, a.num_rows);
+    hipLaunchKernelGGL((delta_prefill_kernel<DK, DV>), g3, dim3(kThreads), 0, s, a, y, kq, ga, gb);
+    return hipGetLastError();
+  }
 }
 
 }  // namespace

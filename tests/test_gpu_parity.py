@@ -155,3 +155,60 @@ def test_nonspec_prefill_lengths(lens, his):
     assert_out_close(g.host_out(), out_ref)
     np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
     assert_states_close(g.host_ssm(slots), ssm_ref[slots])
+
+
+def _prefill_case(seed, lens, his, dk=128, Hk=16, Hv=32, tweak=None):
+    nd = sum(1 for l in lens if l == 1)
+    T = sum(lens)
+    case = helpers.small_case(seed=seed, Hk=Hk, Hv=Hv, dk=dk, dv=dk, K=4, T=T, num_slots=16)
+    if tweak:
+        tweak(case)
+    slots = list(range(3, 3 + len(lens)))
+    tix = np.random.default_rng(seed).permutation(T).astype(np.int32)
+    case["nonspec"] = helpers.nonspec_meta(lens, slots, his=his, tix=tix, num_decodes=nd)
+    case["spec"] = None
+    case["name"] = "prefill"
+    return case, slots
+
+
+def _check_nonspec(case, slots):
+    out_ref, conv_ref, ssm_ref, _ = helpers.run_nonspec(case)
+    g = Gpu(case)
+    say(f"prefill rows {case['nonspec']['query_start_loc'].tolist()} dk={case['dims']['dk']}")
+    g.attention()
+    assert_out_close(g.host_out(), out_ref)
+    np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
+    assert_states_close(g.host_ssm(slots), ssm_ref[slots])
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+def test_chunked_prefill_chunk_edges(dk):
+    # Rows ending one short of, on, and one past a 64-token chunk, a short
+    # row, and a 1024-token row; with and without an initial state.
+    case, slots = _prefill_case(30 + dk, [63, 64, 65, 5, 1024], [1, 0, 1, 1, 0], dk=dk, Hk=4, Hv=8)
+    _check_nonspec(case, slots)
+
+
+def test_chunked_prefill_strong_decay():
+    # log-decays down to about -16 per token (about -1000 per chunk): only
+    # decay differences are exponentiated, so nothing overflows.
+    def tweak(c):
+        c["A_log"][:] = np.float32(np.log(16.0))
+        c["a"][:] = synth.to_bf16(np.abs(synth.from_bf16(c["a"])) + 2.0)
+    case, slots = _prefill_case(41, [200, 130], [1, 1], Hk=4, Hv=8, tweak=tweak)
+    _check_nonspec(case, slots)
+
+
+def test_chunked_prefill_no_decay_parallel_keys():
+    # decay 1 and write strength near 1 with nearly parallel keys: the
+    # (I + A)^-1 solve is at its least well conditioned.
+    def tweak(c):
+        c["A_log"][:] = -np.inf
+        c["b"][:] = synth.to_bf16(np.full(c["b"].shape, 4.0, np.float32))
+        Hk, dk = 4, 128
+        x = synth.from_bf16(c["mixed_qkv"]).copy()
+        base = x[0, Hk * dk:2 * Hk * dk].copy()
+        x[:, Hk * dk:2 * Hk * dk] = base + 0.05 * x[:, Hk * dk:2 * Hk * dk]
+        c["mixed_qkv"] = synth.to_bf16(x)
+    case, slots = _prefill_case(42, [150], [1], Hk=4, Hv=8, tweak=tweak)
+    _check_nonspec(case, slots)
