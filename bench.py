@@ -57,6 +57,43 @@ def algorithmic_bytes(case) -> int:
     return int(total)
 
 
+def nonspec_bytes(case) -> int:
+    """Bytes the non-spec rows must move (decodes and prefills): inputs,
+    gates and outputs of their tokens, ring read/rewrite, the initial state
+    when it is read and the final state."""
+    d, ns = case["dims"], case["nonspec"]
+    Hk, Hv, dk, dv, W, L = d["Hk"], d["Hv"], d["dk"], d["dv"], d["W"], d["L"]
+    C = 2 * Hk * dk + Hv * dv
+    tile = Hv * dv * dk * 4
+    T = ns["num_non_spec_tokens"]
+    total = T * C * 2 + 2 * T * Hv * 2 + T * Hv * dv * 2 + 4 * T
+    qsl, slots = ns["query_start_loc"], ns["cache_indices"]
+    his = ns.get("has_initial_state")
+    for i in range(ns["num_decodes"] + ns["num_prefills"]):
+        Ti = int(qsl[i + 1] - qsl[i])
+        c = int(slots[i])
+        init = (his is None or his[i]) and c > 0
+        if c > 0:
+            total += ((W - 1 + max(L - Ti, 0)) if init else 0) * C * 2 + L * C * 2 + tile
+        if init:
+            total += tile
+    return int(total)
+
+
+def chunked_flops(case) -> int:
+    """Multiply-adds x 2 of the chunked prefill form (64-token chunks)."""
+    d, ns = case["dims"], case["nonspec"]
+    Hv, dk, dv = d["Hv"], d["dk"], d["dv"]
+    qsl = ns["query_start_loc"]
+    total = 0
+    for i in range(ns["num_decodes"], ns["num_decodes"] + ns["num_prefills"]):
+        nch = -(-int(qsl[i + 1] - qsl[i]) // 64)
+        # K K^T, Q K^T, W, U~ (prep); W S^T, Q S^T, P U, state update (state pass)
+        per = 2 * 64 * 64 * dk + 64 * 64 * (dk + dv) + 64 * dk * dv * 3 + 64 * 64 * dv
+        total += 2 * nch * Hv * per
+    return int(total)
+
+
 def cpu_baseline(case, min_seconds=10.0):
     """The oracle (single-threaded C, fp64) on the whole batch, repeated until
     at least ``min_seconds`` of CPU time has been spent."""
@@ -124,39 +161,58 @@ def main():
 
     import speculative_decoding_causal_amd as gdn
     import synth
-    from tests.gpu_util import bf, f32, i32
+    from tests.gpu_util import bf, f32, i32, u8
 
     case = synth.make_case(args.workload, seed=args.seed)
-    d, sp = case["dims"], case["spec"]
+    d, sp, ns = case["dims"], case["spec"], case.get("nonspec")
     cfg = gdn.GdnConfig(d["Hk"], d["Hv"], d["dk"], d["dv"], d["W"], d["activation"],
                         d["use_qk_l2norm"], d["eps"], d["scale"])
     dev = torch.device("cuda:0")
-    T = sp["num_spec_tokens"]
+    T_spec = sp["num_spec_tokens"]
+    T_all = case["num_actual_tokens"]
     meta = dict(sqsl=i32(sp["spec_query_start_loc"]), ssi=i32(sp["spec_state_indices"]),
                 nacc=i32(sp["num_accepted_tokens"]), tix=i32(sp.get("spec_token_indx")),
                 cache=i32(sp.get("spec_cache_indices")))
+    if ns is not None:
+        meta.update(qsl=i32(ns["query_start_loc"]), nsi=i32(ns["cache_indices"]),
+                    his=u8(ns.get("has_initial_state")), ntix=i32(ns.get("token_indx")))
+        ws_bytes = gdn.gdn_workspace_bytes(cfg, d["L"], d["num_slots"],
+                                           ns["num_non_spec_tokens"], ns["num_prefills"])
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     conv0, ssm0 = bf(case["conv_state"]), f32(case["ssm_state"])
     w, A_log, dt_bias = bf(case["conv_weight"]), f32(case["A_log"]), f32(case["dt_bias"])
     layers = []
     g = torch.Generator(device="cpu").manual_seed(args.seed)
     for li in range(args.layers):
-        perm = torch.randperm(case["num_actual_tokens"], generator=g)
+        perm = torch.randperm(T_all, generator=g)
         qkv = bf(case["mixed_qkv"])[perm.to(dev)].contiguous()
         layers.append(dict(qkv=qkv, a=bf(case["a"]), b=bf(case["b"]),
                            conv=conv0.clone(), ssm=ssm0.clone(),
-                           out=torch.empty(case["num_actual_tokens"], d["Hv"], d["dv"],
+                           out=torch.empty(T_all, d["Hv"], d["dv"],
                                            dtype=torch.bfloat16, device=dev)))
     del conv0, ssm0
     torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream()
 
     def step(i):
         L = layers[i % len(layers)]
-        gdn.gdn_spec_attention(cfg, L["qkv"], L["a"], L["b"], w, None, A_log, dt_bias,
-                               L["conv"], L["ssm"], meta["sqsl"], meta["ssi"], meta["nacc"],
-                               L["out"], spec_cache_indices=meta["cache"],
-                               spec_token_indx=meta["tix"], num_spec_tokens=T, stream=stream)
+        if ns is None:
+            gdn.gdn_spec_attention(cfg, L["qkv"], L["a"], L["b"], w, None, A_log, dt_bias,
+                                   L["conv"], L["ssm"], meta["sqsl"], meta["ssi"], meta["nacc"],
+                                   L["out"], spec_cache_indices=meta["cache"],
+                                   spec_token_indx=meta["tix"], num_spec_tokens=T_spec,
+                                   stream=stream)
+        else:
+            gdn.gdn_attention(cfg, L["qkv"], L["a"], L["b"], w, None, A_log, dt_bias,
+                              L["conv"], L["ssm"], L["out"], num_decodes=ns["num_decodes"],
+                              num_prefills=ns["num_prefills"],
+                              num_non_spec_tokens=ns["num_non_spec_tokens"],
+                              query_start_loc=meta["qsl"], non_spec_state_indices=meta["nsi"],
+                              has_initial_state=meta["his"], non_spec_token_indx=meta["ntix"],
+                              spec_query_start_loc=meta["sqsl"], spec_state_indices=meta["ssi"],
+                              num_accepted_tokens=meta["nacc"], spec_cache_indices=meta["cache"],
+                              spec_token_indx=meta["tix"], num_spec_tokens=T_spec,
+                              workspace=workspace, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -180,14 +236,17 @@ def main():
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    avg_launch_s = float(launch_ms.mean()) * 1e-3
-    nbytes = algorithmic_bytes(case)
+    # Kernel time per launch over the timed region (one launch per step for
+    # the spec workload); the per-launch event pairs give the spread.
+    avg_launch_s = ms_per_step * 1e-3
+    nbytes = algorithmic_bytes(case) + (nonspec_bytes(case) if ns is not None else 0)
     achieved = nbytes / avg_launch_s / 1e9
-    traffic = profiled_traffic()
+    traffic = profiled_traffic() if ns is None else None
+    tokens = T_all if ns is not None else T_spec
 
     result = {
         "metric": METRIC,
-        "value": T / (ms_per_step * 1e-3),
+        "value": tokens / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -201,7 +260,7 @@ def main():
         "dtype": "fp32",
         "data": "synthetic",
         "config": {"workload": args.workload, "spec_rows": sp["num_spec_decodes"], "K": sp["K"],
-                   "tokens_per_step": T, "num_k_heads": d["Hk"], "num_v_heads": d["Hv"],
+                   "tokens_per_step": tokens, "num_k_heads": d["Hk"], "num_v_heads": d["Hv"],
                    "head_k_dim": d["dk"], "head_v_dim": d["dv"], "conv_width": d["W"],
                    "state_len": d["L"], "num_slots": d["num_slots"],
                    "layers_cycled": args.layers, "parallelism": "single GPU"},
@@ -213,7 +272,13 @@ def main():
                      "p10_launch_us": float(np.percentile(launch_ms, 10)) * 1e3,
                      "p90_launch_us": float(np.percentile(launch_ms, 90)) * 1e3},
     }
-    if not args.no_cpu_baseline:
+    if ns is not None:
+        result["metric"] = "GDN layer tokens/sec on a mixed spec/decode/prefill batch"
+        result["config"].update(decode_rows=ns["num_decodes"], prefill_rows=ns["num_prefills"],
+                                non_spec_tokens=ns["num_non_spec_tokens"])
+        result["roofline"]["kernel"] = "whole step (6 kernels); see the rocprofv3 profile"
+        result["chunked_prefill_gflop"] = chunked_flops(case) / 1e9
+    if not args.no_cpu_baseline and ns is None:
         result["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(result), flush=True)
 

@@ -52,13 +52,40 @@ __device__ __forceinline__ PRow prow(const PrefillArgs& p, int row) {
   return r;
 }
 
-// Shared-memory carve-up of chunk_prep_kernel (floats, rows padded by one so
-// that MFMA operand reads down a column hit distinct banks).
+// Rows of ROWS x COLS floats gathered in one batch of float4 loads (rows
+// >= nrow read as zeros), then written to LDS with row pitch PITCH.
+template <int ROWS, int COLS>
+struct Tile4 {
+  static constexpr int kPer = ROWS * COLS / 4 / 256;  // float4 per thread
+  v4f v[kPer];
+  template <class RowPtr>
+  __device__ __forceinline__ void load(RowPtr row_ptr, int nrow) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = (i * 256 + (int)threadIdx.x) * 4;
+      const int r = e / COLS, c = e - r * COLS;
+      v[i] = r < nrow ? *reinterpret_cast<const v4f*>(row_ptr(r) + c) : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  template <int PITCH>
+  __device__ __forceinline__ void store(float* lds) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = (i * 256 + (int)threadIdx.x) * 4;
+      const int r = e / COLS, c = e - r * COLS;
+      *reinterpret_cast<v4f*>(lds + r * PITCH + c) = v[i];
+    }
+  }
+};
+
+// Shared-memory carve-up of chunk_prep_kernel (floats; rows padded by four
+// so that MFMA operand reads down a column spread over the banks and rows
+// stay 16-byte aligned).
 template <int DK>
 struct PrepLds {
-  static constexpr int ks = 0;                         // [kC][DK+1] keys
-  static constexpr int qs = ks + kC * (DK + 1);        // [kC][DK+1] queries, then values
-  static constexpr int as = qs + kC * (DK + 1);        // [kC][kC+1] A, then T
+  static constexpr int ks = 0;                         // [kC][DK+4] keys
+  static constexpr int qs = ks + kC * (DK + 4);        // [kC][DK+4] queries, then values
+  static constexpr int as = qs + kC * (DK + 4);        // [kC][kC+1] A, then T
   static constexpr int gs = as + kC * (kC + 1);        // [kC] cumulative log-decay
   static constexpr int bs = gs + kC;                   // [kC] beta
   static constexpr int bg = bs + kC;                   // [kC] beta e^G
@@ -78,7 +105,7 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   float* Gs = sm + Lay::gs;
   float* Bs = sm + Lay::bs;
   float* BG = sm + Lay::bg;
-  constexpr int KP = DK + 1, AP = kC + 1;
+  constexpr int KP = DK + 4, AP = kC + 1;
 
   const int c = blockIdx.x, h = blockIdx.y;
   const PRow pr = prow(p, blockIdx.z);
@@ -88,13 +115,20 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   const int jb = pr.j0 + t0;
   const int ih = h / p.G, Hk = p.Hk, Hv = p.Hv, C = p.C;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  Tile4<kC, DV> vpark;
 
-  // 1. keys and queries of the chunk (normalised in the workspace), gates
-  for (int idx = tid; idx < kC * DK; idx += 256) {
-    const int t = idx / DK, k = idx - t * DK;
-    const float* yr = y + (size_t)(jb + t) * C;
-    Ks[t * KP + k] = t < nt ? yr[Hk * DK + ih * DK + k] : 0.f;
-    Qs[t * KP + k] = t < nt ? yr[ih * DK + k] : 0.f;
+  // 1. keys, queries and values of the chunk (normalised q/k in the
+  //    workspace), gathered in one batch; gates
+  {
+    Tile4<kC, DK> tk, tq, tv;
+    const float* yb = y + (size_t)jb * C;
+    tk.load([&](int r) { return yb + (size_t)r * C + Hk * DK + ih * DK; }, nt);
+    tq.load([&](int r) { return yb + (size_t)r * C + ih * DK; }, nt);
+    tv.load([&](int r) { return yb + (size_t)r * C + 2 * Hk * DK + h * DV; }, nt);
+    tk.template store<KP>(Ks);
+    tq.template store<KP>(Qs);
+    // values wait in registers until Q K^T is done
+    vpark = tv;
   }
   if (tid < kC) {
     Gs[tid] = tid < nt ? glog[(size_t)(jb + tid) * Hv + h] : 0.f;
@@ -151,10 +185,7 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
     for (int t = 0; t < kC; ++t) As[t * AP + lane] = X[t];
   }
   // values replace the queries (Q K^T is done)
-  for (int idx = tid; idx < kC * DV; idx += 256) {
-    const int t = idx / DV, k = idx - t * DV;
-    Qs[t * KP + k] = t < nt ? y[(size_t)(jb + t) * C + 2 * Hk * DK + h * DV + k] : 0.f;
-  }
+  vpark.template store<KP>(Qs);
   __syncthreads();
   // 5. W = T diag(b e^G) K and U~ = T diag(b) V; wave w owns token tile w
   {
@@ -185,11 +216,11 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
 // Shared memory of chunk_state_kernel.
 template <int DK>
 struct StateLds {
-  static constexpr int wl = 0;                    // [kC][DK+1] W of the chunk
-  static constexpr int ql = wl + kC * (DK + 1);   // [kC][DK+1] queries
-  static constexpr int kl = ql + kC * (DK + 1);   // [kC][DK+1] keys
-  static constexpr int pl = kl + kC * (DK + 1);   // [kC][kC+1] P
-  static constexpr int ss = pl + kC * (kC + 1);   // [16][DK+1] state block
+  static constexpr int wl = 0;                    // [kC][DK+4] W of the chunk
+  static constexpr int ql = wl + kC * (DK + 4);   // [kC][DK+4] queries
+  static constexpr int kl = ql + kC * (DK + 4);   // [kC][DK+4] keys
+  static constexpr int pl = kl + kC * (DK + 4);   // [kC][kC+4] P
+  static constexpr int ss = pl + kC * (kC + 4);   // [16][DK+1] state block
   static constexpr int us = ss + 16 * (DK + 1);   // [kC][17] U block
   static constexpr int gc = us + kC * 17;         // [kC] G
   static constexpr int total = gc + kC;
@@ -208,7 +239,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   float* Ss = sm + Lay::ss;
   float* Us = sm + Lay::us;
   float* Gc = sm + Lay::gc;
-  constexpr int KP = DK + 1, AP = kC + 1, UP = 17;
+  constexpr int KP = DK + 4, AP = kC + 4, SP = DK + 1, UP = 17;
   constexpr int TPW = (DK / 16) / 4;  // state tiles per wave
 
   const int Hv = p.Hv, Hk = p.Hk, C = p.C;
@@ -231,28 +262,33 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
                          : 0.f;
 
   const int nch = (pr.T + kC - 1) / kC;
+  // Operands of chunk c+1 are gathered while chunk c is computed.
+  Tile4<kC, DK> tw, tq, tk;
+  Tile4<kC, kC> tp;
+  auto gather = [&](int c) {
+    const int jb = pr.j0 + c * kC;
+    const int nt = min(kC, pr.T - c * kC);
+    const float* yb = y + (size_t)jb * C;
+    tw.load([&](int r) { return ws.W + ((size_t)(jb + r) * Hv + h) * DK; }, nt);
+    tq.load([&](int r) { return yb + (size_t)r * C + ih * DK; }, nt);
+    tk.load([&](int r) { return yb + (size_t)r * C + Hk * DK + ih * DK; }, nt);
+    tp.load([&](int r) { return ws.P + ((size_t)(jb + r) * Hv + h) * kC; }, nt);
+  };
+  gather(0);
   for (int c = 0; c < nch; ++c) {
     const int jb = pr.j0 + c * kC;
     const int nt = min(kC, pr.T - c * kC);
-    // stage the chunk's operands and the current state block
-    for (int idx = tid; idx < kC * DK; idx += 256) {
-      const int t = idx / DK, k = idx - t * DK;
-      const bool v = t < nt;
-      const size_t hw = ((size_t)(jb + t) * Hv + h) * DK + k;
-      const float* yr = y + (size_t)(jb + t) * C;
-      Wl[t * KP + k] = v ? ws.W[hw] : 0.f;
-      Ql[t * KP + k] = v ? yr[ih * DK + k] : 0.f;
-      Kl[t * KP + k] = v ? yr[Hk * DK + ih * DK + k] : 0.f;
-    }
-    for (int idx = tid; idx < kC * kC; idx += 256) {
-      const int t = idx / kC, s = idx - t * kC;
-      Pl[t * AP + s] = t < nt ? ws.P[((size_t)(jb + t) * Hv + h) * kC + s] : 0.f;
-    }
+    tw.template store<KP>(Wl);
+    tq.template store<KP>(Ql);
+    tk.template store<KP>(Kl);
+    tp.template store<AP>(Pl);
     if (tid < kC) Gc[tid] = ws.G[(size_t)(jb + (tid < nt ? tid : nt - 1)) * Hv + h];
 #pragma unroll
     for (int q = 0; q < TPW; ++q)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Ss[(4 * lk + r) * KP + 16 * (wv * TPW + q) + li] = St[q][r];
+      for (int r = 0; r < 4; ++r) Ss[(4 * lk + r) * SP + 16 * (wv * TPW + q) + li] = St[q][r];
+    __syncthreads();
+    if (c + 1 < nch) gather(c + 1);
     __syncthreads();
 
     // (a) U = U~ - W S0^T for token tile wv
@@ -260,7 +296,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
       v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
       for (int k0 = 0; k0 < DK; k0 += 4)
-        acc = mfma4(Wl[(16 * wv + li) * KP + k0 + lk], Ss[li * KP + k0 + lk], acc);
+        acc = mfma4(Wl[(16 * wv + li) * KP + k0 + lk], Ss[li * SP + k0 + lk], acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * wv + 4 * lk + r;
@@ -276,7 +312,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
       v4f aq = {0.f, 0.f, 0.f, 0.f}, ap = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
       for (int k0 = 0; k0 < DK; k0 += 4)
-        aq = mfma4(Ql[(16 * wv + li) * KP + k0 + lk], Ss[li * KP + k0 + lk], aq);
+        aq = mfma4(Ql[(16 * wv + li) * KP + k0 + lk], Ss[li * SP + k0 + lk], aq);
 #pragma unroll 4
       for (int s0 = 0; s0 < kC; s0 += 4)
         ap = mfma4(Pl[(16 * wv + li) * AP + s0 + lk], Us[(s0 + lk) * UP + li], ap);
