@@ -78,17 +78,37 @@ struct Tile4 {
   }
 };
 
-// Shared-memory carve-up of chunk_prep_kernel (floats; rows padded by four
-// so that MFMA operand reads down a column spread over the banks and rows
-// stay 16-byte aligned).
+// N consecutive floats of LDS (16-byte aligned) into registers.
+template <int N>
+__device__ __forceinline__ void lds_run(float (&dst)[N], const float* src) {
+  static_assert(N % 4 == 0, "runs of float4");
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    const v4f v = *reinterpret_cast<const v4f*>(src + 4 * i);
+    dst[4 * i] = v.x;
+    dst[4 * i + 1] = v.y;
+    dst[4 * i + 2] = v.z;
+    dst[4 * i + 3] = v.w;
+  }
+}
+
+// Operand feeding: the sum over k is split so that lane group kk = lane/16
+// owns the contiguous range k = kk*(K/4) + m of every MFMA step m; both
+// operands use the same split, so each lane reads its operands for all K/4
+// steps as one contiguous run.
+
+// Shared-memory carve-up of chunk_prep_kernel (floats).  Row pitches are
+// padded by four: rows stay 16-byte aligned and column reads spread over
+// the banks.
 template <int DK>
 struct PrepLds {
-  static constexpr int ks = 0;                         // [kC][DK+4] keys
-  static constexpr int qs = ks + kC * (DK + 4);        // [kC][DK+4] queries, then values
-  static constexpr int as = qs + kC * (DK + 4);        // [kC][kC+1] A, then T
-  static constexpr int gs = as + kC * (kC + 1);        // [kC] cumulative log-decay
-  static constexpr int bs = gs + kC;                   // [kC] beta
-  static constexpr int bg = bs + kC;                   // [kC] beta e^G
+  static constexpr int KP = DK + 4, CP = kC + 4;
+  static constexpr int ks = 0;                          // [kC][KP]  keys
+  static constexpr int qv = ks + kC * KP;               // [kC][KP]  queries, then values
+  static constexpr int ts = qv + kC * KP;               // [kC][CP]  A, then T
+  static constexpr int gs = ts + kC * CP;               // [kC] cumulative log-decay
+  static constexpr int bs = gs + kC;                    // [kC] beta
+  static constexpr int bg = bs + kC;                    // [kC] beta e^G
   static constexpr int total = bg + kC;
 };
 
@@ -99,13 +119,15 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   static_assert(DK == DV, "dk == dv");
   extern __shared__ __align__(16) float sm[];
   using Lay = PrepLds<DK>;
+  constexpr int KP = Lay::KP, CP = Lay::CP;
+  constexpr int KQ = DK / 4;   // k-run per lane group, Gram products
+  constexpr int SQ = kC / 4;   // k-run per lane group, products over tokens
   float* Ks = sm + Lay::ks;
-  float* Qs = sm + Lay::qs;
-  float* As = sm + Lay::as;
+  float* QV = sm + Lay::qv;
+  float* Ts = sm + Lay::ts;
   float* Gs = sm + Lay::gs;
   float* Bs = sm + Lay::bs;
   float* BG = sm + Lay::bg;
-  constexpr int KP = DK + 4, AP = kC + 1;
 
   const int c = blockIdx.x, h = blockIdx.y;
   const PRow pr = prow(p, blockIdx.z);
@@ -115,20 +137,18 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   const int jb = pr.j0 + t0;
   const int ih = h / p.G, Hk = p.Hk, Hv = p.Hv, C = p.C;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  Tile4<kC, DV> vpark;
+  const int li = lane & 15, lk = lane >> 4;
 
-  // 1. keys, queries and values of the chunk (normalised q/k in the
-  //    workspace), gathered in one batch; gates
+  // 1. keys, queries and values of the chunk gathered in one batch
+  Tile4<kC, DV> tv;
   {
-    Tile4<kC, DK> tk, tq, tv;
+    Tile4<kC, DK> tk, tq;
     const float* yb = y + (size_t)jb * C;
     tk.load([&](int r) { return yb + (size_t)r * C + Hk * DK + ih * DK; }, nt);
     tq.load([&](int r) { return yb + (size_t)r * C + ih * DK; }, nt);
     tv.load([&](int r) { return yb + (size_t)r * C + 2 * Hk * DK + h * DV; }, nt);
     tk.template store<KP>(Ks);
-    tq.template store<KP>(Qs);
-    // values wait in registers until Q K^T is done
-    vpark = tv;
+    tq.template store<KP>(QV);
   }
   if (tid < kC) {
     Gs[tid] = tid < nt ? glog[(size_t)(jb + tid) * Hv + h] : 0.f;
@@ -147,63 +167,78 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
     BG[lane] = Bs[lane] * expf(g);
   }
   __syncthreads();
-  // 3. K K^T and Q K^T, 16x16 tiles; wave w owns token-row tile w
+  // 3. K K^T and Q K^T: wave w owns token-row tile w
   {
-    const int i = lane & 15, kk = lane >> 4;
+    float ak[KQ], aq[KQ];
+    lds_run<KQ>(ak, Ks + (16 * wv + li) * KP + lk * KQ);
+    lds_run<KQ>(aq, QV + (16 * wv + li) * KP + lk * KQ);
     for (int tj = 0; tj < 4; ++tj) {
+      float bk[KQ];
+      lds_run<KQ>(bk, Ks + (16 * tj + li) * KP + lk * KQ);
       v4f akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-      for (int k0 = 0; k0 < DK; k0 += 4) {
-        const float ka = Ks[(16 * wv + i) * KP + k0 + kk];
-        const float qa = Qs[(16 * wv + i) * KP + k0 + kk];
-        const float kb = Ks[(16 * tj + i) * KP + k0 + kk];
-        akk = mfma4(ka, kb, akk);
-        aqk = mfma4(qa, kb, aqk);
+#pragma unroll
+      for (int m = 0; m < KQ; ++m) {
+        akk = mfma4(ak[m], bk[m], akk);
+        aqk = mfma4(aq[m], bk[m], aqk);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * wv + 4 * kk + r, s = 16 * tj + i;
+        const int t = 16 * wv + 4 * lk + r, s = 16 * tj + li;
         const float dec = expf(Gs[t] - Gs[s < t ? s : t]);
-        As[t * AP + s] = s < t ? Bs[t] * dec * akk[r] : 0.f;
+        Ts[t * CP + s] = s < t ? Bs[t] * dec * akk[r] : 0.f;
         if (t < nt)
           ws.P[((size_t)(jb + t) * Hv + h) * kC + s] = s <= t ? dec * aqk[r] : 0.f;
       }
     }
   }
   __syncthreads();
-  // 4. T = (I + A)^{-1}: lane j of wave 0 solves column j by forward substitution
+  // 4. T = (I + A)^{-1}: lane j of wave 0 solves column j by forward
+  //    substitution (four partial sums per row); the values replace the
+  //    queries.
   if (wv == 0) {
     float X[kC];
 #pragma unroll
     for (int t = 0; t < kC; ++t) {
-      float x = (t == lane) ? 1.f : 0.f;
+      float x0 = (t == lane) ? 1.f : 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
 #pragma unroll
-      for (int s = 0; s < t; ++s) x = fmaf(-As[t * AP + s], X[s], x);
-      X[t] = x;
+      for (int s = 0; s < t; ++s) {
+        const float a = Ts[t * CP + s];
+        if ((s & 3) == 0) x0 = fmaf(-a, X[s], x0);
+        else if ((s & 3) == 1) x1 = fmaf(-a, X[s], x1);
+        else if ((s & 3) == 2) x2 = fmaf(-a, X[s], x2);
+        else x3 = fmaf(-a, X[s], x3);
+      }
+      X[t] = (x0 + x1) + (x2 + x3);
     }
 #pragma unroll
-    for (int t = 0; t < kC; ++t) As[t * AP + lane] = X[t];
+    for (int t = 0; t < kC; ++t) Ts[t * CP + lane] = X[t];
   }
-  // values replace the queries (Q K^T is done)
-  vpark.template store<KP>(Qs);
+  tv.template store<KP>(QV);
   __syncthreads();
-  // 5. W = T diag(b e^G) K and U~ = T diag(b) V; wave w owns token tile w
+  // 5. W = T diag(b e^G) K and U~ = T diag(b) V: wave w owns token tile w.
+  //    The sum over tokens s takes the interleaved split s = 4m + lane/16, so
+  //    the key/value operand is a row-major read spread over the banks.
   {
-    const int i = lane & 15, kk = lane >> 4;
+    float at[SQ], bgr[SQ], br[SQ];
+#pragma unroll
+    for (int m = 0; m < SQ; ++m) {
+      at[m] = Ts[(16 * wv + li) * CP + 4 * m + lk];
+      bgr[m] = BG[4 * m + lk];
+      br[m] = Bs[4 * m + lk];
+    }
     for (int n = 0; n < DK / 16; ++n) {
       v4f aw = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int s0 = 0; s0 < kC; s0 += 4) {
-        const int s = s0 + kk;
-        const float ta = As[(16 * wv + i) * AP + s];
-        aw = mfma4(ta, BG[s] * Ks[s * KP + 16 * n + i], aw);
-        au = mfma4(ta, Bs[s] * Qs[s * KP + 16 * n + i], au);
+#pragma unroll
+      for (int m = 0; m < SQ; ++m) {
+        const int srow = (4 * m + lk) * KP + 16 * n + li;
+        aw = mfma4(at[m], bgr[m] * Ks[srow], aw);
+        au = mfma4(at[m], br[m] * QV[srow], au);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * wv + 4 * kk + r;
+        const int t = 16 * wv + 4 * lk + r;
         if (t < nt) {
-          const size_t o = ((size_t)(jb + t) * Hv + h) * DK + 16 * n + i;
+          const size_t o = ((size_t)(jb + t) * Hv + h) * DK + 16 * n + li;
           ws.W[o] = aw[r];
           ws.U[o] = au[r];
         }
@@ -213,16 +248,19 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   if (tid < nt) ws.G[(size_t)(jb + tid) * Hv + h] = Gs[tid];
 }
 
-// Shared memory of chunk_state_kernel.
+// Shared memory of chunk_state_kernel (floats).
 template <int DK>
 struct StateLds {
-  static constexpr int wl = 0;                    // [kC][DK+4] W of the chunk
-  static constexpr int ql = wl + kC * (DK + 4);   // [kC][DK+4] queries
-  static constexpr int kl = ql + kC * (DK + 4);   // [kC][DK+4] keys
-  static constexpr int pl = kl + kC * (DK + 4);   // [kC][kC+4] P
-  static constexpr int ss = pl + kC * (kC + 4);   // [16][DK+1] state block
-  static constexpr int us = ss + 16 * (DK + 1);   // [kC][17] U block
-  static constexpr int gc = us + kC * 17;         // [kC] G
+  static constexpr int KP = DK + 4, CP = kC + 4;
+  static constexpr int wl = 0;                    // [kC][KP] W of the chunk
+  static constexpr int ql = wl + kC * KP;         // [kC][KP] queries
+  static constexpr int kl = ql + kC * KP;         // [kC][KP] keys
+  static constexpr int pl = kl + kC * KP;         // [kC][CP] P
+  static constexpr int ul = pl + kC * CP;         // [kC][16] U~ block
+  static constexpr int ss = ul + kC * 16;         // [16][KP] state block
+  static constexpr int ut = ss + 16 * KP;         // [16][CP] U^T block
+  static constexpr int uts = ut + 16 * CP;        // [16][CP] U^T diag(e^{G_C - G})
+  static constexpr int gc = uts + 16 * CP;        // [kC] G
   static constexpr int total = gc + kC;
 };
 
@@ -232,15 +270,18 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   static_assert(DK == DV && DK % 64 == 0, "dk == dv, multiple of 64");
   extern __shared__ __align__(16) float sm[];
   using Lay = StateLds<DK>;
+  constexpr int KP = Lay::KP, CP = Lay::CP;
+  constexpr int KQ = DK / 4, SQ = kC / 4;
+  constexpr int TPW = (DK / 16) / 4;  // state tiles per wave
   float* Wl = sm + Lay::wl;
   float* Ql = sm + Lay::ql;
   float* Kl = sm + Lay::kl;
   float* Pl = sm + Lay::pl;
+  float* Ul = sm + Lay::ul;
   float* Ss = sm + Lay::ss;
-  float* Us = sm + Lay::us;
+  float* UT = sm + Lay::ut;
+  float* UTs = sm + Lay::uts;
   float* Gc = sm + Lay::gc;
-  constexpr int KP = DK + 4, AP = kC + 4, SP = DK + 1, UP = 17;
-  constexpr int TPW = (DK / 16) / 4;  // state tiles per wave
 
   const int Hv = p.Hv, Hk = p.Hk, C = p.C;
   const int row = blockIdx.x / Hv, h = blockIdx.x - row * Hv;
@@ -265,6 +306,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   // Operands of chunk c+1 are gathered while chunk c is computed.
   Tile4<kC, DK> tw, tq, tk;
   Tile4<kC, kC> tp;
+  Tile4<kC, 16> tu;
   auto gather = [&](int c) {
     const int jb = pr.j0 + c * kC;
     const int nt = min(kC, pr.T - c * kC);
@@ -273,6 +315,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
     tq.load([&](int r) { return yb + (size_t)r * C + ih * DK; }, nt);
     tk.load([&](int r) { return yb + (size_t)r * C + Hk * DK + ih * DK; }, nt);
     tp.load([&](int r) { return ws.P + ((size_t)(jb + r) * Hv + h) * kC; }, nt);
+    tu.load([&](int r) { return ws.U + ((size_t)(jb + r) * Hv + h) * DV + 16 * blk; }, nt);
   };
   gather(0);
   for (int c = 0; c < nch; ++c) {
@@ -281,47 +324,56 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
     tw.template store<KP>(Wl);
     tq.template store<KP>(Ql);
     tk.template store<KP>(Kl);
-    tp.template store<AP>(Pl);
+    tp.template store<CP>(Pl);
+    tu.template store<16>(Ul);
     if (tid < kC) Gc[tid] = ws.G[(size_t)(jb + (tid < nt ? tid : nt - 1)) * Hv + h];
 #pragma unroll
     for (int q = 0; q < TPW; ++q)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Ss[(4 * lk + r) * SP + 16 * (wv * TPW + q) + li] = St[q][r];
+      for (int r = 0; r < 4; ++r) Ss[(4 * lk + r) * KP + 16 * (wv * TPW + q) + li] = St[q][r];
     __syncthreads();
     if (c + 1 < nch) gather(c + 1);
-    __syncthreads();
 
-    // (a) U = U~ - W S0^T for token tile wv
+    const float gC = Gc[kC - 1];
+    // B operand of S0^T products: S[j][k] for this lane's k-run
+    float sb[KQ];
+    lds_run<KQ>(sb, Ss + li * KP + lk * KQ);
+    // (a) U = U~ - W S0^T for token tile wv; U^T kept plain and decay-scaled
     {
+      float aw[KQ];
+      lds_run<KQ>(aw, Wl + (16 * wv + li) * KP + lk * KQ);
       v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-      for (int k0 = 0; k0 < DK; k0 += 4)
-        acc = mfma4(Wl[(16 * wv + li) * KP + k0 + lk], Ss[li * SP + k0 + lk], acc);
+#pragma unroll
+      for (int m = 0; m < KQ; ++m) acc = mfma4(aw[m], sb[m], acc);
+      v4f u, us;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * wv + 4 * lk + r;
-        const float ut =
-            t < nt ? ws.U[((size_t)(jb + t) * Hv + h) * DV + 16 * blk + li] : 0.f;
-        Us[t * UP + li] = t < nt ? ut - acc[r] : 0.f;
+        u[r] = t < nt ? Ul[t * 16 + li] - acc[r] : 0.f;
+        us[r] = u[r] * expf(gC - Gc[t]);
       }
+      *reinterpret_cast<v4f*>(UT + li * CP + 16 * wv + 4 * lk) = u;
+      *reinterpret_cast<v4f*>(UTs + li * CP + 16 * wv + 4 * lk) = us;
     }
     __syncthreads();
 
     // (b) outputs of token tile wv: e^{G_t} (Q S0^T)[t] + (P U)[t]
     {
+      float aqr[KQ], apr[SQ], ubr[SQ];
+      lds_run<KQ>(aqr, Ql + (16 * wv + li) * KP + lk * KQ);
+      lds_run<SQ>(apr, Pl + (16 * wv + li) * CP + lk * SQ);
+      lds_run<SQ>(ubr, UT + li * CP + lk * SQ);
       v4f aq = {0.f, 0.f, 0.f, 0.f}, ap = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-      for (int k0 = 0; k0 < DK; k0 += 4)
-        aq = mfma4(Ql[(16 * wv + li) * KP + k0 + lk], Ss[li * SP + k0 + lk], aq);
-#pragma unroll 4
-      for (int s0 = 0; s0 < kC; s0 += 4)
-        ap = mfma4(Pl[(16 * wv + li) * AP + s0 + lk], Us[(s0 + lk) * UP + li], ap);
+#pragma unroll
+      for (int m = 0; m < KQ; ++m) aq = mfma4(aqr[m], sb[m], aq);
+#pragma unroll
+      for (int m = 0; m < SQ; ++m) ap = mfma4(apr[m], ubr[m], ap);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * wv + 4 * lk + r;
         if (t < nt) {
           const int j = jb + t;
-          int gr = p.tix ? p.tix[j] : j;
+          const int gr = p.tix ? p.tix[j] : j;
           if (gr >= 0 && gr < p.num_actual_tokens)
             p.out[((size_t)gr * Hv + h) * DV + 16 * blk + li] =
                 f2bf(fmaf(expf(Gc[t]), aq[r], ap[r]));
@@ -330,18 +382,18 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
     }
 
     // (c) S = e^{G_C} S0 + U^T diag(e^{G_C - G_t}) K for this wave's tiles
+    //     (interleaved split s = 4m + lane/16: row-major key reads)
     {
-      const float gC = Gc[kC - 1];
+      float ua[SQ];
+#pragma unroll
+      for (int m = 0; m < SQ; ++m) ua[m] = UTs[li * CP + 4 * m + lk];
       const float eC = expf(gC);
 #pragma unroll
       for (int q = 0; q < TPW; ++q) {
-        const int m = wv * TPW + q;
+        const int mt = wv * TPW + q;
         v4f acc = St[q] * eC;
-#pragma unroll 4
-        for (int s0 = 0; s0 < kC; s0 += 4) {
-          const int s = s0 + lk;
-          acc = mfma4(Us[s * UP + li], expf(gC - Gc[s]) * Kl[s * KP + 16 * m + li], acc);
-        }
+#pragma unroll
+        for (int m = 0; m < SQ; ++m) acc = mfma4(ua[m], Kl[(4 * m + lk) * KP + 16 * mt + li], acc);
         St[q] = acc;
       }
     }
