@@ -343,7 +343,6 @@ int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
     p.out = core_attn_out;
     p.num_rows = num_prefills;
     p.stream_tokens = num_non_spec_tokens;
-    p.max_row_len = num_non_spec_tokens - num_decodes;
     p.qsl = query_start_loc + num_decodes;
     p.cache_idx = non_spec_state_indices + num_decodes;
     p.his = has_initial_state ? has_initial_state + num_decodes : nullptr;

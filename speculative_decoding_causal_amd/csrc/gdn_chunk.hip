@@ -6,7 +6,7 @@
 // chunk (G_t = sum_{s<=t} log a_s) and only decay differences t >= s ever
 // exponentiated:
 //   A  = strictly-lower( b_t e^{G_t - G_s} k_t.k_s )          (C x C)
-//   T  = (I + A)^{-1}                                         (forward substitution)
+//   T  = (I + A)^{-1}                                         (unit lower)
 //   W  = T diag(b e^{G}) K,   U~ = T diag(b) V                 (C x dk, C x dv)
 //   P  = lower-incl( e^{G_t - G_s} q_t.k_s )                  (C x C)
 // and then, chunk after chunk, from the chunk's initial state S0:
@@ -22,6 +22,11 @@
 // outputs through token_indx.  Dense products use v_mfma_f32_16x16x4f32
 // (A[i][k] at lane i+16k, B[k][j] at lane j+16k, D[i][j] at lane j+16*(i/4),
 // element i%4).
+//
+// Sums over the 64 tokens of a chunk take 16 MFMA steps m = 4M + e, lane group
+// kk = lane/16 adding token s = 16M + 4kk + e: token block M (16 tokens) is one
+// group of four steps, so blocks a triangular factor zeroes are skipped, and a
+// lane's A operand for a block is one float4.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -36,6 +41,43 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
 }
 
 __device__ __forceinline__ int slot_ok(int s, int n) { return (s > 0 && s < n) ? s : 0; }
+
+// LDS tiles hold P floats per row (P a multiple of 64, no padding); the
+// float4 groups of row r are XOR-permuted by r mod 16.  Float4 reads of 16
+// consecutive rows, scalar writes of an MFMA result (rows 4kk+i, 16
+// consecutive columns) and scalar reads of rows 4kk+e over 16 consecutive
+// columns then all hit distinct banks.
+template <int P>
+__device__ __forceinline__ int sw(int r, int c) {
+  return r * P + (c ^ ((r & 15) << 2));
+}
+
+template <int P>
+__device__ __forceinline__ v4f ld4(const float* t, int r, int c) {
+  return *reinterpret_cast<const v4f*>(t + sw<P>(r, c));
+}
+
+// N consecutive floats of row r from column c0 (a multiple of 4).
+template <int P, int N>
+__device__ __forceinline__ void lds_run(float (&dst)[N], const float* t, int r, int c0) {
+  static_assert(N % 4 == 0, "runs of float4");
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    const v4f v = ld4<P>(t, r, c0 + 4 * i);
+    dst[4 * i] = v.x;
+    dst[4 * i + 1] = v.y;
+    dst[4 * i + 2] = v.z;
+    dst[4 * i + 3] = v.w;
+  }
+}
+
+// Workgroups go to the XCDs round-robin by linear index.  With Hv a multiple
+// of 8 and the head index fastest in the grid, index x lands on XCD x mod 8;
+// head (x mod 8) * Hv/8 + x / 8 then gives each XCD a contiguous run of
+// heads, so v-heads that share a k-head share that XCD's L2.
+__device__ __forceinline__ int head_of(int x, int Hv) {
+  return (Hv & 7) ? x : (x & 7) * (Hv >> 3) + (x >> 3);
+}
 
 struct PRow {
   int j0, T, slot;
@@ -53,7 +95,8 @@ __device__ __forceinline__ PRow prow(const PrefillArgs& p, int row) {
 }
 
 // Rows of ROWS x COLS floats gathered in one batch of float4 loads (rows
-// >= nrow read as zeros), then written to LDS with row pitch PITCH.
+// >= nrow, nrow >= 1, read as zeros: the load goes to row nrow-1 and the
+// value is dropped, so no load sits behind a branch), then written to LDS.
 template <int ROWS, int COLS>
 struct Tile4 {
   static constexpr int kPer = ROWS * COLS / 4 / 256;  // float4 per thread
@@ -64,51 +107,39 @@ struct Tile4 {
     for (int i = 0; i < kPer; ++i) {
       const int e = (i * 256 + (int)threadIdx.x) * 4;
       const int r = e / COLS, c = e - r * COLS;
-      v[i] = r < nrow ? *reinterpret_cast<const v4f*>(row_ptr(r) + c) : v4f{0.f, 0.f, 0.f, 0.f};
+      const v4f x = *reinterpret_cast<const v4f*>(row_ptr(r < nrow ? r : nrow - 1) + c);
+      v[i] = r < nrow ? x : v4f{0.f, 0.f, 0.f, 0.f};
     }
   }
-  template <int PITCH>
-  __device__ __forceinline__ void store(float* lds) const {
+  // swizzled tile of row length COLS
+  __device__ __forceinline__ void store_sw(float* lds) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int e = (i * 256 + (int)threadIdx.x) * 4;
       const int r = e / COLS, c = e - r * COLS;
-      *reinterpret_cast<v4f*>(lds + r * PITCH + c) = v[i];
+      *reinterpret_cast<v4f*>(lds + sw<COLS>(r, c)) = v[i];
     }
+  }
+  // plain row-major tile
+  __device__ __forceinline__ void store_plain(float* lds) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      *reinterpret_cast<v4f*>(lds + (i * 256 + (int)threadIdx.x) * 4) = v[i];
   }
 };
 
-// N consecutive floats of LDS (16-byte aligned) into registers.
-template <int N>
-__device__ __forceinline__ void lds_run(float (&dst)[N], const float* src) {
-  static_assert(N % 4 == 0, "runs of float4");
-#pragma unroll
-  for (int i = 0; i < N / 4; ++i) {
-    const v4f v = *reinterpret_cast<const v4f*>(src + 4 * i);
-    dst[4 * i] = v.x;
-    dst[4 * i + 1] = v.y;
-    dst[4 * i + 2] = v.z;
-    dst[4 * i + 3] = v.w;
-  }
-}
-
-// Operand feeding: the sum over k is split so that lane group kk = lane/16
-// owns the contiguous range k = kk*(K/4) + m of every MFMA step m; both
-// operands use the same split, so each lane reads its operands for all K/4
-// steps as one contiguous run.
-
-// Shared-memory carve-up of chunk_prep_kernel (floats).  Row pitches are
-// padded by four: rows stay 16-byte aligned and column reads spread over
-// the banks.
+// Shared-memory carve-up of chunk_prep_kernel (floats).
 template <int DK>
 struct PrepLds {
-  static constexpr int KP = DK + 4, CP = kC + 4;
-  static constexpr int ks = 0;                          // [kC][KP]  keys
-  static constexpr int qv = ks + kC * KP;               // [kC][KP]  queries, then values
-  static constexpr int ts = qv + kC * KP;               // [kC][CP]  A, then T
-  static constexpr int gs = ts + kC * CP;               // [kC] cumulative log-decay
-  static constexpr int bs = gs + kC;                    // [kC] beta
-  static constexpr int bg = bs + kC;                    // [kC] beta e^G
+  static constexpr int MP = 20;                 // pitch of the 16x16 scratch
+  static constexpr int ks = 0;                  // [kC][DK] keys
+  static constexpr int qv = ks + kC * DK;       // [kC][DK] queries, then values
+  static constexpr int as = qv + kC * DK;       // [kC][kC] A
+  static constexpr int tt = as + kC * kC;       // [kC][kC] T
+  static constexpr int mw = tt + kC * kC;       // [4][16][MP] per-wave scratch
+  static constexpr int gs = mw + 4 * 16 * MP;   // [kC] cumulative log-decay
+  static constexpr int bs = gs + kC;            // [kC] beta
+  static constexpr int bg = bs + kC;            // [kC] beta e^G
   static constexpr int total = bg + kC;
 };
 
@@ -116,21 +147,23 @@ template <int DK, int DV>
 __global__ void __launch_bounds__(256)
 chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __restrict__ glog,
                   const float* __restrict__ gbeta, ChunkWs ws) {
-  static_assert(DK == DV, "dk == dv");
+  static_assert(DK == DV && DK % 64 == 0, "dk == dv, multiple of 64");
   extern __shared__ __align__(16) float sm[];
   using Lay = PrepLds<DK>;
-  constexpr int KP = Lay::KP, CP = Lay::CP;
+  constexpr int MP = Lay::MP;
   constexpr int KQ = DK / 4;   // k-run per lane group, Gram products
-  constexpr int SQ = kC / 4;   // k-run per lane group, products over tokens
   float* Ks = sm + Lay::ks;
   float* QV = sm + Lay::qv;
-  float* Ts = sm + Lay::ts;
+  float* As = sm + Lay::as;
+  float* Tt = sm + Lay::tt;
   float* Gs = sm + Lay::gs;
   float* Bs = sm + Lay::bs;
   float* BG = sm + Lay::bg;
 
-  const int c = blockIdx.x, h = blockIdx.y;
-  const PRow pr = prow(p, blockIdx.z);
+  const int row = p.unit_map[2 * blockIdx.y];
+  if (row < 0) return;
+  const int c = p.unit_map[2 * blockIdx.y + 1], h = head_of(blockIdx.x, p.Hv);
+  const PRow pr = prow(p, row);
   const int t0 = c * kC;
   if (t0 >= pr.T) return;
   const int nt = min(kC, pr.T - t0);
@@ -138,6 +171,7 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   const int ih = h / p.G, Hk = p.Hk, Hv = p.Hv, C = p.C;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int li = lane & 15, lk = lane >> 4;
+  float* Mw = sm + Lay::mw + wv * 16 * MP;
 
   // 1. keys, queries and values of the chunk gathered in one batch
   Tile4<kC, DV> tv;
@@ -147,14 +181,24 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
     tk.load([&](int r) { return yb + (size_t)r * C + Hk * DK + ih * DK; }, nt);
     tq.load([&](int r) { return yb + (size_t)r * C + ih * DK; }, nt);
     tv.load([&](int r) { return yb + (size_t)r * C + 2 * Hk * DK + h * DV; }, nt);
-    tk.template store<KP>(Ks);
-    tq.template store<KP>(QV);
+    tk.store_sw(Ks);
+    tq.store_sw(QV);
   }
   if (tid < kC) {
     Gs[tid] = tid < nt ? glog[(size_t)(jb + tid) * Hv + h] : 0.f;
     Bs[tid] = tid < nt ? gbeta[(size_t)(jb + tid) * Hv + h] : 0.f;
   }
-  __syncthreads();
+  // P is zero right of its diagonal blocks
+  {
+    float* Pg = ws.P + ((size_t)jb * Hv + h) * kC;
+#pragma unroll
+    for (int i = 0; i < kC * kC / 4 / 256; ++i) {
+      const int e = i * 256 + tid, t = e >> 4, g = e & 15;
+      if ((g >> 2) > (t >> 4) && t < nt)
+        *reinterpret_cast<v4f*>(Pg + (size_t)t * Hv * kC + 4 * g) = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  lds_barrier();
   // 2. cumulative log-decay (inclusive scan over the 64 tokens)
   if (wv == 0) {
     float g = Gs[lane];
@@ -166,84 +210,147 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
     Gs[lane] = g;
     BG[lane] = Bs[lane] * expf(g);
   }
-  __syncthreads();
-  // 3. K K^T and Q K^T: wave w owns token-row tile w
+  lds_barrier();
+  // 3. K K^T and Q K^T on the ten 16x16 tiles (ti >= tj) that A and P use:
+  //    twenty tile products, five per wave (waves 0 and 2 K K^T, 1 and 3
+  //    Q K^T; waves 0 and 1 the even tiles in row order, 2 and 3 the odd).
   {
-    float ak[KQ], aq[KQ];
-    lds_run<KQ>(ak, Ks + (16 * wv + li) * KP + lk * KQ);
-    lds_run<KQ>(aq, QV + (16 * wv + li) * KP + lk * KQ);
-    for (int tj = 0; tj < 4; ++tj) {
-      float bk[KQ];
-      lds_run<KQ>(bk, Ks + (16 * tj + li) * KP + lk * KQ);
-      v4f akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+    const bool qk = (wv & 1) != 0;
+    const float* Asrc = qk ? QV : Ks;
 #pragma unroll
-      for (int m = 0; m < KQ; ++m) {
-        akk = mfma4(ak[m], bk[m], akk);
-        aqk = mfma4(aq[m], bk[m], aqk);
-      }
+    for (int it = 0; it < 5; ++it) {
+      const int x = 2 * it + (wv >> 1);
+      const int ti = x < 1 ? 0 : (x < 3 ? 1 : (x < 6 ? 2 : 3));
+      const int tj = x - ti * (ti + 1) / 2;
+      float ar[KQ], br[KQ];
+      lds_run<DK>(ar, Asrc, 16 * ti + li, lk * KQ);
+      lds_run<DK>(br, Ks, 16 * tj + li, lk * KQ);
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < KQ; ++m) acc = mfma4(ar[m], br[m], acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * wv + 4 * lk + r, s = 16 * tj + li;
+        const int t = 16 * ti + 4 * lk + r, s = 16 * tj + li;
         const float dec = expf(Gs[t] - Gs[s < t ? s : t]);
-        Ts[t * CP + s] = s < t ? Bs[t] * dec * akk[r] : 0.f;
-        if (t < nt)
-          ws.P[((size_t)(jb + t) * Hv + h) * kC + s] = s <= t ? dec * aqk[r] : 0.f;
+        if (!qk)
+          As[sw<kC>(t, s)] = s < t ? Bs[t] * dec * acc[r] : 0.f;
+        else if (t < nt)
+          ws.P[((size_t)(jb + t) * Hv + h) * kC + s] = s <= t ? dec * acc[r] : 0.f;
       }
     }
   }
-  __syncthreads();
-  // 4. T = (I + A)^{-1}: lane j of wave 0 solves column j by forward
-  //    substitution (four partial sums per row); the values replace the
-  //    queries.
-  if (wv == 0) {
-    float X[kC];
-#pragma unroll
-    for (int t = 0; t < kC; ++t) {
-      float x0 = (t == lane) ? 1.f : 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
-#pragma unroll
-      for (int s = 0; s < t; ++s) {
-        const float a = Ts[t * CP + s];
-        if ((s & 3) == 0) x0 = fmaf(-a, X[s], x0);
-        else if ((s & 3) == 1) x1 = fmaf(-a, X[s], x1);
-        else if ((s & 3) == 2) x2 = fmaf(-a, X[s], x2);
-        else x3 = fmaf(-a, X[s], x3);
-      }
-      X[t] = (x0 + x1) + (x2 + x3);
-    }
-#pragma unroll
-    for (int t = 0; t < kC; ++t) Ts[t * CP + lane] = X[t];
-  }
-  tv.template store<KP>(QV);
-  __syncthreads();
-  // 5. W = T diag(b e^G) K and U~ = T diag(b) V: wave w owns token tile w.
-  //    The sum over tokens s takes the interleaved split s = 4m + lane/16, so
-  //    the key/value operand is a row-major read spread over the banks.
+  lds_barrier();
+  // 4. T = (I + A)^{-1} in 16x16 blocks.  Wave w inverts diagonal block w by
+  //    forward substitution (lane j of each 16 solves column j) and clears
+  //    T's blocks right of it; the values replace the queries meanwhile.
   {
-    float at[SQ], bgr[SQ], br[SQ];
+    const int b0 = 16 * wv;
+    float X[16];
 #pragma unroll
-    for (int m = 0; m < SQ; ++m) {
-      at[m] = Ts[(16 * wv + li) * CP + 4 * m + lk];
-      bgr[m] = BG[4 * m + lk];
-      br[m] = Bs[4 * m + lk];
-    }
-    for (int n = 0; n < DK / 16; ++n) {
-      v4f aw = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 16; ++t) {
+      float x0 = (t == li) ? 1.f : 0.f, x1 = 0.f;
 #pragma unroll
-      for (int m = 0; m < SQ; ++m) {
-        const int srow = (4 * m + lk) * KP + 16 * n + li;
-        aw = mfma4(at[m], bgr[m] * Ks[srow], aw);
-        au = mfma4(at[m], br[m] * QV[srow], au);
-      }
+      for (int g = 0; g < (t + 3) / 4; ++g) {
+        const v4f a = ld4<kC>(As, b0 + t, b0 + 4 * g);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * wv + 4 * lk + r;
-        if (t < nt) {
-          const size_t o = ((size_t)(jb + t) * Hv + h) * DK + 16 * n + li;
-          ws.W[o] = aw[r];
-          ws.U[o] = au[r];
+        for (int e = 0; e < 4; ++e) {
+          const int s = 4 * g + e;
+          if (s < t) {
+            if (e & 1) x1 = fmaf(-a[e], X[s], x1);
+            else x0 = fmaf(-a[e], X[s], x0);
+          }
         }
       }
+      X[t] = x0 + x1;
     }
+    if (lk == 0) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) Tt[sw<kC>(b0 + t, b0 + li)] = X[t];
+    }
+    for (int cb = wv + 1; cb < 4; ++cb)
+      *reinterpret_cast<v4f*>(Tt + sw<kC>(b0 + li, 16 * cb + 4 * lk)) = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  tv.store_sw(QV);
+  lds_barrier();
+  //    Blocks below the diagonal, one diagonal level at a time:
+  //    T_ij = -T_ii M with M = sum_{k=j}^{i-1} A_ik T_kj (wave w: j = w).
+  for (int lv = 1; lv < 4; ++lv) {
+    const bool act = wv < 4 - lv;
+    const int i = wv + lv, j = wv;
+    if (act) {
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k = j; k < i; ++k) {
+        const v4f a = ld4<kC>(As, 16 * i + li, 16 * k + 4 * lk);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc = mfma4(a[e], Tt[sw<kC>(16 * k + 4 * lk + e, 16 * j + li)], acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Mw[(4 * lk + r) * MP + li] = acc[r];
+    }
+    lds_barrier();
+    if (act) {
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+      const v4f d = ld4<kC>(Tt, 16 * i + li, 16 * i + 4 * lk);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = mfma4(d[e], Mw[(4 * lk + e) * MP + li], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Tt[sw<kC>(16 * i + 4 * lk + r, 16 * j + li)] = -acc[r];
+    }
+    lds_barrier();
+  }
+  // 5. W = T diag(b e^G) K and U~ = T diag(b) V.  Wave w computes column
+  //    tiles NW*w .. NW*w+NW-1 for every token tile; token block M feeds
+  //    token tiles ti >= M only (T is block lower triangular).
+  {
+    constexpr int NW = DK / 64;
+    v4f aw[4][NW], au[4][NW];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        aw[ti][q] = v4f{0.f, 0.f, 0.f, 0.f};
+        au[ti][q] = v4f{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int M = 0; M < 4; ++M) {
+      const v4f g4 = *reinterpret_cast<const v4f*>(BG + 16 * M + 4 * lk);
+      const v4f b4 = *reinterpret_cast<const v4f*>(Bs + 16 * M + 4 * lk);
+      float kb[4][NW], vb[4][NW];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int q = 0; q < NW; ++q) {
+          const int sidx = sw<DK>(16 * M + 4 * lk + e, 16 * (NW * wv + q) + li);
+          kb[e][q] = g4[e] * Ks[sidx];
+          vb[e][q] = b4[e] * QV[sidx];
+        }
+#pragma unroll
+      for (int ti = M; ti < 4; ++ti) {
+        const v4f a = ld4<kC>(Tt, 16 * ti + li, 16 * M + 4 * lk);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int q = 0; q < NW; ++q) {
+            aw[ti][q] = mfma4(a[e], kb[e][q], aw[ti][q]);
+            au[ti][q] = mfma4(a[e], vb[e][q], au[ti][q]);
+          }
+      }
+    }
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * ti + 4 * lk + r;
+        if (t < nt) {
+#pragma unroll
+          for (int q = 0; q < NW; ++q) {
+            const size_t o = ((size_t)(jb + t) * Hv + h) * DK + 16 * (NW * wv + q) + li;
+            ws.W[o] = aw[ti][q][r];
+            ws.U[o] = au[ti][q][r];
+          }
+        }
+      }
   }
   if (tid < nt) ws.G[(size_t)(jb + tid) * Hv + h] = Gs[tid];
 }
@@ -251,16 +358,15 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
 // Shared memory of chunk_state_kernel (floats).
 template <int DK>
 struct StateLds {
-  static constexpr int KP = DK + 4, CP = kC + 4;
-  static constexpr int wl = 0;                    // [kC][KP] W of the chunk
-  static constexpr int ql = wl + kC * KP;         // [kC][KP] queries
-  static constexpr int kl = ql + kC * KP;         // [kC][KP] keys
-  static constexpr int pl = kl + kC * KP;         // [kC][CP] P
-  static constexpr int ul = pl + kC * CP;         // [kC][16] U~ block
-  static constexpr int ss = ul + kC * 16;         // [16][KP] state block
-  static constexpr int ut = ss + 16 * KP;         // [16][CP] U^T block
-  static constexpr int uts = ut + 16 * CP;        // [16][CP] U^T diag(e^{G_C - G})
-  static constexpr int gc = uts + 16 * CP;        // [kC] G
+  static constexpr int wl = 0;                    // [kC][DK] W of the chunk
+  static constexpr int ql = wl + kC * DK;         // [kC][DK] queries
+  static constexpr int kl = ql + kC * DK;         // [kC][DK] keys
+  static constexpr int pl = kl + kC * DK;         // [kC][kC] P
+  static constexpr int ul = pl + kC * kC;         // [kC][16] U~ block (plain)
+  static constexpr int ss = ul + kC * 16;         // [16][DK] state block
+  static constexpr int ut = ss + 16 * DK;         // [16][kC] U^T block
+  static constexpr int uts = ut + 16 * kC;        // [16][kC] U^T diag(e^{G_C - G})
+  static constexpr int gc = uts + 16 * kC;        // [kC] G
   static constexpr int total = gc + kC;
 };
 
@@ -270,8 +376,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   static_assert(DK == DV && DK % 64 == 0, "dk == dv, multiple of 64");
   extern __shared__ __align__(16) float sm[];
   using Lay = StateLds<DK>;
-  constexpr int KP = Lay::KP, CP = Lay::CP;
-  constexpr int KQ = DK / 4, SQ = kC / 4;
+  constexpr int KQ = DK / 4;
   constexpr int TPW = (DK / 16) / 4;  // state tiles per wave
   float* Wl = sm + Lay::wl;
   float* Ql = sm + Lay::ql;
@@ -284,7 +389,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   float* Gc = sm + Lay::gc;
 
   const int Hv = p.Hv, Hk = p.Hk, C = p.C;
-  const int row = blockIdx.x / Hv, h = blockIdx.x - row * Hv;
+  const int row = blockIdx.x / Hv, h = head_of(blockIdx.x - row * Hv, Hv);
   const int blk = blockIdx.y;  // state rows 16*blk .. 16*blk+15
   const PRow pr = prow(p, row);
   if (pr.T <= 0) return;
@@ -307,6 +412,8 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   Tile4<kC, DK> tw, tq, tk;
   Tile4<kC, kC> tp;
   Tile4<kC, 16> tu;
+  float tg;     // G of token lane % 64
+  int tx[4];    // global rows of this lane's output tokens (-1: none)
   auto gather = [&](int c) {
     const int jb = pr.j0 + c * kC;
     const int nt = min(kC, pr.T - c * kC);
@@ -316,32 +423,42 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
     tk.load([&](int r) { return yb + (size_t)r * C + Hk * DK + ih * DK; }, nt);
     tp.load([&](int r) { return ws.P + ((size_t)(jb + r) * Hv + h) * kC; }, nt);
     tu.load([&](int r) { return ws.U + ((size_t)(jb + r) * Hv + h) * DV + 16 * blk; }, nt);
+    tg = ws.G[(size_t)(jb + min(lane, nt - 1)) * Hv + h];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * wv + 4 * lk + r;
+      const int j = jb + min(t, nt - 1);
+      const int gr = p.tix ? p.tix[j] : j;
+      tx[r] = (t < nt && gr >= 0 && gr < p.num_actual_tokens) ? gr : -1;
+    }
   };
   gather(0);
   for (int c = 0; c < nch; ++c) {
-    const int jb = pr.j0 + c * kC;
     const int nt = min(kC, pr.T - c * kC);
-    tw.template store<KP>(Wl);
-    tq.template store<KP>(Ql);
-    tk.template store<KP>(Kl);
-    tp.template store<CP>(Pl);
-    tu.template store<16>(Ul);
-    if (tid < kC) Gc[tid] = ws.G[(size_t)(jb + (tid < nt ? tid : nt - 1)) * Hv + h];
+    tw.store_sw(Wl);
+    tq.store_sw(Ql);
+    tk.store_sw(Kl);
+    tp.store_sw(Pl);
+    tu.store_plain(Ul);
+    if (tid < kC) Gc[tid] = tg;
+    int orow[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) orow[r] = tx[r];
 #pragma unroll
     for (int q = 0; q < TPW; ++q)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Ss[(4 * lk + r) * KP + 16 * (wv * TPW + q) + li] = St[q][r];
-    __syncthreads();
+      for (int r = 0; r < 4; ++r) Ss[sw<DK>(4 * lk + r, 16 * (wv * TPW + q) + li)] = St[q][r];
+    lds_barrier();
     if (c + 1 < nch) gather(c + 1);
 
     const float gC = Gc[kC - 1];
     // B operand of S0^T products: S[j][k] for this lane's k-run
     float sb[KQ];
-    lds_run<KQ>(sb, Ss + li * KP + lk * KQ);
+    lds_run<DK>(sb, Ss, li, lk * KQ);
     // (a) U = U~ - W S0^T for token tile wv; U^T kept plain and decay-scaled
     {
       float aw[KQ];
-      lds_run<KQ>(aw, Wl + (16 * wv + li) * KP + lk * KQ);
+      lds_run<DK>(aw, Wl, 16 * wv + li, lk * KQ);
       v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < KQ; ++m) acc = mfma4(aw[m], sb[m], acc);
@@ -352,52 +469,60 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
         u[r] = t < nt ? Ul[t * 16 + li] - acc[r] : 0.f;
         us[r] = u[r] * expf(gC - Gc[t]);
       }
-      *reinterpret_cast<v4f*>(UT + li * CP + 16 * wv + 4 * lk) = u;
-      *reinterpret_cast<v4f*>(UTs + li * CP + 16 * wv + 4 * lk) = us;
+      *reinterpret_cast<v4f*>(UT + sw<kC>(li, 16 * wv + 4 * lk)) = u;
+      *reinterpret_cast<v4f*>(UTs + sw<kC>(li, 16 * wv + 4 * lk)) = us;
     }
-    __syncthreads();
+    lds_barrier();
 
-    // (b) outputs of token tile wv: e^{G_t} (Q S0^T)[t] + (P U)[t]
+    // (b) outputs of token tile wv: e^{G_t} (Q S0^T)[t] + (P U)[t]; P is
+    //     zero right of the diagonal block
     {
-      float aqr[KQ], apr[SQ], ubr[SQ];
-      lds_run<KQ>(aqr, Ql + (16 * wv + li) * KP + lk * KQ);
-      lds_run<SQ>(apr, Pl + (16 * wv + li) * CP + lk * SQ);
-      lds_run<SQ>(ubr, UT + li * CP + lk * SQ);
+      float aqr[KQ];
+      lds_run<DK>(aqr, Ql, 16 * wv + li, lk * KQ);
       v4f aq = {0.f, 0.f, 0.f, 0.f}, ap = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < KQ; ++m) aq = mfma4(aqr[m], sb[m], aq);
 #pragma unroll
-      for (int m = 0; m < SQ; ++m) ap = mfma4(apr[m], ubr[m], ap);
+      for (int M = 0; M < 4; ++M) {
+        if (M <= wv) {
+          const v4f a = ld4<kC>(Pl, 16 * wv + li, 16 * M + 4 * lk);
+          const v4f b = ld4<kC>(UT, li, 16 * M + 4 * lk);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ap = mfma4(a[e], b[e], ap);
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * wv + 4 * lk + r;
-        if (t < nt) {
-          const int j = jb + t;
-          const int gr = p.tix ? p.tix[j] : j;
-          if (gr >= 0 && gr < p.num_actual_tokens)
-            p.out[((size_t)gr * Hv + h) * DV + 16 * blk + li] =
-                f2bf(fmaf(expf(Gc[t]), aq[r], ap[r]));
-        }
+        if (orow[r] >= 0)
+          p.out[((size_t)orow[r] * Hv + h) * DV + 16 * blk + li] =
+              f2bf(fmaf(expf(Gc[t]), aq[r], ap[r]));
       }
     }
 
     // (c) S = e^{G_C} S0 + U^T diag(e^{G_C - G_t}) K for this wave's tiles
-    //     (interleaved split s = 4m + lane/16: row-major key reads)
     {
-      float ua[SQ];
+      float ua[16];
 #pragma unroll
-      for (int m = 0; m < SQ; ++m) ua[m] = UTs[li * CP + 4 * m + lk];
+      for (int M = 0; M < 4; ++M) {
+        const v4f a = ld4<kC>(UTs, li, 16 * M + 4 * lk);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ua[4 * M + e] = a[e];
+      }
       const float eC = expf(gC);
 #pragma unroll
       for (int q = 0; q < TPW; ++q) {
         const int mt = wv * TPW + q;
         v4f acc = St[q] * eC;
 #pragma unroll
-        for (int m = 0; m < SQ; ++m) acc = mfma4(ua[m], Kl[(4 * m + lk) * KP + 16 * mt + li], acc);
+        for (int M = 0; M < 4; ++M)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc = mfma4(ua[4 * M + e], Kl[sw<DK>(16 * M + 4 * lk + e, 16 * mt + li)], acc);
         St[q] = acc;
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
   if (pr.slot > 0) {
 #pragma unroll
@@ -437,13 +562,14 @@ static hipError_t launch_chunked_typed(const PrefillArgs& a, const float* y, con
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_state_kernel<DK, DV>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)l2);
   if (e != hipSuccess) return e;
-  const int nch = (a.max_row_len + kC - 1) / kC;
-  if (nch <= 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_prep_kernel<DK, DV>), dim3(nch, a.Hv, a.num_rows), dim3(256), l1, s,
+  if (a.units <= 0) return hipSuccess;
+  // one workgroup per (v-head, 64-token unit of a row), head index fastest
+  hipLaunchKernelGGL((chunk_prep_kernel<DK, DV>), dim3(a.Hv, a.units), dim3(256), l1, s,
                      a, y, glog, gbeta, ws);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // Head index fastest, so the 16-row blocks of one head share an XCD's L2.
+  // Head index fastest, so the 16-row blocks of one head share an XCD's L2
+  // (grid.x is a multiple of 8 whenever Hv is).
   hipLaunchKernelGGL((chunk_state_kernel<DK, DV>), dim3(a.Hv * a.num_rows, DV / 16), dim3(256), l2,
                      s, a, y, ws);
   return hipGetLastError();

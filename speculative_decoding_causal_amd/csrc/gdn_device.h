@@ -65,6 +65,16 @@ __device__ __forceinline__ float gate_log(float a, float A_log, float dt_bias) {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.f + expf(-x)); }
 
+// Workgroup barrier that orders LDS only: outstanding global loads (prefetches
+// into registers) stay in flight across it, unlike __syncthreads(), whose
+// workgroup-scope fence also waits for every global access.  Use it only where
+// no thread reads, across the barrier, global memory another thread wrote.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ int clampi(int v, int lo, int hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }

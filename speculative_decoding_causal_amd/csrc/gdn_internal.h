@@ -72,7 +72,8 @@ struct PrefillArgs {
   uint16_t* out;
   int num_rows;        // prefill rows
   int stream_tokens;   // tokens of the non-spec stream (workspace capacity)
-  int max_row_len;     // upper bound on tokens per prefill row
+  int units;           // capacity of unit_map: stream_tokens/64 rounded up + rows
+  const int* unit_map; // [units][2]: (row, 64-token unit of the row), row -1 past the end
   const int* qsl;      // [num_rows+1], non-spec stream indices
   const int* cache_idx;
   const uint8_t* his;

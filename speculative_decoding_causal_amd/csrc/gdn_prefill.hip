@@ -1,6 +1,9 @@
 // Non-spec prefill rows (rows of any length).
 //
-// Three launches on the caller's stream:
+// Launches on the caller's stream:
+//   0. prefill_map: one workgroup lists the 64-token units of the rows, row
+//      after row, so the kernels below launch one workgroup per unit that
+//      exists rather than per (row, longest possible row) pair.
 //   1. conv_prefill: one thread per (channel, 64-token segment of a row)
 //      slides the width-W window along the row and writes the fp32 conv
 //      output to the workspace at the token's non-spec stream index.  The
@@ -29,10 +32,16 @@ constexpr int kChunk = 32;  // tokens staged per LDS refill in the recurrence
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 struct WsLayout {
-  size_t y, kq, ga, gb, W, U, P, G, total;
+  size_t y, kq, ga, gb, W, U, P, G, map, total;
+  int units;
 };
 
-WsLayout ws_layout(int Hk, int Hv, int dk, int dv, int stream_tokens) {
+// Units of 64 tokens the rows can hold: each row adds at most one partial unit.
+int unit_capacity(int stream_tokens, int rows) {
+  return (stream_tokens + kSeg - 1) / kSeg + rows;
+}
+
+WsLayout ws_layout(int Hk, int Hv, int dk, int dv, int stream_tokens, int rows) {
   const size_t C = 2ull * Hk * dk + (size_t)Hv * dv;
   const size_t n = stream_tokens > 0 ? (size_t)stream_tokens : 0;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -46,6 +55,8 @@ WsLayout ws_layout(int Hk, int Hv, int dk, int dv, int stream_tokens) {
   w.U = o;  o += al(n * Hv * dv * 4);
   w.P = o;  o += al(n * Hv * 64 * 4);
   w.G = o;  o += al(n * Hv * 4);
+  w.units = unit_capacity(stream_tokens > 0 ? stream_tokens : 0, rows > 0 ? rows : 0);
+  w.map = o; o += al((size_t)w.units * 2 * 4);
   w.total = o;
   return w;
 }
@@ -74,13 +85,69 @@ __device__ __forceinline__ int global_row(const PrefillArgs& p, int j) {
   return (r >= 0 && r < p.num_actual_tokens) ? r : -1;
 }
 
+// The 64-token units of the rows in row order: map[2i] = row, map[2i+1] =
+// unit within the row; entries from the last unit up to cap hold row -1.
+// One workgroup: rows are taken 1024 at a time, their unit counts scanned,
+// then wave w writes the units of rows w, w+16, ... one lane per unit.
+constexpr int kMapThreads = 1024;
+__global__ void __launch_bounds__(kMapThreads)
+prefill_map_kernel(PrefillArgs p, int* __restrict__ map, int cap) {
+  __shared__ int start[kMapThreads + 1];
+  __shared__ int wsum[kMapThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int carry = 0;
+  for (int r0 = 0; r0 < p.num_rows; r0 += kMapThreads) {
+    const int r = r0 + tid;
+    int n = 0;
+    if (r < p.num_rows) n = (prefill_row(p, r).T + kSeg - 1) / kSeg;
+    int x = n;  // inclusive scan within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int up = __shfl_up(x, o, 64);
+      if (lane >= o) x += up;
+    }
+    if (lane == 63) wsum[wv] = x;
+    __syncthreads();
+    if (wv == 0) {
+      int w = lane < kMapThreads / 64 ? wsum[lane] : 0;
+#pragma unroll
+      for (int o = 1; o < kMapThreads / 64; o <<= 1) {
+        const int up = __shfl_up(w, o, 64);
+        if (lane >= o) w += up;
+      }
+      if (lane < kMapThreads / 64) wsum[lane] = w;
+    }
+    __syncthreads();
+    const int excl = carry + (wv > 0 ? wsum[wv - 1] : 0) + x - n;
+    start[tid] = excl;
+    if (tid == kMapThreads - 1) start[kMapThreads] = excl + n;
+    __syncthreads();
+    const int nr = min(kMapThreads, p.num_rows - r0);
+    for (int i = wv; i < nr; i += kMapThreads / 64) {
+      const int s0 = start[i], cnt = start[i + 1] - s0;
+      for (int u = lane; u < cnt && s0 + u < cap; u += 64) {
+        map[2 * (s0 + u)] = r0 + i;
+        map[2 * (s0 + u) + 1] = u;
+      }
+    }
+    carry = start[kMapThreads];
+    __syncthreads();
+  }
+  for (int i = carry + tid; i < cap; i += kMapThreads) {
+    map[2 * i] = -1;
+    map[2 * i + 1] = 0;
+  }
+}
+
 __global__ void __launch_bounds__(kThreads)
 conv_prefill_kernel(PrefillArgs p, float* __restrict__ y) {
   const int C = p.C, L = p.L, W = p.W;
   const int c = blockIdx.y * kThreads + threadIdx.x;
   if (c >= C) return;
-  const PrefillRow pr = prefill_row(p, blockIdx.z);
-  const int base = blockIdx.x * kSeg;
+  const int row = p.unit_map[2 * blockIdx.x], seg = p.unit_map[2 * blockIdx.x + 1];
+  if (row < 0) return;
+  const PrefillRow pr = prefill_row(p, row);
+  const int base = seg * kSeg;
   if (base >= pr.T) return;
   const int end = min(pr.T, base + kSeg);
   const uint16_t* ring = p.conv_pool + (size_t)pr.slot * L * C + c;
@@ -133,7 +200,7 @@ conv_prefill_kernel(PrefillArgs p, float* __restrict__ y) {
   }
   // Roll: new column l <- (history ++ inputs)[T + l].  Column T + l is read
   // before column l is written, and only this thread touches the channel.
-  if (blockIdx.x == 0 && pr.slot > 0) {
+  if (seg == 0 && pr.slot > 0) {
     uint16_t* wr = p.conv_pool + (size_t)pr.slot * L * C + c;
     for (int l = 0; l < L; ++l) {
       int src = pr.T + l;
@@ -289,18 +356,23 @@ delta_prefill_kernel(PrefillArgs p, const float* __restrict__ y,
 }
 
 template <int DK, int DV>
-hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t s) {
-  const WsLayout w = ws_layout(a.Hk, a.Hv, DK, DV, a.stream_tokens);
-  char* ws = static_cast<char*>(a.workspace);
+hipError_t launch_prefill_typed(const PrefillArgs& args, hipStream_t s) {
+  const WsLayout w = ws_layout(args.Hk, args.Hv, DK, DV, args.stream_tokens, args.num_rows);
+  char* ws = static_cast<char*>(args.workspace);
   float* y = reinterpret_cast<float*>(ws + w.y);
   float* kq = reinterpret_cast<float*>(ws + w.kq);
   float* ga = reinterpret_cast<float*>(ws + w.ga);
   float* gb = reinterpret_cast<float*>(ws + w.gb);
-  const int segs = (a.max_row_len + kSeg - 1) / kSeg;
-  if (segs <= 0) return hipSuccess;
-  dim3 g1(segs, (a.C + kThreads - 1) / kThreads, a.num_rows);
-  hipLaunchKernelGGL(conv_prefill_kernel, g1, dim3(kThreads), 0, s, a, y);
+  int* map = reinterpret_cast<int*>(ws + w.map);
+  PrefillArgs a = args;
+  a.units = w.units;
+  a.unit_map = map;
+  hipLaunchKernelGGL(prefill_map_kernel, dim3(1), dim3(kMapThreads), 0, s, a, map, w.units);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 g1(a.units, (a.C + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(conv_prefill_kernel, g1, dim3(kThreads), 0, s, a, y);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(prep_prefill_kernel<DK>, dim3(a.stream_tokens), dim3(kThreads), 0, s,
                      a, y, kq, ga, gb);
@@ -323,7 +395,7 @@ hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t s) {
 size_t prefill_workspace_bytes(int Hk, int Hv, int dk, int dv, int stream_tokens,
                                int rows) {
   if (rows <= 0) return 0;
-  return ws_layout(Hk, Hv, dk, dv, stream_tokens).total;
+  return ws_layout(Hk, Hv, dk, dv, stream_tokens, rows).total;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dk, int dv, hipStream_t s) {
