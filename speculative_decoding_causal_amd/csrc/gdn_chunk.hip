@@ -17,7 +17,7 @@
 //
 // chunk_prep_kernel: one workgroup per (row, chunk, v-head) computes W, U~, P
 // and G for its chunk (all chunks in parallel).
-// chunk_state_kernel: one workgroup per (row, v-head, 16 state rows) carries
+// chunk_state_kernel: one workgroup per (row, v-head, 32 state rows) carries
 // its rows of S through the row's chunks in MFMA accumulators and writes the
 // outputs through token_indx.  Dense products use v_mfma_f32_16x16x4f32
 // (A[i][k] at lane i+16k, B[k][j] at lane j+16k, D[i][j] at lane j+16*(i/4),
@@ -94,37 +94,47 @@ __device__ __forceinline__ PRow prow(const PrefillArgs& p, int row) {
   return r;
 }
 
-// Rows of ROWS x COLS floats gathered in one batch of float4 loads (rows
-// >= nrow, nrow >= 1, read as zeros: the load goes to row nrow-1 and the
-// value is dropped, so no load sits behind a branch), then written to LDS.
-template <int ROWS, int COLS>
+// Rows of ROWS x COLS floats gathered in one batch of float4 loads, then
+// written to LDS.  Thread x loads row x*4/COLS + i*NT*4/COLS of the tile:
+// one uniform base per i and one 32-bit lane offset.  Rows >= nrow are
+// loaded too and dropped (zeros kept): every array read this way holds a
+// chunk of padding rows past its last token, so the loads stay inside it,
+// and no load sits behind a branch.
+template <int ROWS, int COLS, int NT = 256>
 struct Tile4 {
-  static constexpr int kPer = ROWS * COLS / 4 / 256;  // float4 per thread
+  static_assert((ROWS * COLS / 4) % NT == 0 && (NT * 4) % COLS == 0, "tile shape");
+  static constexpr int kPer = ROWS * COLS / 4 / NT;  // float4 per thread
+  static constexpr int kRowStep = NT * 4 / COLS;     // rows between them
   v4f v[kPer];
-  template <class RowPtr>
-  __device__ __forceinline__ void load(RowPtr row_ptr, int nrow) {
+  // base: row 0, column 0 of the tile (uniform); pitch: floats per row
+  __device__ __forceinline__ void load(const float* base, int pitch, int nrow) {
+    const int r0 = (int)threadIdx.x * 4 / COLS, c0 = (int)threadIdx.x * 4 % COLS;
+    const unsigned off = (unsigned)(r0 * pitch + c0);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int e = (i * 256 + (int)threadIdx.x) * 4;
-      const int r = e / COLS, c = e - r * COLS;
-      const v4f x = *reinterpret_cast<const v4f*>(row_ptr(r < nrow ? r : nrow - 1) + c);
-      v[i] = r < nrow ? x : v4f{0.f, 0.f, 0.f, 0.f};
+      const float* bi = base + (size_t)(i * kRowStep) * pitch;
+      const v4f x = *reinterpret_cast<const v4f*>(bi + off);
+      v[i] = r0 + i * kRowStep < nrow ? x : v4f{0.f, 0.f, 0.f, 0.f};
     }
   }
   // swizzled tile of row length COLS
   __device__ __forceinline__ void store_sw(float* lds) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int e = (i * 256 + (int)threadIdx.x) * 4;
+      const int e = (i * NT + (int)threadIdx.x) * 4;
       const int r = e / COLS, c = e - r * COLS;
       *reinterpret_cast<v4f*>(lds + sw<COLS>(r, c)) = v[i];
     }
   }
-  // plain row-major tile
-  __device__ __forceinline__ void store_plain(float* lds) const {
+  // row-major tile with row pitch PITCH (a multiple of 4)
+  template <int PITCH>
+  __device__ __forceinline__ void store_pitched(float* lds) const {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      *reinterpret_cast<v4f*>(lds + (i * 256 + (int)threadIdx.x) * 4) = v[i];
+    for (int i = 0; i < kPer; ++i) {
+      const int e = (i * NT + (int)threadIdx.x) * 4;
+      const int r = e / COLS, c = e - r * COLS;
+      *reinterpret_cast<v4f*>(lds + r * PITCH + c) = v[i];
+    }
   }
 };
 
@@ -178,9 +188,9 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   {
     Tile4<kC, DK> tk, tq;
     const float* yb = y + (size_t)jb * C;
-    tk.load([&](int r) { return yb + (size_t)r * C + Hk * DK + ih * DK; }, nt);
-    tq.load([&](int r) { return yb + (size_t)r * C + ih * DK; }, nt);
-    tv.load([&](int r) { return yb + (size_t)r * C + 2 * Hk * DK + h * DV; }, nt);
+    tk.load(yb + Hk * DK + ih * DK, C, nt);
+    tq.load(yb + ih * DK, C, nt);
+    tv.load(yb + 2 * Hk * DK + h * DV, C, nt);
     tk.store_sw(Ks);
     tq.store_sw(QV);
   }
@@ -355,29 +365,37 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   if (tid < nt) ws.G[(size_t)(jb + tid) * Hv + h] = Gs[tid];
 }
 
-// Shared memory of chunk_state_kernel (floats).
-template <int DK>
+// Shared memory of chunk_state_kernel (floats); RB state rows per workgroup.
+template <int DK, int RB>
 struct StateLds {
+  static constexpr int UP = RB + 4;               // pitch of the U~ block
   static constexpr int wl = 0;                    // [kC][DK] W of the chunk
   static constexpr int ql = wl + kC * DK;         // [kC][DK] queries
   static constexpr int kl = ql + kC * DK;         // [kC][DK] keys
   static constexpr int pl = kl + kC * DK;         // [kC][kC] P
-  static constexpr int ul = pl + kC * kC;         // [kC][16] U~ block (plain)
-  static constexpr int ss = ul + kC * 16;         // [16][DK] state block
-  static constexpr int ut = ss + 16 * DK;         // [16][kC] U^T block
-  static constexpr int uts = ut + 16 * kC;        // [16][kC] U^T diag(e^{G_C - G})
-  static constexpr int gc = uts + 16 * kC;        // [kC] G
-  static constexpr int total = gc + kC;
+  static constexpr int ul = pl + kC * kC;         // [kC][UP] U~ block (plain)
+  static constexpr int ss = ul + kC * UP;         // [RB][DK] state block
+  static constexpr int ut = ss + RB * DK;         // [RB][kC] U^T block
+  static constexpr int gc = ut + RB * kC;         // [kC] G
+  static constexpr int fs = gc + kC;              // [kC] e^{G_C - G_t}
+  static constexpr int total = fs + kC;
 };
 
+constexpr int kStateThreads = 512;  // 8 waves, two per SIMD
+constexpr int kStateRows = 32;      // state rows per workgroup
+
+// Wave w works on token tile tt = w % 4 and state-row tile jt = w / 4 for
+// U and the outputs, and on state tiles (jt, TPW*tt + q) for the update.
 template <int DK, int DV>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kStateThreads)
 chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   static_assert(DK == DV && DK % 64 == 0, "dk == dv, multiple of 64");
+  constexpr int NT = kStateThreads, RB = kStateRows;
   extern __shared__ __align__(16) float sm[];
-  using Lay = StateLds<DK>;
+  using Lay = StateLds<DK, RB>;
+  constexpr int UP = Lay::UP;
   constexpr int KQ = DK / 4;
-  constexpr int TPW = (DK / 16) / 4;  // state tiles per wave
+  constexpr int TPW = DK / 64;  // state column tiles per wave
   float* Wl = sm + Lay::wl;
   float* Ql = sm + Lay::ql;
   float* Kl = sm + Lay::kl;
@@ -385,48 +403,49 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   float* Ul = sm + Lay::ul;
   float* Ss = sm + Lay::ss;
   float* UT = sm + Lay::ut;
-  float* UTs = sm + Lay::uts;
   float* Gc = sm + Lay::gc;
+  float* Fs = sm + Lay::fs;
 
   const int Hv = p.Hv, Hk = p.Hk, C = p.C;
   const int row = blockIdx.x / Hv, h = head_of(blockIdx.x - row * Hv, Hv);
-  const int blk = blockIdx.y;  // state rows 16*blk .. 16*blk+15
+  const int blk = blockIdx.y;  // state rows RB*blk .. RB*blk+RB-1
   const PRow pr = prow(p, row);
   if (pr.T <= 0) return;
   const int ih = h / p.G;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int li = lane & 15, lk = lane >> 4;
+  const int tt = wv & 3, jt = wv >> 2;
 
-  // state rows in C layout: tile m = wv*TPW + q holds S[4*lk + r][16m + li]
+  // state tiles in C layout: St[q] holds S[16 jt + 4 lk + r][16 (TPW tt + q) + li]
   v4f St[TPW];
-  const size_t tile_base = ((size_t)pr.slot * Hv + h) * DV * DK + (size_t)(16 * blk) * DK;
+  const size_t tile_base = ((size_t)pr.slot * Hv + h) * DV * DK + (size_t)(RB * blk + 16 * jt) * DK;
 #pragma unroll
   for (int q = 0; q < TPW; ++q)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      St[q][r] = pr.init ? p.ssm_pool[tile_base + (size_t)(4 * lk + r) * DK + 16 * (wv * TPW + q) + li]
+      St[q][r] = pr.init ? p.ssm_pool[tile_base + (size_t)(4 * lk + r) * DK + 16 * (TPW * tt + q) + li]
                          : 0.f;
 
   const int nch = (pr.T + kC - 1) / kC;
   // Operands of chunk c+1 are gathered while chunk c is computed.
-  Tile4<kC, DK> tw, tq, tk;
-  Tile4<kC, kC> tp;
-  Tile4<kC, 16> tu;
+  Tile4<kC, DK, NT> tw, tq, tk;
+  Tile4<kC, kC, NT> tp;
+  Tile4<kC, RB, NT> tu;
   float tg;     // G of token lane % 64
   int tx[4];    // global rows of this lane's output tokens (-1: none)
   auto gather = [&](int c) {
     const int jb = pr.j0 + c * kC;
     const int nt = min(kC, pr.T - c * kC);
     const float* yb = y + (size_t)jb * C;
-    tw.load([&](int r) { return ws.W + ((size_t)(jb + r) * Hv + h) * DK; }, nt);
-    tq.load([&](int r) { return yb + (size_t)r * C + ih * DK; }, nt);
-    tk.load([&](int r) { return yb + (size_t)r * C + Hk * DK + ih * DK; }, nt);
-    tp.load([&](int r) { return ws.P + ((size_t)(jb + r) * Hv + h) * kC; }, nt);
-    tu.load([&](int r) { return ws.U + ((size_t)(jb + r) * Hv + h) * DV + 16 * blk; }, nt);
+    tw.load(ws.W + ((size_t)jb * Hv + h) * DK, Hv * DK, nt);
+    tq.load(yb + ih * DK, C, nt);
+    tk.load(yb + Hk * DK + ih * DK, C, nt);
+    tp.load(ws.P + ((size_t)jb * Hv + h) * kC, Hv * kC, nt);
+    tu.load(ws.U + ((size_t)jb * Hv + h) * DV + RB * blk, Hv * DV, nt);
     tg = ws.G[(size_t)(jb + min(lane, nt - 1)) * Hv + h];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = 16 * wv + 4 * lk + r;
+      const int t = 16 * tt + 4 * lk + r;
       const int j = jb + min(t, nt - 1);
       const int gr = p.tix ? p.tix[j] : j;
       tx[r] = (t < nt && gr >= 0 && gr < p.num_actual_tokens) ? gr : -1;
@@ -439,7 +458,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
     tq.store_sw(Ql);
     tk.store_sw(Kl);
     tp.store_sw(Pl);
-    tu.store_plain(Ul);
+    tu.template store_pitched<UP>(Ul);
     if (tid < kC) Gc[tid] = tg;
     int orow[4];
 #pragma unroll
@@ -447,72 +466,75 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
 #pragma unroll
     for (int q = 0; q < TPW; ++q)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Ss[sw<DK>(4 * lk + r, 16 * (wv * TPW + q) + li)] = St[q][r];
+      for (int r = 0; r < 4; ++r)
+        Ss[sw<DK>(16 * jt + 4 * lk + r, 16 * (TPW * tt + q) + li)] = St[q][r];
     lds_barrier();
-    if (c + 1 < nch) gather(c + 1);
 
     const float gC = Gc[kC - 1];
-    // B operand of S0^T products: S[j][k] for this lane's k-run
+    if (tid < kC) Fs[tid] = expf(gC - Gc[tid]);
+    // B operand of S0^T products: S[j][k], j in row tile jt, this lane's k-run
     float sb[KQ];
-    lds_run<DK>(sb, Ss, li, lk * KQ);
-    // (a) U = U~ - W S0^T for token tile wv; U^T kept plain and decay-scaled
+    lds_run<DK>(sb, Ss, 16 * jt + li, lk * KQ);
+    // (a) U = U~ - W S0^T on (token tile tt, row tile jt), kept as U^T
     {
       float aw[KQ];
-      lds_run<DK>(aw, Wl, 16 * wv + li, lk * KQ);
+      lds_run<DK>(aw, Wl, 16 * tt + li, lk * KQ);
       v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < KQ; ++m) acc = mfma4(aw[m], sb[m], acc);
-      v4f u, us;
+      v4f u;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * wv + 4 * lk + r;
-        u[r] = t < nt ? Ul[t * 16 + li] - acc[r] : 0.f;
-        us[r] = u[r] * expf(gC - Gc[t]);
+        const int t = 16 * tt + 4 * lk + r;
+        u[r] = t < nt ? Ul[t * UP + 16 * jt + li] - acc[r] : 0.f;
       }
-      *reinterpret_cast<v4f*>(UT + sw<kC>(li, 16 * wv + 4 * lk)) = u;
-      *reinterpret_cast<v4f*>(UTs + sw<kC>(li, 16 * wv + 4 * lk)) = us;
+      *reinterpret_cast<v4f*>(UT + sw<kC>(16 * jt + li, 16 * tt + 4 * lk)) = u;
     }
     lds_barrier();
+    // the next chunk's operands load during (b) and (c); their registers are
+    // free while (a) holds its operand runs
+    if (c + 1 < nch) gather(c + 1);
 
-    // (b) outputs of token tile wv: e^{G_t} (Q S0^T)[t] + (P U)[t]; P is
-    //     zero right of the diagonal block
+    // (b) outputs on (tt, jt): e^{G_t} (Q S0^T)[t] + (P U)[t]; P is zero
+    //     right of the diagonal block
     {
       float aqr[KQ];
-      lds_run<DK>(aqr, Ql, 16 * wv + li, lk * KQ);
+      lds_run<DK>(aqr, Ql, 16 * tt + li, lk * KQ);
       v4f aq = {0.f, 0.f, 0.f, 0.f}, ap = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < KQ; ++m) aq = mfma4(aqr[m], sb[m], aq);
 #pragma unroll
       for (int M = 0; M < 4; ++M) {
-        if (M <= wv) {
-          const v4f a = ld4<kC>(Pl, 16 * wv + li, 16 * M + 4 * lk);
-          const v4f b = ld4<kC>(UT, li, 16 * M + 4 * lk);
+        if (M <= tt) {
+          const v4f a = ld4<kC>(Pl, 16 * tt + li, 16 * M + 4 * lk);
+          const v4f b = ld4<kC>(UT, 16 * jt + li, 16 * M + 4 * lk);
 #pragma unroll
           for (int e = 0; e < 4; ++e) ap = mfma4(a[e], b[e], ap);
         }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * wv + 4 * lk + r;
+        const int t = 16 * tt + 4 * lk + r;
         if (orow[r] >= 0)
-          p.out[((size_t)orow[r] * Hv + h) * DV + 16 * blk + li] =
+          p.out[((size_t)orow[r] * Hv + h) * DV + RB * blk + 16 * jt + li] =
               f2bf(fmaf(expf(Gc[t]), aq[r], ap[r]));
       }
     }
 
-    // (c) S = e^{G_C} S0 + U^T diag(e^{G_C - G_t}) K for this wave's tiles
+    // (c) S = e^{G_C} S0 + U^T diag(e^{G_C - G_t}) K on this wave's tiles
     {
       float ua[16];
 #pragma unroll
       for (int M = 0; M < 4; ++M) {
-        const v4f a = ld4<kC>(UTs, li, 16 * M + 4 * lk);
+        const v4f a = ld4<kC>(UT, 16 * jt + li, 16 * M + 4 * lk);
+        const v4f f = *reinterpret_cast<const v4f*>(Fs + 16 * M + 4 * lk);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ua[4 * M + e] = a[e];
+        for (int e = 0; e < 4; ++e) ua[4 * M + e] = a[e] * f[e];
       }
       const float eC = expf(gC);
 #pragma unroll
       for (int q = 0; q < TPW; ++q) {
-        const int mt = wv * TPW + q;
+        const int mt = TPW * tt + q;
         v4f acc = St[q] * eC;
 #pragma unroll
         for (int M = 0; M < 4; ++M)
@@ -529,7 +551,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
     for (int q = 0; q < TPW; ++q)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        p.ssm_pool[tile_base + (size_t)(4 * lk + r) * DK + 16 * (wv * TPW + q) + li] = St[q][r];
+        p.ssm_pool[tile_base + (size_t)(4 * lk + r) * DK + 16 * (TPW * tt + q) + li] = St[q][r];
   }
 }
 
@@ -545,8 +567,8 @@ size_t chunk_lds_prep(int dk) {
 
 size_t chunk_lds_state(int dk) {
   switch (dk) {
-    case 64: return sizeof(float) * StateLds<64>::total;
-    case 128: return sizeof(float) * StateLds<128>::total;
+    case 64: return sizeof(float) * StateLds<64, kStateRows>::total;
+    case 128: return sizeof(float) * StateLds<128, kStateRows>::total;
     default: return 0;
   }
 }
@@ -555,7 +577,7 @@ template <int DK, int DV>
 static hipError_t launch_chunked_typed(const PrefillArgs& a, const float* y, const float* glog,
                                        const float* gbeta, const ChunkWs& ws, hipStream_t s) {
   const size_t l1 = sizeof(float) * PrepLds<DK>::total;
-  const size_t l2 = sizeof(float) * StateLds<DK>::total;
+  const size_t l2 = sizeof(float) * StateLds<DK, kStateRows>::total;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_prep_kernel<DK, DV>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)l1);
   if (e != hipSuccess) return e;
@@ -570,8 +592,8 @@ static hipError_t launch_chunked_typed(const PrefillArgs& a, const float* y, con
   if (e != hipSuccess) return e;
   // Head index fastest, so the 16-row blocks of one head share an XCD's L2
   // (grid.x is a multiple of 8 whenever Hv is).
-  hipLaunchKernelGGL((chunk_state_kernel<DK, DV>), dim3(a.Hv * a.num_rows, DV / 16), dim3(256), l2,
-                     s, a, y, ws);
+  hipLaunchKernelGGL((chunk_state_kernel<DK, DV>), dim3(a.Hv * a.num_rows, DV / kStateRows),
+                     dim3(kStateThreads), l2, s, a, y, ws);
   return hipGetLastError();
 }
 

@@ -44,17 +44,20 @@ int unit_capacity(int stream_tokens, int rows) {
 WsLayout ws_layout(int Hk, int Hv, int dk, int dv, int stream_tokens, int rows) {
   const size_t C = 2ull * Hk * dk + (size_t)Hv * dv;
   const size_t n = stream_tokens > 0 ? (size_t)stream_tokens : 0;
+  // Arrays the chunk kernels read a 64-token tile at a time carry 64
+  // padding rows, so a row's last tile can be loaded whole.
+  const size_t np = n + 64;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   WsLayout w;
   size_t o = 0;
-  w.y = o;  o += al(n * C * 4);
+  w.y = o;  o += al(np * C * 4);
   w.kq = o; o += al(n * Hk * 4);
   w.ga = o; o += al(n * Hv * 4);
   w.gb = o; o += al(n * Hv * 4);
-  w.W = o;  o += al(n * Hv * dk * 4);
-  w.U = o;  o += al(n * Hv * dv * 4);
-  w.P = o;  o += al(n * Hv * 64 * 4);
-  w.G = o;  o += al(n * Hv * 4);
+  w.W = o;  o += al(np * Hv * dk * 4);
+  w.U = o;  o += al(np * Hv * dv * 4);
+  w.P = o;  o += al(np * Hv * 64 * 4);
+  w.G = o;  o += al(np * Hv * 4);
   w.units = unit_capacity(stream_tokens > 0 ? stream_tokens : 0, rows > 0 ? rows : 0);
   w.map = o; o += al((size_t)w.units * 2 * 4);
   w.total = o;

@@ -181,6 +181,45 @@ def _check_nonspec(case, slots):
     assert_states_close(g.host_ssm(slots), ssm_ref[slots])
 
 
+def _rows_case(seed, lens, dk, Hk=2, Hv=4):
+    """Prefill rows only (1-token rows included), slots 3.., random
+    has_initial_state and a random token_indx."""
+    rng = np.random.default_rng(seed)
+    T = int(sum(lens))
+    case = helpers.small_case(seed=seed, Hk=Hk, Hv=Hv, dk=dk, dv=dk, K=4, T=T,
+                              num_slots=len(lens) + 4)
+    slots = list(range(3, 3 + len(lens)))
+    his = rng.integers(0, 2, len(lens)).tolist()
+    tix = rng.permutation(T).astype(np.int32)
+    case["nonspec"] = helpers.nonspec_meta(lens, slots, his=his, tix=tix, num_decodes=0)
+    case["spec"] = None
+    case["name"] = "prefill-rows"
+    return case, [s for s, n in zip(slots, lens) if n > 0]
+
+
+@pytest.mark.parametrize("dk", [32, 64])
+def test_prefill_many_rows(dk):
+    # 70 rows of 0..150 tokens (some empty, some of one token) around a
+    # 700-token row: the 64-token unit map packs rows of every length, and
+    # empty rows touch neither pool.
+    rng = np.random.default_rng(50 + dk)
+    lens = rng.integers(0, 151, 70)
+    lens[rng.choice(70, 6, replace=False)] = 0
+    lens[rng.choice(70, 4, replace=False)] = 1
+    lens = lens.tolist()
+    lens.insert(35, 700)
+    case, touched = _rows_case(60 + dk, lens, dk)
+    _check_nonspec(case, touched)
+
+
+def test_prefill_rows_past_one_map_block():
+    # 1100 rows of 0..3 tokens: the unit map is built 1024 rows at a time.
+    rng = np.random.default_rng(7)
+    lens = rng.integers(0, 4, 1100).tolist()
+    case, touched = _rows_case(8, lens, 64, Hk=1, Hv=2)
+    _check_nonspec(case, touched)
+
+
 @pytest.mark.parametrize("dk", [64, 128])
 def test_chunked_prefill_chunk_edges(dk):
     # Rows ending one short of, on, and one past a 64-token chunk, a short
