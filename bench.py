@@ -115,14 +115,16 @@ def cpu_baseline(case, min_seconds=10.0):
                       f"tokens) {reps} times in a row on one thread, {dt:.1f} s"}
 
 
-def profiled_traffic():
+def profiled_traffic(workload):
     """HBM bytes per launch from the committed rocprofv3 counters, if they
-    were taken on the current kernel source."""
+    were taken on this workload and on the current kernel source."""
     import hashlib
     if not os.path.exists(PROFILE_TRAFFIC):
         return None
     with open(PROFILE_TRAFFIC) as f:
         rec = json.load(f)
+    if rec.get("workload") != workload:
+        return None
     src = os.path.join(ROOT, "speculative_decoding_causal_amd", "csrc", "gdn_rows.hip")
     with open(src, "rb") as f:
         cur = hashlib.sha256(f.read()).hexdigest()[:16]
@@ -241,7 +243,7 @@ def main():
     avg_launch_s = ms_per_step * 1e-3
     nbytes = algorithmic_bytes(case) + (nonspec_bytes(case) if ns is not None else 0)
     achieved = nbytes / avg_launch_s / 1e9
-    traffic = profiled_traffic() if ns is None else None
+    traffic = profiled_traffic(args.workload) if ns is None else None
     tokens = T_all if ns is not None else T_spec
 
     result = {

@@ -14,6 +14,8 @@ Shapes and value distributions (one record per workload):
            one NULL store
 ``qwen3next_k3_b64``  64 spec rows, K=3, 16 k-heads / 32 v-heads, dk=dv=128,
            C=8192, L=5, 512 slots, 192 distinct slots from [1, 512)
+``qwen3next_k3_b64_tp2``  the same batch on one GPU's share of a two-way
+           head split: 8 k-heads / 16 v-heads, C=4096
 ``deep_k4_b256``  256 spec rows, K=4, same heads, L=6, 2048 slots, at least
            one row with n_acc=1
 ``mixed``  32 spec rows (K=4) + 32 one-token decodes + 2 prefills of 1024
@@ -77,6 +79,8 @@ CONFIGS = {
                   num_slots=64, null_p=0.25),
     "qwen3next_k3_b64": dict(kind="spec", Ns=64, K=3, Hk=16, Hv=32, dk=128,
                              dv=128, W=4, num_slots=512, null_p=0.0),
+    "qwen3next_k3_b64_tp2": dict(kind="spec", Ns=64, K=3, Hk=8, Hv=16, dk=128,
+                                 dv=128, W=4, num_slots=512, null_p=0.0),
     "deep_k4_b256": dict(kind="spec", Ns=256, K=4, Hk=16, Hv=32, dk=128,
                          dv=128, W=4, num_slots=2048, null_p=0.0,
                          force_nacc1=True),

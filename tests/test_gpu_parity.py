@@ -59,6 +59,11 @@ def test_spec_qwen3next_k3_b64(permute):
     check_spec_case(synth.make_case("qwen3next_k3_b64", seed=3, permute_tokens=permute))
 
 
+def test_spec_qwen3next_k3_b64_tp2():
+    # the batch at one GPU's share of a two-way head split (8/16 heads)
+    check_spec_case(synth.make_case("qwen3next_k3_b64_tp2", seed=5, permute_tokens=True))
+
+
 def test_spec_deep_k4_b256_sampled():
     rows = list(range(0, 256, 11))
     case = synth.make_case("deep_k4_b256", seed=4, fill=rows)
