@@ -80,6 +80,15 @@ enum {
   GDN_ERR_METADATA = -9          /* gdn_check_metadata_host found a violation */
 };
 
+/* Channel order of mixed_qkv's rows [P1 "Test Plan", the reorder_input
+ * equivalence test].  Grouped: all q heads, then all k heads, then all v
+ * heads (C = 2*Hk*dk + Hv*dv), the input of the pages' reorder_input=True.
+ * Per k-head: for each k-head i in turn its q (dk), its k (dk) and the v of
+ * its G = Hv/Hk v-heads (G*dv), the projections as produced, read directly
+ * (reorder_input=False).  Only the reads of mixed_qkv depend on it: conv
+ * weights, conv bias, the conv ring and conv_out stay in grouped order. */
+enum { GDN_QKV_GROUPED = 0, GDN_QKV_PER_K_HEAD = 1 };
+
 /* Layer shape.  Supported by the kernels: head_k_dim == head_v_dim in
  * {16, 32, 64, 128}; 1 <= conv_width <= 4; conv_width-1 <= state_len <= 16;
  * num_v_heads a multiple of num_k_heads with (Hv/Hk)*head_v_dim <= 1024. */
@@ -95,6 +104,7 @@ typedef struct gdn_dims {
   int32_t use_qk_l2norm; /* 1: q, k <- x / sqrt(sum x^2 + l2norm_eps) */
   float l2norm_eps;
   float scale;           /* multiplies q after normalisation (o = scale S q) */
+  int32_t qkv_layout;    /* GDN_QKV_GROUPED (0) or GDN_QKV_PER_K_HEAD (1) */
 } gdn_dims;
 
 /* Largest tokens per row in a spec call (K) and per decode row. */

@@ -41,6 +41,8 @@ GDN_ERR_WORKSPACE = -6
 GDN_ERR_HIP = -7
 GDN_ERR_UNSUPPORTED = -8
 GDN_ERR_METADATA = -9
+GDN_QKV_GROUPED = 0
+GDN_QKV_PER_K_HEAD = 1
 GDN_ROWS_NON_SPEC = 0
 GDN_ROWS_SPEC = 1
 MAX_ROW_TOKENS = 16
@@ -59,7 +61,7 @@ class GdnDims(ctypes.Structure):
         ("conv_width", ctypes.c_int32), ("state_len", ctypes.c_int32),
         ("num_slots", ctypes.c_int32), ("activation", ctypes.c_int32),
         ("use_qk_l2norm", ctypes.c_int32), ("l2norm_eps", ctypes.c_float),
-        ("scale", ctypes.c_float),
+        ("scale", ctypes.c_float), ("qkv_layout", ctypes.c_int32),
     ]
 
 
@@ -124,6 +126,9 @@ class GdnConfig:
     use_qk_l2norm: int = 1
     l2norm_eps: float = 1e-6
     scale: float | None = None   # default head_k_dim ** -0.5
+    # mixed_qkv channel order: True = grouped [q | k | v] (GDN_QKV_GROUPED),
+    # False = per k-head [q_i k_i v_i ...] as projected (GDN_QKV_PER_K_HEAD)
+    reorder_input: bool = True
 
     @property
     def conv_dim(self) -> int:
@@ -137,7 +142,8 @@ class GdnConfig:
         return GdnDims(self.num_k_heads, self.num_v_heads, self.head_k_dim,
                        self.head_v_dim, self.conv_width, int(state_len),
                        int(num_slots), self.activation, self.use_qk_l2norm,
-                       float(self.l2norm_eps), float(scale))
+                       float(self.l2norm_eps), float(scale),
+                       GDN_QKV_GROUPED if self.reorder_input else GDN_QKV_PER_K_HEAD)
 
 
 def _ptr(t, dtype=None, name="tensor", device=None):

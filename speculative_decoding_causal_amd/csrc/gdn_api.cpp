@@ -57,6 +57,8 @@ int check_dims(const gdn_dims* d) {
   if (d->use_qk_l2norm != 0 && d->use_qk_l2norm != 1)
     return fail(GDN_ERR_DIMS, "use_qk_l2norm must be 0 or 1");
   if (!(d->l2norm_eps >= 0.f)) return fail(GDN_ERR_DIMS, "l2norm_eps must be >= 0");
+  if (d->qkv_layout != GDN_QKV_GROUPED && d->qkv_layout != GDN_QKV_PER_K_HEAD)
+    return fail(GDN_ERR_DIMS, "qkv_layout must be GDN_QKV_GROUPED (0) or GDN_QKV_PER_K_HEAD (1)");
   const int G = d->num_v_heads / d->num_k_heads;
   if (G * d->head_v_dim > 1024)
     return fail(GDN_ERR_UNSUPPORTED, "(Hv/Hk)*head_v_dim = %d exceeds 1024", G * d->head_v_dim);
@@ -78,6 +80,7 @@ void fill_common(gdn::RowArgs& a, const gdn_dims* d, int num_actual_tokens) {
   a.num_slots = d->num_slots;
   a.act = d->activation;
   a.l2norm = d->use_qk_l2norm;
+  a.qkv_layout = d->qkv_layout;
   a.eps = d->l2norm_eps;
   a.scale = d->scale;
   a.num_actual_tokens = num_actual_tokens;
@@ -328,6 +331,9 @@ int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
     p.num_slots = dims->num_slots;
     p.act = dims->activation;
     p.l2norm = dims->use_qk_l2norm;
+    p.dk = dims->head_k_dim;
+    p.dv = dims->head_v_dim;
+    p.qkv_layout = dims->qkv_layout;
     p.eps = dims->l2norm_eps;
     p.scale = dims->scale;
     p.num_actual_tokens = num_actual_tokens;

@@ -75,6 +75,18 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Column of mixed_qkv holding grouped channel c ([q heads | k heads | v
+// heads]) when the rows are laid out per k-head (q_i, k_i, then the v of
+// the k-head's G v-heads, block after block).
+__device__ __forceinline__ int per_k_head_column(int c, int Hk, int G, int dk, int dv) {
+  const int B = 2 * dk + G * dv;
+  if (c < Hk * dk) return (c / dk) * B + c % dk;
+  c -= Hk * dk;
+  if (c < Hk * dk) return (c / dk) * B + dk + c % dk;
+  c -= Hk * dk;
+  return (c / (G * dv)) * B + 2 * dk + c % (G * dv);
+}
+
 __device__ __forceinline__ int clampi(int v, int lo, int hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }

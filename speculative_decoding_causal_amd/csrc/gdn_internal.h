@@ -20,6 +20,7 @@ enum Stage : int { kFused = 0, kConvOnly = 1, kDeltaOnly = 2 };
 struct RowArgs {
   // shape
   int Hk, Hv, G, C, L, W, num_slots, act, l2norm;
+  int qkv_layout;  // 0 grouped [q | k | v], 1 per k-head [q_i k_i v_i..]
   float eps, scale;
   int num_actual_tokens;
   // layer tensors
@@ -58,6 +59,7 @@ size_t rows_lds_bytes(const RowArgs& a, int dk, int dv);
 // then the delta rule over the row.
 struct PrefillArgs {
   int Hk, Hv, G, C, L, W, num_slots, act, l2norm;
+  int dk, dv, qkv_layout;
   float eps, scale;
   int num_actual_tokens;
   const uint16_t* qkv;

@@ -154,12 +154,13 @@ conv_prefill_kernel(PrefillArgs p, float* __restrict__ y) {
   if (base >= pr.T) return;
   const int end = min(pr.T, base + kSeg);
   const uint16_t* ring = p.conv_pool + (size_t)pr.slot * L * C + c;
+  const int cin = p.qkv_layout ? per_k_head_column(c, p.Hk, p.G, p.dk, p.dv) : c;
 
   // Input at row position t; t < 0 reads ring column L + t (history).
   auto xin = [&](int t) -> uint16_t {
     if (t >= 0) {
       int r = global_row(p, pr.j0 + t);
-      return r >= 0 ? p.qkv[(size_t)r * C + c] : (uint16_t)0;
+      return r >= 0 ? p.qkv[(size_t)r * C + cin] : (uint16_t)0;
     }
     return pr.init ? ring[(size_t)(L + t) * C] : (uint16_t)0;
   };

@@ -194,16 +194,24 @@ __device__ __forceinline__ int channel_of(int pc, int ih, int Hk, int DK, int NR
   return 2 * Hk * DK + ih * NR + (pc - 2 * DK);
 }
 
+// Column of mixed_qkv for channel position pc (grouped channel c) of k-head
+// ih: with the per-k-head layout the workgroup's channels are one block.
+__device__ __forceinline__ int input_column(const RowArgs& p, int pc, int c, int ih, int DK,
+                                            int NR) {
+  return p.qkv_layout ? ih * (2 * DK + NR) + pc : c;
+}
+
 template <int LM, int KT>
 __device__ __forceinline__ void load_chan(ChanIn<LM, KT>& in, const RowArgs& p,
-                                          const RowPlan& rp, int c, const int (&rj)[KT]) {
+                                          const RowPlan& rp, int c, int cin,
+                                          const int (&rj)[KT]) {
   const bool hist = rp.read_hist && rp.conv_slot > 0;
   const uint16_t* ring = p.conv_pool + (size_t)rp.conv_slot * p.L * p.C + c;
 #pragma unroll
   for (int l = 0; l < LM; ++l) in.h[l] = (hist && l < p.L) ? ring[(size_t)l * p.C] : (uint16_t)0;
 #pragma unroll
   for (int j = 0; j < KT; ++j)
-    in.x[j] = rj[j] >= 0 ? p.qkv[(size_t)rj[j] * p.C + c] : (uint16_t)0;
+    in.x[j] = rj[j] >= 0 ? p.qkv[(size_t)rj[j] * p.C + cin] : (uint16_t)0;
 #pragma unroll
   for (int m = 0; m < kMaxWidth; ++m)
     in.w[m] = m < p.W ? bf2f(p.conv_w[(size_t)c * p.W + m]) : 0.f;
@@ -330,7 +338,7 @@ gdn_rows_kernel(RowArgs p) {
   {
     ChanIn<LM, KT> in0;
     if (have_chan) {
-      load_chan<LM, KT>(in0, p, rp, c0, rj);
+      load_chan<LM, KT>(in0, p, rp, c0, input_column(p, tid, c0, ih, DK, NR), rj);
 #pragma unroll
       for (int m = 0; m < kMaxWidth; ++m) w0[m] = in0.w[m];
       bias0 = in0.bias;
@@ -370,7 +378,7 @@ gdn_rows_kernel(RowArgs p) {
       conv_chan<KT>(w0, bias0, p, rp, c, pc, NCH, T, zb, dst, dstride, rj);
     } else {
       ChanIn<LM, KT> in;
-      load_chan<LM, KT>(in, p, rp, c, rj);
+      load_chan<LM, KT>(in, p, rp, c, input_column(p, pc, c, ih, DK, NR), rj);
       stage_chan<LM, KT>(in, L, T, pc, NCH, zb);
       conv_chan<KT>(in.w, in.bias, p, rp, c, pc, NCH, T, zb, dst, dstride, rj);
     }
