@@ -111,6 +111,20 @@ typedef struct gdn_dims {
 #define GDN_MAX_ROW_TOKENS 16
 
 /*
+ * Graph-padded calls [P1 "Related issues": the size(0) == num_actual_tokens
+ * precondition under graph capture; P2: graph-padded spec metadata].  A call
+ * enqueues kernels only (no allocation, memset or host synchronisation; the
+ * first call per device and kernel raises its LDS limit), so it can be
+ * captured into a HIP graph.  The scalars are then frozen, so a captured
+ * call is made at padded sizes: num_actual_tokens, row and token counts as
+ * the graph's buffers hold them.  Rows that are padding carry NULL (<= 0)
+ * slots in every index array (spec_state_indices, spec_cache_indices,
+ * non-spec cache indices) and their tokens map to rows of the buffers that
+ * no real token uses: they read and write no pool, and only their own
+ * output rows are written.  Real rows give the same bits as an unpadded call.
+ */
+
+/*
  * gdn_spec_attention - one spec-verify step over `num_spec_decodes` rows.
  *
  * Row b owns tokens [spec_query_start_loc[b], spec_query_start_loc[b+1]) of

@@ -193,10 +193,13 @@ def gdn_spec_attention(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias,
                        spec_query_start_loc, spec_state_indices,
                        num_accepted_tokens, core_attn_out,
                        spec_cache_indices=None, spec_token_indx=None,
-                       num_spec_tokens: int | None = None, stream=None) -> None:
+                       num_spec_tokens: int | None = None, num_actual_tokens: int | None = None,
+                       stream=None) -> None:
     """One spec-verify step (see ``include/gdn.h``); pools are updated in
     place and ``core_attn_out`` [num_actual_tokens, Hv, dv] is written at the
-    rows named by ``spec_token_indx``."""
+    rows named by ``spec_token_indx``.  ``num_actual_tokens`` defaults to the
+    rows of ``mixed_qkv``; pass ``num_spec_tokens`` too when capturing the
+    call in a graph (it is read back from the device otherwise)."""
     dev = mixed_qkv.device
     _check_pools(cfg, conv_state, ssm_state)
     dims = cfg.dims(conv_state)
@@ -208,7 +211,8 @@ def gdn_spec_attention(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias,
         _ptr(b, _BF16, "b", dev), _ptr(conv_weight, _BF16, "conv_weight", dev),
         _ptr(conv_bias, _BF16, "conv_bias", dev), _ptr(A_log, torch.float32, "A_log", dev),
         _ptr(dt_bias, torch.float32, "dt_bias", dev), _ptr(conv_state, _BF16, "conv_state", dev),
-        _ptr(ssm_state, torch.float32, "ssm_state", dev), int(mixed_qkv.shape[0]), Ns, T, K,
+        _ptr(ssm_state, torch.float32, "ssm_state", dev),
+        int(mixed_qkv.shape[0] if num_actual_tokens is None else num_actual_tokens), Ns, T, K,
         _ptr(spec_query_start_loc, _I32, "spec_query_start_loc", dev),
         _ptr(spec_cache_indices, _I32, "spec_cache_indices", dev),
         _ptr(spec_state_indices, _I32, "spec_state_indices", dev),
@@ -234,7 +238,7 @@ def gdn_attention(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias, A_log
                   spec_query_start_loc=None, spec_state_indices=None,
                   num_accepted_tokens=None, spec_cache_indices=None,
                   spec_token_indx=None, num_spec_tokens=None, workspace=None,
-                  stream=None) -> None:
+                  num_actual_tokens=None, stream=None) -> None:
     """A layer step over a batch of non-spec rows (decodes, then prefills)
     and spec rows.  ``workspace`` (uint8 device tensor) is needed when
     ``num_prefills > 0``; size it with ``gdn_workspace_bytes``."""
@@ -251,7 +255,8 @@ def gdn_attention(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias, A_log
         _ptr(b, _BF16, "b", dev), _ptr(conv_weight, _BF16, "conv_weight", dev),
         _ptr(conv_bias, _BF16, "conv_bias", dev), _ptr(A_log, torch.float32, "A_log", dev),
         _ptr(dt_bias, torch.float32, "dt_bias", dev), _ptr(conv_state, _BF16, "conv_state", dev),
-        _ptr(ssm_state, torch.float32, "ssm_state", dev), int(mixed_qkv.shape[0]),
+        _ptr(ssm_state, torch.float32, "ssm_state", dev),
+        int(mixed_qkv.shape[0] if num_actual_tokens is None else num_actual_tokens),
         int(num_decodes), int(num_prefills), int(num_non_spec_tokens),
         _ptr(query_start_loc, _I32, "query_start_loc", dev),
         _ptr(non_spec_state_indices, _I32, "non_spec_state_indices", dev),

@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <set>
 #include <vector>
 
@@ -30,6 +31,28 @@ int fail(int code, const char* fmt, ...) {
   va_end(ap);
   return code;
 }
+
+}  // namespace
+
+namespace gdn {
+hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes) {
+  // (kernel, device) pairs whose limit is already at least `bytes`
+  struct Entry { const void* k; int dev; size_t bytes; };
+  static std::mutex mu;
+  static std::vector<Entry> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& x : done)
+    if (x.k == kernel && x.dev == dev && x.bytes >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done.push_back({kernel, dev, bytes});
+  return e;
+}
+}  // namespace gdn
+
+namespace {
 
 int check_dims(const gdn_dims* d) {
   if (!d) return fail(GDN_ERR_NULL, "dims is NULL");

@@ -578,11 +578,9 @@ static hipError_t launch_chunked_typed(const PrefillArgs& a, const float* y, con
                                        const float* gbeta, const ChunkWs& ws, hipStream_t s) {
   const size_t l1 = sizeof(float) * PrepLds<DK>::total;
   const size_t l2 = sizeof(float) * StateLds<DK, kStateRows>::total;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_prep_kernel<DK, DV>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)l1);
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(chunk_prep_kernel<DK, DV>), l1);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_state_kernel<DK, DV>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)l2);
+  e = ensure_dynamic_lds(reinterpret_cast<const void*>(chunk_state_kernel<DK, DV>), l2);
   if (e != hipSuccess) return e;
   if (a.units <= 0) return hipSuccess;
   // one workgroup per (v-head, 64-token unit of a row), head index fastest

@@ -16,6 +16,10 @@ constexpr int kMaxWidth = 4;
 enum RowKind : int { kNonSpec = 0, kSpec = 1 };
 enum Stage : int { kFused = 0, kConvOnly = 1, kDeltaOnly = 2 };
 
+// Raise a kernel's dynamic LDS limit once per device (kernel launches may be
+// captured into a graph; the attribute is set outside any stream work).
+hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes);
+
 // Everything one launch of the row kernel needs, passed by value.
 struct RowArgs {
   // shape

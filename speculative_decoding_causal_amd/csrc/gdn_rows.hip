@@ -547,9 +547,7 @@ hipError_t launch_typed(const RowArgs& a, hipStream_t s) {
   constexpr int RB = DK == 128 ? GDN_ROWS_RB128 : R;
   auto kern = gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT, RB>;
   if (lay.total > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       lay.total);
+    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lay.total);
     if (e != hipSuccess) return e;
   }
   dim3 grid(static_cast<unsigned>(a.num_rows) * static_cast<unsigned>(a.Hk));

@@ -1,0 +1,145 @@
+"""Graph-padded calls under HIP graph capture.
+
+"[GDN] Spec-decoding-aware attention kernel" ("Related issues") names the
+size(0) == num_actual_tokens precondition that breaks graph capture, and the
+graph-padded spec metadata is named on "[XE2] Support MTP of QWEN model".
+Reading: a step is captured once at padded shapes (scalars are frozen in the
+graph) and replayed with batches of fewer real rows.  Pad rows carry NULL (0)
+slots and their tokens sit in rows past the real ones, so they read and write
+no pool; the real rows must equal an eager call on the unpadded batch bit for
+bit, replay after replay, with eager work between the replays."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from tests import helpers
+from tests.gpu_util import Gpu, bf, cfg_of, f32, gpu_available, i32, say, u8
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU and libgdn.so")]
+
+Hk, Hv, DK, K, SLOTS = 4, 8, 128, 3, 96
+NS_PAD, ND_PAD = 8, 6
+
+
+def scenario(seed, ns, nd):
+    """Padded metadata for ns real spec rows and nd real decodes, and the
+    unpadded case with the same real rows."""
+    rng = np.random.default_rng(seed)
+    t_pad = ND_PAD + NS_PAD * K
+    t_real = nd + ns * K
+    case = helpers.small_case(seed=seed, Hk=Hk, Hv=Hv, dk=DK, dv=DK, K=K, T=t_pad,
+                              num_slots=SLOTS)
+    slots = rng.choice(np.arange(1, SLOTS), ns * K + nd, replace=False).astype(np.int32)
+    rows = rng.permutation(t_real).astype(np.int32)      # real tokens -> rows [0, t_real)
+    pad_rows = np.arange(t_real, t_pad, dtype=np.int32)  # pad tokens -> rows past them
+    # spec rows
+    ssi = np.zeros((NS_PAD, K), np.int32)
+    ssi[:ns] = slots[:ns * K].reshape(ns, K)
+    nacc = np.ones(NS_PAD, np.int32)
+    nacc[:ns] = rng.integers(1, K + 1, ns)
+    sqsl = np.arange(0, NS_PAD * K + 1, K, dtype=np.int32)
+    stix = np.concatenate([rows[:ns * K], pad_rows[:(NS_PAD - ns) * K]]).astype(np.int32)
+    # decode rows
+    cache = np.zeros(ND_PAD, np.int32)
+    cache[:nd] = slots[ns * K:]
+    his = np.zeros(ND_PAD, np.uint8)
+    his[:nd] = rng.integers(0, 2, nd)
+    dtix = np.concatenate([rows[ns * K:], pad_rows[(NS_PAD - ns) * K:]]).astype(np.int32)
+    dqsl = np.arange(ND_PAD + 1, dtype=np.int32)
+    padded = dict(sqsl=sqsl, ssi=ssi, nacc=nacc, stix=stix, dqsl=dqsl, cache=cache, his=his,
+                  dtix=dtix, t=t_pad)
+    real = dict(case)
+    for k in ("mixed_qkv", "a", "b"):
+        real[k] = case[k][:t_real]
+    real["num_actual_tokens"] = t_real
+    real["spec"] = (helpers.spec_meta(sqsl[:ns + 1], ssi[:ns], nacc[:ns], stix[:ns * K])
+                    if ns else None)
+    real["nonspec"] = (helpers.nonspec_meta([1] * nd, cache[:nd], his=his[:nd], tix=dtix[:nd])
+                       if nd else None)
+    return case, padded, real
+
+
+class Static:
+    """Device buffers a captured step reads and writes (fixed addresses)."""
+
+    def __init__(self, case, padded, with_decodes):
+        self.g = Gpu(case)
+        self.cfg = cfg_of(case)
+        self.meta = {k: (i32(v) if v.dtype == np.int32 else u8(v))
+                     for k, v in padded.items() if k != "t"}
+        self.t = padded["t"]
+        self.with_decodes = with_decodes
+
+    def load(self, case, padded):
+        g = self.g
+        for name, t, src in (("qkv", g.qkv, case["mixed_qkv"]), ("a", g.a, case["a"]),
+                             ("b", g.b, case["b"]), ("w", g.w, case["conv_weight"]),
+                             ("conv", g.conv, case["conv_state"])):
+            t.copy_(bf(src))
+        g.A_log.copy_(f32(case["A_log"]))
+        g.dt_bias.copy_(f32(case["dt_bias"]))
+        g.ssm.copy_(f32(case["ssm_state"]))
+        for k, t in self.meta.items():
+            t.copy_(i32(padded[k]) if padded[k].dtype == np.int32 else u8(padded[k]))
+
+    def call(self):
+        import speculative_decoding_causal_amd as gdn
+        g, m = self.g, self.meta
+        spec = dict(spec_query_start_loc=m["sqsl"], spec_state_indices=m["ssi"],
+                    num_accepted_tokens=m["nacc"], spec_token_indx=m["stix"],
+                    num_spec_tokens=NS_PAD * K)
+        if not self.with_decodes:
+            gdn.gdn_spec_attention(self.cfg, g.qkv[:NS_PAD * K], g.a[:NS_PAD * K],
+                                   g.b[:NS_PAD * K], g.w, None, g.A_log, g.dt_bias, g.conv,
+                                   g.ssm, m["sqsl"], m["ssi"], m["nacc"], g.out,
+                                   spec_token_indx=m["stix"], num_spec_tokens=NS_PAD * K,
+                                   num_actual_tokens=NS_PAD * K)
+        else:
+            gdn.gdn_attention(self.cfg, g.qkv, g.a, g.b, g.w, None, g.A_log, g.dt_bias, g.conv,
+                              g.ssm, g.out, num_decodes=ND_PAD, num_non_spec_tokens=ND_PAD,
+                              query_start_loc=m["dqsl"],
+                              non_spec_state_indices=m["cache"], has_initial_state=m["his"],
+                              non_spec_token_indx=m["dtix"], num_actual_tokens=self.t, **spec)
+
+
+def _run_graph(with_decodes, plan):
+    case0, pad0, _ = scenario(*plan[0])
+    st = Static(case0, pad0, with_decodes)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st.call()                       # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st.call()
+    for seed, ns, nd in plan:
+        case, padded, real = scenario(seed, ns, nd)
+        st.load(case, padded)
+        torch.cuda.synchronize()
+        say(f"graph replay: {ns} spec rows, {nd} decodes (padded to {NS_PAD}, {ND_PAD})")
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = Gpu(real)
+        if with_decodes:
+            eager.attention()
+        else:
+            eager.spec()
+        torch.cuda.synchronize()
+        t_real = real["num_actual_tokens"]
+        np.testing.assert_array_equal(st.g.host_out()[:t_real], eager.host_out())
+        np.testing.assert_array_equal(st.g.host_conv(), eager.host_conv())
+        np.testing.assert_array_equal(st.g.host_ssm(), eager.host_ssm())
+
+
+def test_graph_padded_spec_replays():
+    # spec-only graph: the padded step uses the first NS_PAD * K input rows
+    _run_graph(False, [(300, 8, 0), (301, 5, 0), (302, 2, 0), (303, 8, 0), (304, 1, 0)])
+
+
+def test_graph_padded_decodes_and_spec_replays():
+    _run_graph(True, [(310, 8, 6), (311, 3, 4), (312, 6, 0), (313, 0, 5), (314, 8, 6)])
