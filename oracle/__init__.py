@@ -55,7 +55,7 @@ class Dims(ctypes.Structure):
         ("num_slots", ctypes.c_int32),
         ("activation", ctypes.c_int32),
         ("use_qk_l2norm", ctypes.c_int32),
-        ("pad_", ctypes.c_int32),
+        ("conv_layout", ctypes.c_int32),
         ("l2norm_eps", ctypes.c_double),
         ("scale", ctypes.c_double),
     ]
@@ -99,7 +99,8 @@ def _ptr(arr, dtype=None):
 def make_dims(d: dict) -> Dims:
     return Dims(int(d["Hk"]), int(d["Hv"]), int(d["dk"]), int(d["dv"]),
                 int(d["W"]), int(d["L"]), int(d["num_slots"]),
-                int(d.get("activation", 1)), int(d.get("use_qk_l2norm", 1)), 0,
+                int(d.get("activation", 1)), int(d.get("use_qk_l2norm", 1)),
+                int(d.get("conv_layout", 0)),
                 float(d.get("eps", 1e-6)), float(d["scale"]))
 
 

@@ -42,6 +42,9 @@
  *   - softplus(x) = x for x > 20, else log1p(exp(x));
  *   - GQA: v-head h reads k-head floor(h / (Hv/Hk));
  *   - non-spec rows read the conv window at the ring tail and roll by T_i;
+ *   - with per-token checkpoint slots (conv_layout 1) a spec row's conv slots
+ *     are its SSM slots, each holding one window (state_len == W-1), and
+ *     spec_cache_indices is not used;
  *   - a slot value <= 0 (NULL_BLOCK_ID / pad slot) means "no prior state":
  *     zeros are read and nothing is written.
  */
@@ -60,7 +63,7 @@ typedef struct oracle_dims {
   int32_t num_slots;    /* slots in both pools */
   int32_t activation;   /* 0 identity, 1 SiLU */
   int32_t use_qk_l2norm;
-  int32_t pad_;
+  int32_t conv_layout;  /* 0 rolled history, 1 per-token checkpoint slots */
   double l2norm_eps;
   double scale;
 } oracle_dims;
@@ -140,6 +143,7 @@ static int dims_ok(const oracle_dims* d) {
   if (d->head_k_dim <= 0 || d->head_v_dim <= 0) return 0;
   if (d->conv_width < 1 || d->state_len < d->conv_width - 1) return 0;
   if (d->num_slots <= 0) return 0;
+  if (d->conv_layout != 0 && d->conv_layout != 1) return 0;
   return 1;
 }
 
@@ -193,6 +197,45 @@ static void conv_row(const oracle_dims* d, const uint16_t* mixed_qkv,
     }
   }
   free(H);
+  free(xs);
+}
+
+/*
+ * Conv of one spec row with per-token checkpoint slots ("[XE2] Support MTP
+ * of QWEN model", review of the spec conv kernel: the conv state is saved
+ * after every spec token into that token's cache slot, as the SSM states
+ * are).  A slot holds one window: its columns 0..W-2 are the last W-1 conv
+ * inputs, oldest first (state_len == W-1).  The window before the row's
+ * first token is read from slot load_slot (zeros if <= 0); after token j
+ * the last W-1 samples of (window ++ inputs 0..j) go to save_slots[j] when
+ * that is > 0, in token order.  Every read of a channel precedes its writes.
+ */
+static void conv_row_per_token(const oracle_dims* d, const uint16_t* mixed_qkv,
+                               const int32_t* rows, int32_t T, const uint16_t* w,
+                               const uint16_t* bias, uint16_t* conv_state,
+                               int32_t load_slot, const int32_t* save_slots, double* y) {
+  const int64_t C = conv_channels(d);
+  const int32_t L = d->state_len, W = d->conv_width;
+  uint16_t* xs = (uint16_t*)calloc((size_t)(W - 1 + T), sizeof(uint16_t));
+  for (int64_t c = 0; c < C; ++c) {
+    for (int32_t m = 0; m < W - 1; ++m)
+      xs[m] = load_slot > 0 ? conv_state[((int64_t)load_slot * L + m) * C + c] : (uint16_t)0;
+    for (int32_t j = 0; j < T; ++j)
+      xs[W - 1 + j] = mixed_qkv[(int64_t)rows[j] * C + c];
+    double bc = bias ? bf16_value(bias[c]) : 0.0;
+    for (int32_t j = 0; j < T; ++j) {
+      double acc = bc;
+      for (int32_t m = 0; m < W; ++m)
+        acc += bf16_value(w[c * W + m]) * bf16_value(xs[j + m]);
+      if (d->activation == 1) acc = acc / (1.0 + exp(-acc));
+      y[(int64_t)j * C + c] = acc;
+    }
+    for (int32_t j = 0; j < T; ++j) {
+      if (save_slots[j] <= 0) continue;
+      for (int32_t m = 0; m < W - 1; ++m)
+        conv_state[((int64_t)save_slots[j] * L + m) * C + c] = xs[j + 1 + m];
+    }
+  }
   free(xs);
 }
 
@@ -325,7 +368,12 @@ int oracle_spec_step(const oracle_dims* d, const uint16_t* mixed_qkv,
     const int32_t n = num_accepted_tokens[bi];
     const int32_t* ssi = spec_state_indices + (int64_t)bi * K;
     const int32_t cs = spec_cache_indices ? spec_cache_indices[bi] : ssi[0];
-    if (T < 1 || T > K || n < 1 || n > T || n - 1 + W - 1 > L ||
+    const int per_token = d->conv_layout == 1;
+    if (per_token && (spec_cache_indices || L != W - 1)) {
+      status = ORACLE_ERR_DIMS;
+      break;
+    }
+    if (T < 1 || T > K || n < 1 || n > T || (!per_token && n - 1 + W - 1 > L) ||
         cs >= d->num_slots) {
       status = ORACLE_ERR_META;
       break;
@@ -338,8 +386,12 @@ int oracle_spec_step(const oracle_dims* d, const uint16_t* mixed_qkv,
         status = ORACLE_ERR_META;
     }
     if (status != ORACLE_OK) break;
-    conv_row(d, mixed_qkv, rows, T, conv_weight, conv_bias, conv_state, cs,
-             /*read_hist=*/1, /*off=*/n - 1, /*shift=*/n, y);
+    if (per_token)
+      conv_row_per_token(d, mixed_qkv, rows, T, conv_weight, conv_bias, conv_state,
+                         ssi[n - 1], stores, y);
+    else
+      conv_row(d, mixed_qkv, rows, T, conv_weight, conv_bias, conv_state, cs,
+               /*read_hist=*/1, /*off=*/n - 1, /*shift=*/n, y);
     if (conv_out)
       for (int32_t j = 0; j < T; ++j)
         memcpy(conv_out + (int64_t)rows[j] * C, y + (int64_t)j * C,
