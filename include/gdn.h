@@ -89,6 +89,17 @@ enum {
  * weights, conv bias, the conv ring and conv_out stay in grouped order. */
 enum { GDN_QKV_GROUPED = 0, GDN_QKV_PER_K_HEAD = 1 };
 
+/* Conv-state contract of spec rows ("[XE2] Support MTP of QWEN model", the
+ * conv-checkpoint review thread: both can be right).  Rolled history: one
+ * slot per row (spec_cache_indices[b], else spec_state_indices[b][0]) holds
+ * a ring of state_len columns read at n_acc-1 and rolled.  Per-token slots:
+ * each slot holds one window (state_len == conv_width-1); the window is read
+ * from spec_state_indices[b][n_acc-1] and, after token t, the window ending
+ * at t is written to spec_state_indices[b][t] (NULL slots skipped), as the
+ * SSM states are; spec_cache_indices must then be NULL.  Non-spec rows are
+ * the same under both. */
+enum { GDN_CONV_ROLLED_HISTORY = 0, GDN_CONV_PER_TOKEN_SLOTS = 1 };
+
 /* Layer shape.  Supported by the kernels: head_k_dim == head_v_dim in
  * {16, 32, 64, 128}; 1 <= conv_width <= 4; conv_width-1 <= state_len <= 16;
  * num_v_heads a multiple of num_k_heads with (Hv/Hk)*head_v_dim <= 1024. */
@@ -105,6 +116,7 @@ typedef struct gdn_dims {
   float l2norm_eps;
   float scale;           /* multiplies q after normalisation (o = scale S q) */
   int32_t qkv_layout;    /* GDN_QKV_GROUPED (0) or GDN_QKV_PER_K_HEAD (1) */
+  int32_t conv_layout;   /* GDN_CONV_ROLLED_HISTORY (0) or GDN_CONV_PER_TOKEN_SLOTS (1) */
 } gdn_dims;
 
 /* Largest tokens per row in a spec call (K) and per decode row. */
@@ -259,7 +271,7 @@ int gdn_delta_rule_only(const gdn_dims* dims, const float* conv_out,
  * tensors (same meaning as in gdn_attention; any group may be absent by
  * passing 0 rows).  Checks: query_start_loc starts at 0 and is
  * non-decreasing; decode rows hold one token; spec rows hold 1..max_spec_len
- * tokens; 1 <= n_acc <= T_b and n_acc + W - 2 <= state_len; slots
+ * tokens; 1 <= n_acc <= T_b and (rolled history) n_acc + W - 2 <= state_len; slots
  * < num_slots; token rows in [0, num_actual_tokens) and distinct across both
  * streams; slots of different rows disjoint.  Returns GDN_OK or
  * GDN_ERR_METADATA (with gdn_last_error() naming the first violation).

@@ -43,6 +43,8 @@ GDN_ERR_UNSUPPORTED = -8
 GDN_ERR_METADATA = -9
 GDN_QKV_GROUPED = 0
 GDN_QKV_PER_K_HEAD = 1
+GDN_CONV_ROLLED_HISTORY = 0
+GDN_CONV_PER_TOKEN_SLOTS = 1
 GDN_ROWS_NON_SPEC = 0
 GDN_ROWS_SPEC = 1
 MAX_ROW_TOKENS = 16
@@ -62,6 +64,7 @@ class GdnDims(ctypes.Structure):
         ("num_slots", ctypes.c_int32), ("activation", ctypes.c_int32),
         ("use_qk_l2norm", ctypes.c_int32), ("l2norm_eps", ctypes.c_float),
         ("scale", ctypes.c_float), ("qkv_layout", ctypes.c_int32),
+        ("conv_layout", ctypes.c_int32),
     ]
 
 
@@ -129,6 +132,9 @@ class GdnConfig:
     # mixed_qkv channel order: True = grouped [q | k | v] (GDN_QKV_GROUPED),
     # False = per k-head [q_i k_i v_i ...] as projected (GDN_QKV_PER_K_HEAD)
     reorder_input: bool = True
+    # conv state of spec rows: GDN_CONV_ROLLED_HISTORY (one rolled ring per
+    # row) or GDN_CONV_PER_TOKEN_SLOTS (a window per token slot, L = W-1)
+    conv_layout: int = GDN_CONV_ROLLED_HISTORY
 
     @property
     def conv_dim(self) -> int:
@@ -143,7 +149,8 @@ class GdnConfig:
                        self.head_v_dim, self.conv_width, int(state_len),
                        int(num_slots), self.activation, self.use_qk_l2norm,
                        float(self.l2norm_eps), float(scale),
-                       GDN_QKV_GROUPED if self.reorder_input else GDN_QKV_PER_K_HEAD)
+                       GDN_QKV_GROUPED if self.reorder_input else GDN_QKV_PER_K_HEAD,
+                       int(self.conv_layout))
 
 
 def _ptr(t, dtype=None, name="tensor", device=None):

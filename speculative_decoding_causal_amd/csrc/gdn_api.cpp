@@ -82,6 +82,12 @@ int check_dims(const gdn_dims* d) {
   if (!(d->l2norm_eps >= 0.f)) return fail(GDN_ERR_DIMS, "l2norm_eps must be >= 0");
   if (d->qkv_layout != GDN_QKV_GROUPED && d->qkv_layout != GDN_QKV_PER_K_HEAD)
     return fail(GDN_ERR_DIMS, "qkv_layout must be GDN_QKV_GROUPED (0) or GDN_QKV_PER_K_HEAD (1)");
+  if (d->conv_layout != GDN_CONV_ROLLED_HISTORY && d->conv_layout != GDN_CONV_PER_TOKEN_SLOTS)
+    return fail(GDN_ERR_DIMS, "conv_layout must be GDN_CONV_ROLLED_HISTORY (0) or "
+                              "GDN_CONV_PER_TOKEN_SLOTS (1)");
+  if (d->conv_layout == GDN_CONV_PER_TOKEN_SLOTS && d->state_len != d->conv_width - 1)
+    return fail(GDN_ERR_DIMS, "per-token conv slots hold one window: state_len must be "
+                              "conv_width-1 (%d), got %d", d->conv_width - 1, d->state_len);
   const int G = d->num_v_heads / d->num_k_heads;
   if (G * d->head_v_dim > 1024)
     return fail(GDN_ERR_UNSUPPORTED, "(Hv/Hk)*head_v_dim = %d exceeds 1024", G * d->head_v_dim);
@@ -104,6 +110,7 @@ void fill_common(gdn::RowArgs& a, const gdn_dims* d, int num_actual_tokens) {
   a.act = d->activation;
   a.l2norm = d->use_qk_l2norm;
   a.qkv_layout = d->qkv_layout;
+  a.conv_per_token = d->conv_layout == GDN_CONV_PER_TOKEN_SLOTS;
   a.eps = d->l2norm_eps;
   a.scale = d->scale;
   a.num_actual_tokens = num_actual_tokens;
@@ -259,6 +266,8 @@ int gdn_spec_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
               spec_cache_indices, spec_state_indices, num_accepted_tokens, spec_token_indx};
   if (int e = check_spec(s, num_actual_tokens)) return e;
   if (num_spec_decodes == 0) return GDN_OK;
+  if (dims->conv_layout == GDN_CONV_PER_TOKEN_SLOTS && spec_cache_indices)
+    return fail(GDN_ERR_DIMS, "spec_cache_indices is not used with per-token conv slots");
   if (int e = check_layer_ptrs(mixed_qkv, a, b, conv_weight, A_log, dt_bias, conv_state,
                                ssm_state, core_attn_out))
     return e;
@@ -294,6 +303,9 @@ int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
   SpecBatch s{num_spec_decodes, num_spec_tokens, max_spec_len, spec_query_start_loc,
               spec_cache_indices, spec_state_indices, num_accepted_tokens, spec_token_indx};
   if (int e = check_spec(s, num_actual_tokens)) return e;
+  if (dims->conv_layout == GDN_CONV_PER_TOKEN_SLOTS && num_spec_decodes > 0 &&
+      spec_cache_indices)
+    return fail(GDN_ERR_DIMS, "spec_cache_indices is not used with per-token conv slots");
   const int ns_rows = num_decodes + num_prefills;
   if (ns_rows == 0 && num_non_spec_tokens != 0)
     return fail(GDN_ERR_DIMS, "num_non_spec_tokens=%d with no non-spec rows", num_non_spec_tokens);
@@ -403,6 +415,9 @@ static int stage_rows(const gdn_dims* dims, const gdn_rows* rows, int num_actual
                     "state_indices and num_accepted_tokens must be given together");
       if (!rows->state_indices)
         return fail(GDN_ERR_MISSING_OPTIONAL, "spec rows need state_indices");
+      if (dims->conv_layout == GDN_CONV_PER_TOKEN_SLOTS && rows->cache_indices)
+        return fail(GDN_ERR_DIMS, "cache_indices is not used by spec rows with per-token conv "
+                                  "slots");
     } else if (!rows->cache_indices) {
       return fail(GDN_ERR_MISSING_OPTIONAL, "non-spec rows need cache_indices");
     }
@@ -528,12 +543,15 @@ int gdn_check_metadata_host(const gdn_dims* dims, int32_t num_actual_tokens,
       if (n < 1 || n > T)
         return fail(GDN_ERR_METADATA, "spec row %d: num_accepted_tokens %d not in [1,%d]", bi,
                     n, T);
-      if (n + W - 2 > L)
+      const bool per_token = dims->conv_layout == GDN_CONV_PER_TOKEN_SLOTS;
+      if (!per_token && n + W - 2 > L)
         return fail(GDN_ERR_METADATA, "spec row %d: window n_acc-1=%d needs state_len >= %d",
                     bi, n - 1, n + W - 2);
       const int32_t* ssi = spec_state_indices + (size_t)bi * max_spec_len;
-      int cs = spec_cache_indices ? spec_cache_indices[bi] : ssi[0];
-      if (int e = claim_slot(cs, owner, "conv")) return e;
+      if (!per_token) {
+        int cs = spec_cache_indices ? spec_cache_indices[bi] : ssi[0];
+        if (int e = claim_slot(cs, owner, "conv")) return e;
+      }
       for (int t = 0; t < T; ++t)
         if (int e = claim_slot(ssi[t], owner, "spec state")) return e;
       for (int j = spec_query_start_loc[bi]; j < spec_query_start_loc[bi + 1]; ++j)

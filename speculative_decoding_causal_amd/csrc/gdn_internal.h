@@ -25,6 +25,7 @@ struct RowArgs {
   // shape
   int Hk, Hv, G, C, L, W, num_slots, act, l2norm;
   int qkv_layout;  // 0 grouped [q | k | v], 1 per k-head [q_i k_i v_i..]
+  int conv_per_token;  // spec rows: conv window saved per token (state_len == W-1)
   float eps, scale;
   int num_actual_tokens;
   // layer tensors

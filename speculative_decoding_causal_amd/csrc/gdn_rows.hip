@@ -39,6 +39,7 @@ struct RowPlan {
   int off;         // ring column of the first window sample
   int shift;       // roll: new column l <- old column shift + l
   int load_slot;   // initial state slot (<= 0: zero state)
+  const int* save; // per-token conv slots (spec rows, per-token layout), else null
 };
 
 __device__ __forceinline__ int slot_or_null(int s, int num_slots) {
@@ -52,7 +53,19 @@ __device__ RowPlan plan_row(const RowArgs& p, int row) {
   r.j0 = j0;
   r.T = min(j1 - j0, p.max_row_tokens);
   const int L = p.L, W = p.W;
-  if (p.kind == kSpec) {
+  r.save = nullptr;
+  if (p.kind == kSpec && p.conv_per_token) {
+    // one window per slot (L == W-1): read at the slot of token n_acc-1,
+    // saved after every token to that token's slot
+    const int* ssi = p.ssi + (size_t)row * p.row_stride;
+    const int T = r.T > 0 ? r.T : 1;
+    r.load_slot = slot_or_null(ssi[clampi(p.nacc[row], 1, T) - 1], p.num_slots);
+    r.conv_slot = r.load_slot;
+    r.read_hist = true;
+    r.off = 0;
+    r.shift = 0;
+    r.save = ssi;
+  } else if (p.kind == kSpec) {
     const int* ssi = p.ssi + (size_t)row * p.row_stride;
     int T = r.T > 0 ? r.T : 1;
     // n_acc outside [1, min(T, L-W+2)] is a precondition violation; clamp so
@@ -257,7 +270,16 @@ __device__ __forceinline__ void conv_chan(const float (&w)[kMaxWidth], float bia
       dst[j * dstride] = acc;
     }
   }
-  if (rp.conv_slot > 0) {
+  if (rp.save) {
+    // per-token slots: the window after token t is staged rows t+1 .. t+W-1
+    // (L == W-1 history rows, then the inputs), in token order
+    for (int t = 0; t < T; ++t) {
+      const int s = slot_or_null(rp.save[t], p.num_slots);
+      if (s <= 0) continue;
+      uint16_t* wslot = p.conv_pool + (size_t)s * L * p.C + c;
+      for (int l = 0; l < L; ++l) wslot[(size_t)l * p.C] = zb[(t + 1 + l) * NCH + pc];
+    }
+  } else if (rp.conv_slot > 0) {
     uint16_t* wring = p.conv_pool + (size_t)rp.conv_slot * L * p.C + c;
     for (int l = 0; l < L; ++l) {
       const int src = l < L - T ? rp.shift + l : T + l;

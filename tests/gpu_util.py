@@ -39,7 +39,8 @@ def cfg_of(case):
     import speculative_decoding_causal_amd as gdn
     d = case["dims"]
     return gdn.GdnConfig(d["Hk"], d["Hv"], d["dk"], d["dv"], d["W"], d["activation"],
-                         d["use_qk_l2norm"], d["eps"], d["scale"])
+                         d["use_qk_l2norm"], d["eps"], d["scale"],
+                         conv_layout=int(d.get("conv_layout", 0)))
 
 
 def bf(x, device=None):

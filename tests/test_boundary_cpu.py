@@ -36,7 +36,8 @@ def test_every_declared_symbol_is_exported():
 def dims(**kw):
     d = dict(num_k_heads=16, num_v_heads=32, head_k_dim=128, head_v_dim=128, conv_width=4,
              state_len=5, num_slots=512, activation=1, use_qk_l2norm=1, l2norm_eps=1e-6,
-             scale=128 ** -0.5, qkv_layout=gdn.GDN_QKV_GROUPED)
+             scale=128 ** -0.5, qkv_layout=gdn.GDN_QKV_GROUPED,
+             conv_layout=gdn.GDN_CONV_ROLLED_HISTORY)
     d.update(kw)
     return gdn.GdnDims(*[d[f] for f, _ in gdn.GdnDims._fields_])
 
@@ -95,7 +96,8 @@ def test_workspace_required_for_prefills():
                                  dict(conv_width=5), dict(num_v_heads=20),
                                  dict(state_len=2), dict(state_len=17), dict(num_slots=0),
                                  dict(activation=2), dict(qkv_layout=2),
-                                 dict(qkv_layout=-1)])
+                                 dict(qkv_layout=-1), dict(conv_layout=2),
+                                 dict(conv_layout=1, state_len=5)])
 def test_bad_dims_rejected(bad):
     rc = spec_call(dims(**bad))
     assert rc in (gdn.GDN_ERR_DIMS, gdn.GDN_ERR_UNSUPPORTED)
