@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
   gdn_spec_attention, gdn_attention, gdn_workspace_bytes, gdn_conv_only,
   gdn_delta_rule_only, gdn_check_metadata_host, gdn_status_string,
   gdn_last_error.
+Capture and replay of step calls: ``speculative_decoding_causal_amd.capture``.
 """
 from __future__ import annotations
 
