@@ -150,35 +150,33 @@ __device__ __forceinline__ void store_row4(float* p, v4f v) {
 #endif
 }
 
-// Load (or zero) the R state rows of one lane group: rows rho0 + s*RPW,
-// 16 columns each (four float4 at columns (n*LPR + jl)*4).
+// Load the R state rows of one lane group: rows rho0 + s*RPW, 16 columns
+// each (four float4 at columns (n*LPR + jl)*4).  No load sits behind a
+// branch (a branch join would wait for it): `base` is readable even for a
+// NULL slot (slot 0 stands in) and rows past NR re-read row NR-1;
+// zero_rows drops those values where the rows are first used, so the loads
+// stay in flight until then.
 template <int DK, int R, int LPR, int RPW>
-__device__ __forceinline__ void load_rows(v4f (&S)[R][4], const float* base, int rho0,
-                                          int jl, int NR, bool full) {
-  if (base == nullptr) {
+__device__ __forceinline__ void load_rows(v4f (&S)[R][4], const float* base, int rho0, int jl,
+                                          int NR) {
 #pragma unroll
-    for (int s = 0; s < R; ++s)
+  for (int s = 0; s < R; ++s) {
+    const int rho = rho0 + s * RPW;
+    const int rc = rho < NR ? rho : NR - 1;
 #pragma unroll
-      for (int n = 0; n < 4; ++n) S[s][n] = v4f{0.f, 0.f, 0.f, 0.f};
-    return;
+    for (int n = 0; n < 4; ++n)
+      S[s][n] = __builtin_nontemporal_load(
+          reinterpret_cast<const v4f*>(base + (size_t)rc * DK + (n * LPR + jl) * 4));
   }
-  if (full) {
+}
+
+template <int R, int RPW>
+__device__ __forceinline__ void zero_rows(v4f (&S)[R][4], bool valid, int rho0, int NR) {
 #pragma unroll
-    for (int s = 0; s < R; ++s)
+  for (int s = 0; s < R; ++s) {
+    const bool keep = valid && rho0 + s * RPW < NR;
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
-        S[s][n] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(
-            base + (size_t)(rho0 + s * RPW) * DK + (n * LPR + jl) * 4));
-  } else {
-#pragma unroll
-    for (int s = 0; s < R; ++s) {
-      const int rho = rho0 + s * RPW;
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-        S[s][n] = rho < NR ? __builtin_nontemporal_load(reinterpret_cast<const v4f*>(
-                                 base + (size_t)rho * DK + (n * LPR + jl) * 4))
-                           : v4f{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int n = 0; n < 4; ++n) S[s][n] = keep ? S[s][n] : v4f{0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -186,10 +184,11 @@ __device__ __forceinline__ void load_rows(v4f (&S)[R][4], const float* base, int
 // columns (LM >= L), the row's inputs (KT >= T), taps and bias.
 template <int LM, int KT>
 struct ChanIn {
-  uint16_t h[LM];
-  uint16_t x[KT];
-  float w[kMaxWidth];
-  float bias;
+  uint16_t h[LM];         // raw ring columns (dropped without history / past L)
+  uint16_t x[KT];         // raw inputs (dropped for tokens outside the batch)
+  uint16_t w[kMaxWidth];  // raw bf16 taps (dropped past W)
+  uint16_t bias;          // raw bf16 bias (dropped without one)
+  bool hist;
 };
 
 template <int KT>
@@ -218,30 +217,50 @@ template <int LM, int KT>
 __device__ __forceinline__ void load_chan(ChanIn<LM, KT>& in, const RowArgs& p,
                                           const RowPlan& rp, int c, int cin,
                                           const int (&rj)[KT]) {
+  // Every load goes to an address that exists and unwanted values are
+  // dropped afterwards: a load behind a branch is waited for where the
+  // branch joins, one memory round trip each.  Stand-ins: slot 0's ring for
+  // a row without history, the taps for an empty ring, a missing bias or an
+  // empty mixed_qkv (the taps hold C*W >= C values), row 0 for a token
+  // outside the batch, the last tap for taps past W.
   const bool hist = rp.read_hist && rp.conv_slot > 0;
-  const uint16_t* ring = p.conv_pool + (size_t)rp.conv_slot * p.L * p.C + c;
+  const uint16_t* ring = p.L > 0
+      ? p.conv_pool + (size_t)(hist ? rp.conv_slot : 0) * p.L * p.C + c
+      : p.conv_w + c;
+  const int lmax = p.L > 0 ? p.L - 1 : 0;
+  const uint16_t* xs = p.num_actual_tokens > 0 ? p.qkv : p.conv_w;
+  const uint16_t* bs = p.conv_b ? p.conv_b : p.conv_w;
 #pragma unroll
-  for (int l = 0; l < LM; ++l) in.h[l] = (hist && l < p.L) ? ring[(size_t)l * p.C] : (uint16_t)0;
+  for (int l = 0; l < LM; ++l) in.h[l] = ring[(size_t)(l < lmax ? l : lmax) * p.C];
 #pragma unroll
-  for (int j = 0; j < KT; ++j)
-    in.x[j] = rj[j] >= 0 ? p.qkv[(size_t)rj[j] * p.C + cin] : (uint16_t)0;
+  for (int j = 0; j < KT; ++j) in.x[j] = xs[(size_t)(rj[j] >= 0 ? rj[j] : 0) * p.C + cin];
 #pragma unroll
   for (int m = 0; m < kMaxWidth; ++m)
-    in.w[m] = m < p.W ? bf2f(p.conv_w[(size_t)c * p.W + m]) : 0.f;
-  in.bias = p.conv_b ? bf2f(p.conv_b[c]) : 0.f;
+    in.w[m] = p.conv_w[(size_t)c * p.W + (m < p.W ? m : p.W - 1)];
+  in.bias = bs[c];
+  in.hist = hist;
+}
+
+// Taps and bias as floats, zero past W and without a bias.
+template <int LM, int KT>
+__device__ __forceinline__ void taps_of(const ChanIn<LM, KT>& in, const RowArgs& p,
+                                        float (&w)[kMaxWidth], float& bias) {
+#pragma unroll
+  for (int m = 0; m < kMaxWidth; ++m) w[m] = m < p.W ? bf2f(in.w[m]) : 0.f;
+  bias = p.conv_b ? bf2f(in.bias) : 0.f;
 }
 
 // Stage one channel's pre-state and inputs in this thread's LDS column
 // zb[.][pc] (runtime window offsets are cheap there).
 template <int LM, int KT>
 __device__ __forceinline__ void stage_chan(const ChanIn<LM, KT>& in, int L, int T, int pc,
-                                           int NCH, uint16_t* zb) {
+                                           int NCH, uint16_t* zb, const int (&rj)[KT]) {
 #pragma unroll
   for (int l = 0; l < LM; ++l)
-    if (l < L) zb[l * NCH + pc] = in.h[l];
+    if (l < L) zb[l * NCH + pc] = in.hist ? in.h[l] : (uint16_t)0;
 #pragma unroll
   for (int j = 0; j < KT; ++j)
-    if (j < T) zb[(L + j) * NCH + pc] = in.x[j];
+    if (j < T) zb[(L + j) * NCH + pc] = rj[j] >= 0 ? in.x[j] : (uint16_t)0;
 }
 
 // Convolve one staged channel and roll its ring; every ring write follows
@@ -291,7 +310,7 @@ __device__ __forceinline__ void conv_chan(const float (&w)[kMaxWidth], float bia
 // NT threads per workgroup, R state rows per lane; WPE waves per SIMD is the
 // occupancy the register budget is fitted to.  LM / KT bound state_len and
 // the tokens per row for the register gathers of the conv phase.
-template <int DK, int DV, int R, int NT, int WPE, int LM, int KT, int RB>
+template <int DK, int DV, int R, int NT, int WPE, int LM, int KT, int RB, bool FUSED>
 __global__ void __launch_bounds__(NT, WPE)
 gdn_rows_kernel(RowArgs p) {
   static_assert(R % RB == 0, "row batch");
@@ -352,34 +371,62 @@ gdn_rows_kernel(RowArgs p) {
 
   // The conv and gate inputs are gathered in one batch of loads (vector loads
   // complete in order, so nothing slow may be issued ahead of them).
-  const int stage = p.stage;
+  // The fused step knows its stage at compile time (no branch around its
+  // loads); the stage entry points read it from the arguments.
+  const int stage = FUSED ? kFused : p.stage;
   const bool conv_stage = stage != kDeltaOnly;
   const bool have_chan = conv_stage && tid < NCH;
   const int c0 = channel_of(tid, ih, Hk, DK, NR);
   float w0[kMaxWidth], bias0 = 0.f;
+  // State rows of this lane (first pass), their slot and head block.
+  const int jl = lane % LPR, gl = lane / LPR;
+  const size_t slot_stride = (size_t)p.Hv * DV * DK;
+  const size_t head_off = (size_t)ih * NR * DK;
+  const bool load_valid = rp.load_slot > 0;
+  const float* load_base = p.ssm_pool + (size_t)(load_valid ? rp.load_slot : 0) * slot_stride +
+                           head_off;
+  constexpr int kRowsPerWavePass = RPW * R;
+  constexpr int kRowsPerPass = (NT / 64) * kRowsPerWavePass;
+  constexpr bool kEarlyRows = LM + KT <= 10;
+  v4f S[R][4];
   {
-    ChanIn<LM, KT> in0;
-    if (have_chan) {
-      load_chan<LM, KT>(in0, p, rp, c0, input_column(p, tid, c0, ih, DK, NR), rj);
-#pragma unroll
-      for (int m = 0; m < kMaxWidth; ++m) w0[m] = in0.w[m];
-      bias0 = in0.bias;
-    }
+    // Gate inputs join the same batch (no branch around the loads): rows
+    // outside the batch read row 0; with no token rows, or in the conv-only
+    // stage (no gates), the loads go to A_log or the taps and are dropped.
     const bool have_gate0 = stage != kConvOnly && tid < T * G;
-    uint16_t gate_a = 0, gate_b = 0;
-    if (have_gate0) {
-      const int r = pick<KT>(rj, tid / G);
-      const int h = ih * G + tid % G;
-      if (r >= 0) {
-        gate_a = p.a[(size_t)r * p.Hv + h];
-        gate_b = p.b[(size_t)r * p.Hv + h];
-      }
+    const bool gate_rows = stage != kConvOnly && p.num_actual_tokens > 0;
+    const uint16_t* gsrc_a = gate_rows ? p.a
+        : (stage != kConvOnly ? reinterpret_cast<const uint16_t*>(p.A_log) : p.conv_w);
+    const uint16_t* gsrc_b = gate_rows ? p.b : gsrc_a;
+    const int gr = have_gate0 ? pick<KT>(rj, tid / G) : -1;
+    const int gh = ih * G + tid % G;
+    const size_t gi = gate_rows ? (size_t)(gr >= 0 ? gr : 0) * p.Hv + gh : (size_t)gh;
+    const uint16_t raw_a = gsrc_a[gi], raw_b = gsrc_b[gi];
+    // Every thread loads a channel (threads past the last one repeat it) so
+    // that no load waits behind a per-thread branch.
+    ChanIn<LM, KT> in0;
+    if (conv_stage) {
+      const int pcl = tid < NCH ? tid : NCH - 1;
+      const int cl = tid < NCH ? c0 : channel_of(pcl, ih, Hk, DK, NR);
+      load_chan<LM, KT>(in0, p, rp, cl, input_column(p, pcl, cl, ih, DK, NR), rj);
     }
-    if (have_chan) stage_chan<LM, KT>(in0, L, T, tid, NCH, zb);
-    if (have_gate0) {
-      ga[tid] = bf2f(gate_a);  // raw gate inputs; turned into alpha/beta below
-      gb[tid] = bf2f(gate_b);
+    // The first pass of state rows follows the conv and gate inputs in the
+    // same stream of loads: it lands while the conv runs (vector loads
+    // complete in order, so the conv waits only for its own inputs).
+    // (Only with the smallest register gathers: the others leave no room.)
+    if constexpr (kEarlyRows) {
+      if (stage != kConvOnly)
+        load_rows<DK, R, LPR, RPW>(S, load_base, wv * kRowsPerWavePass + gl, jl, NR);
+      // keep the state loads ahead of the staging, which waits for the conv inputs
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (have_chan) stage_chan<LM, KT>(in0, L, T, tid, NCH, zb, rj);
+    if (have_gate0) {
+      // raw gate inputs; turned into alpha/beta below
+      ga[tid] = gr >= 0 ? bf2f(raw_a) : 0.f;
+      gb[tid] = gr >= 0 ? bf2f(raw_b) : 0.f;
+    }
+    if (have_chan) taps_of<LM, KT>(in0, p, w0, bias0);
   }
   // ---- phase 1: conv (or load of a precomputed conv output) -------------
   for (int pc = tid; pc < NCH; pc += NT) {
@@ -401,26 +448,16 @@ gdn_rows_kernel(RowArgs p) {
     } else {
       ChanIn<LM, KT> in;
       load_chan<LM, KT>(in, p, rp, c, input_column(p, pc, c, ih, DK, NR), rj);
-      stage_chan<LM, KT>(in, L, T, pc, NCH, zb);
-      conv_chan<KT>(in.w, in.bias, p, rp, c, pc, NCH, T, zb, dst, dstride, rj);
+      stage_chan<LM, KT>(in, L, T, pc, NCH, zb, rj);
+      float w[kMaxWidth], bias;
+      taps_of<LM, KT>(in, p, w, bias);
+      conv_chan<KT>(w, bias, p, rp, c, pc, NCH, T, zb, dst, dstride, rj);
     }
   }
   if (stage == kConvOnly) return;
+  if constexpr (!kEarlyRows)
+    load_rows<DK, R, LPR, RPW>(S, load_base, wv * kRowsPerWavePass + gl, jl, NR);
 
-  // The state rows (the bulk of the reads) are issued now and land while the
-  // gates and norms run.
-  const int jl = lane % LPR, gl = lane / LPR;
-  const size_t slot_stride = (size_t)p.Hv * DV * DK;
-  const size_t head_off = (size_t)ih * NR * DK;
-  const float* load_base =
-      rp.load_slot > 0 ? p.ssm_pool + (size_t)rp.load_slot * slot_stride + head_off : nullptr;
-  constexpr int kRowsPerWavePass = RPW * R;
-  constexpr int kRowsPerPass = (NT / 64) * kRowsPerWavePass;
-  v4f S[R][4];
-  {
-    const int r0 = wv * kRowsPerWavePass;
-    load_rows<DK, R, LPR, RPW>(S, load_base, r0 + gl, jl, NR, r0 + kRowsPerWavePass <= NR);
-  }
 
 
   // ---- phase 2: gates and q/k norms ---------------------------------------
@@ -466,7 +503,8 @@ gdn_rows_kernel(RowArgs p) {
   for (int r0 = wv * kRowsPerWavePass; r0 < NR; r0 += kRowsPerPass) {
     const bool full = r0 + kRowsPerWavePass <= NR;
     const int rho0 = r0 + gl;
-    if (r0 != wv * kRowsPerWavePass) load_rows<DK, R, LPR, RPW>(S, load_base, rho0, jl, NR, full);
+    if (r0 != wv * kRowsPerWavePass) load_rows<DK, R, LPR, RPW>(S, load_base, rho0, jl, NR);
+    zero_rows<R, RPW>(S, load_valid, rho0, NR);
 #pragma unroll
     for (int sb = 0; sb < R; sb += RB) {
       for (int j = 0; j < T; ++j) {
@@ -567,7 +605,8 @@ template <int DK, int DV, int R, int NT, int WPE, int LM, int KT>
 hipError_t launch_typed(const RowArgs& a, hipStream_t s) {
   const Lds lay = lds_layout(DK, DV, a.G, a.L, a.max_row_tokens);
   constexpr int RB = DK == 128 ? GDN_ROWS_RB128 : R;
-  auto kern = gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT, RB>;
+  auto kern = a.stage == kFused ? gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT, RB, true>
+                                : gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT, RB, false>;
   if (lay.total > 64 * 1024) {
     hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lay.total);
     if (e != hipSuccess) return e;
@@ -580,6 +619,7 @@ hipError_t launch_typed(const RowArgs& a, hipStream_t s) {
 // Short rows on a short ring take the small register gathers.
 template <int DK, int DV, int R, int NT, int WPE>
 hipError_t launch_sized(const RowArgs& a, hipStream_t s) {
+  if (a.L <= 6 && a.max_row_tokens <= 4) return launch_typed<DK, DV, R, NT, WPE, 6, 4>(a, s);
   if (a.L <= 8 && a.max_row_tokens <= 4) return launch_typed<DK, DV, R, NT, WPE, 8, 4>(a, s);
   return launch_typed<DK, DV, R, NT, WPE, kMaxStateLen, kMaxRowTokens>(a, s);
 }
