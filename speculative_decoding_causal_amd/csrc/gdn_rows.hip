@@ -378,6 +378,7 @@ gdn_rows_kernel(RowArgs p) {
   const bool have_chan = conv_stage && tid < NCH;
   const int c0 = channel_of(tid, ih, Hk, DK, NR);
   float w0[kMaxWidth], bias0 = 0.f;
+  float a_log0, dt_bias0;
   // State rows of this lane (first pass), their slot and head block.
   const int jl = lane % LPR, gl = lane / LPR;
   const size_t slot_stride = (size_t)p.Hv * DV * DK;
@@ -402,6 +403,12 @@ gdn_rows_kernel(RowArgs p) {
     const int gh = ih * G + tid % G;
     const size_t gi = gate_rows ? (size_t)(gr >= 0 ? gr : 0) * p.Hv + gh : (size_t)gh;
     const uint16_t raw_a = gsrc_a[gi], raw_b = gsrc_b[gi];
+    // the head's A_log and dt_bias too (the taps stand in for the conv-only
+    // stage, which has no gates), so phase 2 issues no load behind the state
+    const float* gsrc_l = stage != kConvOnly ? p.A_log : reinterpret_cast<const float*>(p.conv_w);
+    const float* gsrc_d = stage != kConvOnly ? p.dt_bias : gsrc_l;
+    a_log0 = gsrc_l[gh];
+    dt_bias0 = gsrc_d[gh];
     // Every thread loads a channel (threads past the last one repeat it) so
     // that no load waits behind a per-thread branch.
     ChanIn<LM, KT> in0;
@@ -461,10 +468,7 @@ gdn_rows_kernel(RowArgs p) {
 
 
   // ---- phase 2: gates and q/k norms ---------------------------------------
-  if (tid < T * G) {
-    const int h = ih * G + tid % G;
-    gate_pair(ga[tid], gb[tid], p.A_log[h], p.dt_bias[h], &ga[tid], &gb[tid]);
-  }
+  if (tid < T * G) gate_pair(ga[tid], gb[tid], a_log0, dt_bias0, &ga[tid], &gb[tid]);
   for (int idx = tid + NT; idx < T * G; idx += NT) {
     const int j = idx / G, g = idx - j * G, h = ih * G + g;
     const int r = pick<KT>(rj, j);
