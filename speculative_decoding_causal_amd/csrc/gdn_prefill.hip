@@ -4,7 +4,7 @@
 //   0. prefill_map: one workgroup lists the 64-token units of the rows, row
 //      after row, so the kernels below launch one workgroup per unit that
 //      exists rather than per (row, longest possible row) pair.
-//   1. conv_prefill: one thread per (channel, 64-token segment of a row)
+//   1. conv_prefill: one thread per (4 channels, 32 tokens of a row)
 //      slides the width-W window along the row and writes the fp32 conv
 //      output to the workspace at the token's non-spec stream index.  The
 //      thread of segment 0 is the only one that reads the ring history (the
@@ -25,8 +25,7 @@
 namespace gdn {
 namespace {
 
-constexpr int kSeg = 64;    // tokens per conv thread
-constexpr int kBatch = 16;  // tokens gathered per round of loads
+constexpr int kSeg = 64;    // tokens per unit of the unit map
 constexpr int kChunk = 32;  // tokens staged per LDS refill in the recurrence
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -142,75 +141,175 @@ prefill_map_kernel(PrefillArgs p, int* __restrict__ map, int cap) {
   }
 }
 
+// Four consecutive channels per thread: one 8-byte load per token and one
+// 16-byte store per output (channel blocks are multiples of 16 in both
+// layouts of mixed_qkv, so the four are contiguous in either).
+constexpr int kCh = 4;
+constexpr int kTokThread = 32;  // tokens per thread: half a 64-token unit
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf_lo(unsigned int u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(unsigned int u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ void unpack4(u32x2 v, bool live, float (&x)[kCh]) {
+  x[0] = live ? bf_lo(v.x) : 0.f;
+  x[1] = live ? bf_hi(v.x) : 0.f;
+  x[2] = live ? bf_lo(v.y) : 0.f;
+  x[3] = live ? bf_hi(v.y) : 0.f;
+}
+
+// grid (units, C / (kCh * kThreads), 2): thread (x, y, z) convolves channels
+// 4 * (y * kThreads + tid) .. +3 over tokens [32 z, 32 z + 32) of its unit.
+// Every load goes to an address that exists and unwanted values are dropped
+// afterwards (a load behind a branch is waited for where the branch joins):
+// slot 0's ring stands in without history, the taps for an empty ring or an
+// empty mixed_qkv (they hold C*W >= C values), row 0 for a token outside the
+// batch, the segment's last token for positions past it.
 __global__ void __launch_bounds__(kThreads)
 conv_prefill_kernel(PrefillArgs p, float* __restrict__ y) {
   const int C = p.C, L = p.L, W = p.W;
-  const int c = blockIdx.y * kThreads + threadIdx.x;
+  const int c = (blockIdx.y * kThreads + threadIdx.x) * kCh;
   if (c >= C) return;
   const int row = p.unit_map[2 * blockIdx.x], seg = p.unit_map[2 * blockIdx.x + 1];
   if (row < 0) return;
   const PrefillRow pr = prefill_row(p, row);
-  const int base = seg * kSeg;
+  const int base = seg * kSeg + blockIdx.z * kTokThread;
   if (base >= pr.T) return;
-  const int end = min(pr.T, base + kSeg);
-  const uint16_t* ring = p.conv_pool + (size_t)pr.slot * L * C + c;
+  const int end = min(pr.T, base + kTokThread);
   const int cin = p.qkv_layout ? per_k_head_column(c, p.Hk, p.G, p.dk, p.dv) : c;
-
-  // Input at row position t; t < 0 reads ring column L + t (history).
-  auto xin = [&](int t) -> uint16_t {
-    if (t >= 0) {
-      int r = global_row(p, pr.j0 + t);
-      return r >= 0 ? p.qkv[(size_t)r * C + cin] : (uint16_t)0;
-    }
-    return pr.init ? ring[(size_t)(L + t) * C] : (uint16_t)0;
+  const uint16_t* ring = L > 0 ? p.conv_pool + (size_t)(pr.init ? pr.slot : 0) * L * C + c
+                               : p.conv_w + c;
+  const uint16_t* xs = p.num_actual_tokens > 0 ? p.qkv : p.conv_w;
+  auto in_ptr = [&](int r) -> const u32x2* {
+    return reinterpret_cast<const u32x2*>(xs + (size_t)(r >= 0 ? r : 0) * (xs == p.qkv ? C : 0) +
+                                          (xs == p.qkv ? cin : c));
+  };
+  auto ring_col = [&](int col) -> const u32x2* {
+    const int cc = L > 0 ? (col < 0 ? 0 : (col > L - 1 ? L - 1 : col)) : 0;
+    return reinterpret_cast<const u32x2*>(ring + (size_t)cc * C);
   };
 
-  float w[kMaxWidth];
+  // Global rows of this thread's positions and of the window before them
+  // (uniform scalar loads), then every vector load of the segment in one
+  // round: inputs, window, taps, bias.
+  int rr[kTokThread], hr[kMaxWidth - 1];
 #pragma unroll
-  for (int m = 0; m < kMaxWidth; ++m) w[m] = m < W ? bf2f(p.conv_w[(size_t)c * W + m]) : 0.f;
-  const float wlast = bf2f(p.conv_w[(size_t)c * W + W - 1]);
-  const float bias = p.conv_b ? bf2f(p.conv_b[c]) : 0.f;
-  float win[kMaxWidth];  // win[m] = input at t - (W-1) + m, m < W-1
+  for (int i = 0; i < kTokThread; ++i)
+    rr[i] = global_row(p, pr.j0 + (base + i < end ? base + i : end - 1));
 #pragma unroll
-  for (int m = 0; m < kMaxWidth - 1; ++m)
-    win[m] = m < W - 1 ? bf2f(xin(base - (W - 1) + m)) : 0.f;
-  // Inputs are gathered kBatch tokens at a time (one round of loads), then
-  // the window slides over them.
-  for (int t0 = base; t0 < end; t0 += kBatch) {
-    uint16_t xb[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) xb[i] = (t0 + i < end) ? xin(t0 + i) : (uint16_t)0;
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      if (t0 + i < end) {
-        const float xt = bf2f(xb[i]);
-        float acc = bias;
-#pragma unroll
-        for (int m = 0; m < kMaxWidth - 1; ++m)
-          if (m < W - 1) acc = fmaf(w[m], win[m], acc);
-        acc = fmaf(wlast, xt, acc);
-        if (p.act) acc = silu(acc);
-        y[(size_t)(pr.j0 + t0 + i) * C + c] = acc;
-#pragma unroll
-        for (int m = 0; m < kMaxWidth - 2; ++m)
-          if (m < W - 2) win[m] = win[m + 1];
-        if (W >= 2) {
-#pragma unroll
-          for (int m = 0; m < kMaxWidth - 1; ++m)
-            if (m == W - 2) win[m] = xt;
-        }
-      }
-    }
+  for (int m = 0; m < kMaxWidth - 1; ++m) {
+    const int t = base - (W - 1) + m;
+    hr[m] = global_row(p, pr.j0 + (t > 0 ? t : 0));
   }
-  // Roll: new column l <- (history ++ inputs)[T + l].  Column T + l is read
-  // before column l is written, and only this thread touches the channel.
-  if (seg == 0 && pr.slot > 0) {
-    uint16_t* wr = p.conv_pool + (size_t)pr.slot * L * C + c;
-    for (int l = 0; l < L; ++l) {
-      int src = pr.T + l;
-      uint16_t v = src < L ? (pr.init ? wr[(size_t)src * C] : (uint16_t)0) : xin(src - L);
-      wr[(size_t)l * C] = v;
+  u32x2 xv[kTokThread], hv[kMaxWidth - 1], iv[kMaxWidth - 1];
+  uint16_t wr[kMaxWidth][kCh];
+#pragma unroll
+  for (int i = 0; i < kTokThread; ++i) xv[i] = *in_ptr(rr[i]);
+#pragma unroll
+  for (int m = 0; m < kMaxWidth - 1; ++m) {
+    hv[m] = *ring_col(L + base - (W - 1) + m);
+    iv[m] = *in_ptr(hr[m]);
+  }
+#pragma unroll
+  for (int m = 0; m < kMaxWidth; ++m)
+#pragma unroll
+    for (int e = 0; e < kCh; ++e) wr[m][e] = p.conv_w[(size_t)(c + e) * W + (m < W ? m : W - 1)];
+  const u32x2 br = *reinterpret_cast<const u32x2*>((p.conv_b ? p.conv_b : p.conv_w) + c);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // taps and bias
+  float w[kMaxWidth][kCh], wl[kCh], bias[kCh];
+#pragma unroll
+  for (int m = 0; m < kMaxWidth; ++m)
+#pragma unroll
+    for (int e = 0; e < kCh; ++e) w[m][e] = m < W ? bf2f(wr[m][e]) : 0.f;
+#pragma unroll
+  for (int e = 0; e < kCh; ++e) {
+    wl[e] = 0.f;
+#pragma unroll
+    for (int m = 0; m < kMaxWidth; ++m)
+      if (m == W - 1) wl[e] = w[m][e];
+  }
+  unpack4(br, p.conv_b != nullptr, bias);
+  // Window before the first token: positions base-(W-1) .. base-1, which are
+  // ring columns L + t (zeros without history) for t < 0, inputs otherwise.
+  float win[kMaxWidth - 1][kCh];
+#pragma unroll
+  for (int m = 0; m < kMaxWidth - 1; ++m) {
+    const int t = base - (W - 1) + m;
+    const bool hist = t < 0;
+    const bool live = m < W - 1 && (hist ? (pr.init && L + t >= 0) : hr[m] >= 0);
+    unpack4(hist ? hv[m] : iv[m], live, win[m]);
+  }
+  // the window slides over the inputs
+#pragma unroll
+  for (int i = 0; i < kTokThread; ++i) {
+    const int t = base + i;
+    if (t >= end) break;
+    float xt[kCh];
+    unpack4(xv[i], rr[i] >= 0, xt);
+    float o[kCh];
+#pragma unroll
+    for (int e = 0; e < kCh; ++e) {
+      float acc = bias[e];
+#pragma unroll
+      for (int m = 0; m < kMaxWidth - 1; ++m)
+        if (m < W - 1) acc = fmaf(w[m][e], win[m][e], acc);
+      acc = fmaf(wl[e], xt[e], acc);
+      o[e] = p.act ? silu(acc) : acc;
     }
+    *reinterpret_cast<float4*>(y + (size_t)(pr.j0 + t) * C + c) =
+        make_float4(o[0], o[1], o[2], o[3]);
+    // slide the window: drop the oldest sample, append x_t
+#pragma unroll
+    for (int m = 0; m < kMaxWidth - 2; ++m)
+#pragma unroll
+      for (int e = 0; e < kCh; ++e)
+        if (m < W - 2) win[m][e] = win[m + 1][e];
+#pragma unroll
+    for (int m = 0; m < kMaxWidth - 1; ++m)
+#pragma unroll
+      for (int e = 0; e < kCh; ++e)
+        if (m == W - 2) win[m][e] = xt[e];
+  }
+  // Roll: new column l <- (history ++ inputs)[T + l].  All sources are
+  // loaded (in column order) before the first store: vector loads complete
+  // in order, so the store of column l, which waits for its own source,
+  // also follows the read of column l.  Only this thread writes these
+  // channels, and only the thread of the row's first tokens reads history.
+  if (seg == 0 && blockIdx.z == 0 && pr.slot > 0 && L > 0) {
+    uint16_t* wring = p.conv_pool + (size_t)pr.slot * L * C + c;
+    int ir[kMaxStateLen];
+    // stream indices of the inputs the new columns take (clamped into the
+    // row), their global rows in one batch of loads, then the range checks
+#pragma unroll
+    for (int l = 0; l < kMaxStateLen; ++l) {
+      const int tin = pr.T + l - L;        // input position when >= 0
+      ir[l] = pr.j0 + (tin > 0 ? (tin < pr.T ? tin : pr.T - 1) : 0);
+    }
+    if (p.tix) {
+#pragma unroll
+      for (int l = 0; l < kMaxStateLen; ++l) ir[l] = p.tix[ir[l]];
+    }
+#pragma unroll
+    for (int l = 0; l < kMaxStateLen; ++l)
+      ir[l] = (ir[l] >= 0 && ir[l] < p.num_actual_tokens) ? ir[l] : -1;
+    u32x2 hv[kMaxStateLen], iv[kMaxStateLen], nv[kMaxStateLen];
+#pragma unroll
+    for (int l = 0; l < kMaxStateLen; ++l) {
+      hv[l] = *ring_col(pr.T + l);         // position pr.T + l of (history ++ inputs)
+      iv[l] = *in_ptr(ir[l]);
+    }
+#pragma unroll
+    for (int l = 0; l < kMaxStateLen; ++l) {
+      const bool hist = pr.T + l < L;
+      const bool live = hist ? pr.init : ir[l] >= 0;
+      nv[l] = live ? (hist ? hv[l] : iv[l]) : u32x2{0u, 0u};
+    }
+#pragma unroll
+    for (int l = 0; l < kMaxStateLen; ++l)
+      if (l < L) *reinterpret_cast<u32x2*>(wring + (size_t)l * C) = nv[l];
   }
 }
 
@@ -374,7 +473,7 @@ hipError_t launch_prefill_typed(const PrefillArgs& args, hipStream_t s) {
   hipLaunchKernelGGL(prefill_map_kernel, dim3(1), dim3(kMapThreads), 0, s, a, map, w.units);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 g1(a.units, (a.C + kThreads - 1) / kThreads);
+  dim3 g1(a.units, (a.C / kCh + kThreads - 1) / kThreads, kSeg / kTokThread);
   hipLaunchKernelGGL(conv_prefill_kernel, g1, dim3(kThreads), 0, s, a, y);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
