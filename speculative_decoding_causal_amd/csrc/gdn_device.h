@@ -63,7 +63,12 @@ __device__ __forceinline__ float gate_log(float a, float A_log, float dt_bias) {
   return -expf(A_log) * sp;
 }
 
-__device__ __forceinline__ float silu(float x) { return x / (1.f + expf(-x)); }
+// SiLU x * sigma(x) with the hardware exp2 and reciprocal (about 1 ulp each):
+// x -> -inf gives exp2 = inf, rcp = 0, -0; x -> +inf gives x; NaN stays NaN.
+__device__ __forceinline__ float silu(float x) {
+  const float e = __builtin_amdgcn_exp2f(-x * 1.4426950408889634f);
+  return x * __builtin_amdgcn_rcpf(1.f + e);
+}
 
 // Workgroup barrier that orders LDS only: outstanding global loads (prefetches
 // into registers) stay in flight across it, unlike __syncthreads(), whose

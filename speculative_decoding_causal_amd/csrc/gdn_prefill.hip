@@ -4,16 +4,16 @@
 //   0. prefill_map: one workgroup lists the 64-token units of the rows, row
 //      after row, so the kernels below launch one workgroup per unit that
 //      exists rather than per (row, longest possible row) pair.
-//   1. conv_prefill: one thread per (4 channels, 32 tokens of a row)
+//   1. conv_prefill: one thread per (4 channels, 16 tokens of a row)
 //      slides the width-W window along the row and writes the fp32 conv
-//      output to the workspace at the token's non-spec stream index.  The
-//      thread of segment 0 is the only one that reads the ring history (the
-//      window of the row's first tokens) and it alone rolls the ring by T
-//      afterwards, so reads of the pre-state precede the writes.
-//   2. prep_prefill: per token, the q/k L2 norms (wave reductions, q scaled)
-//      are applied in place in the workspace, k.q is kept, and the gates of
-//      every v-head are evaluated at the token's global row (log-decay and
-//      beta).
+//      output to the workspace at the token's non-spec stream index, q and
+//      k L2-normalised (q scaled) by a reduction over the lanes of a head;
+//      the workgroups of a unit also evaluate the gates of every v-head at
+//      the token's global row (log-decay and beta).  The thread of the
+//      row's first tokens is the only one that reads the ring history and
+//      it alone rolls the ring by T afterwards, so reads of the pre-state
+//      precede the writes.
+//   2. for head dims below 64, kq_prefill: k.q per (token, k-head).
 //   3. the chunked WY/UT recurrence on MFMA (gdn_chunk.hip) for head dims 64
 //      and 128; for smaller heads, delta_prefill: one workgroup per (row,
 //      v-head, block of state rows) carries its rows in VGPRs through the
@@ -145,7 +145,7 @@ prefill_map_kernel(PrefillArgs p, int* __restrict__ map, int cap) {
 // 16-byte store per output (channel blocks are multiples of 16 in both
 // layouts of mixed_qkv, so the four are contiguous in either).
 constexpr int kCh = 4;
-constexpr int kTokThread = 32;  // tokens per thread: half a 64-token unit
+constexpr int kTokThread = 16;  // tokens per thread: a quarter of a 64-token unit
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -159,15 +159,25 @@ __device__ __forceinline__ void unpack4(u32x2 v, bool live, float (&x)[kCh]) {
   x[3] = live ? bf_hi(v.y) : 0.f;
 }
 
-// grid (units, C / (kCh * kThreads), 2): thread (x, y, z) convolves channels
-// 4 * (y * kThreads + tid) .. +3 over tokens [32 z, 32 z + 32) of its unit.
+// grid (units, C / (kCh * kThreads), 4): thread (x, y, z) convolves channels
+// 4 * (y * kThreads + tid) .. +3 over tokens [16 z, 16 z + 16) of its unit.
+// q and k leave L2-normalised (q also scaled): the DK/4 lanes holding one
+// head's channels reduce the sum of squares per token (heads start at lane
+// multiples of DK/4, and q/k/v boundaries fall on head boundaries).  The
+// workgroups of a unit also evaluate the gates of its tokens, log-decay ga
+// and write strength gb per (token, v-head), the pairs spread over the
+// channel blocks.
 // Every load goes to an address that exists and unwanted values are dropped
 // afterwards (a load behind a branch is waited for where the branch joins):
 // slot 0's ring stands in without history, the taps for an empty ring or an
 // empty mixed_qkv (they hold C*W >= C values), row 0 for a token outside the
 // batch, the segment's last token for positions past it.
+template <int DK>
 __global__ void __launch_bounds__(kThreads)
-conv_prefill_kernel(PrefillArgs p, float* __restrict__ y) {
+conv_prefill_kernel(PrefillArgs p, float* __restrict__ y, float* __restrict__ ga,
+                    float* __restrict__ gb) {
+  constexpr int LPH = DK / kCh;  // lanes per head
+  static_assert(LPH >= 4 && LPH <= 32, "head dim");
   const int C = p.C, L = p.L, W = p.W;
   const int c = (blockIdx.y * kThreads + threadIdx.x) * kCh;
   if (c >= C) return;
@@ -190,17 +200,30 @@ conv_prefill_kernel(PrefillArgs p, float* __restrict__ y) {
     return reinterpret_cast<const u32x2*>(ring + (size_t)cc * C);
   };
 
-  // Global rows of this thread's positions and of the window before them
-  // (uniform scalar loads), then every vector load of the segment in one
-  // round: inputs, window, taps, bias.
-  int rr[kTokThread], hr[kMaxWidth - 1];
+  // Global rows of the positions this thread reads, one per lane in one
+  // coalesced load, then made uniform lane by lane: lanes 0..31 the
+  // segment's tokens, 32..34 the window before them, 35..50 the inputs the
+  // rolled ring takes (row positions T-L .. T-1); every position is clamped
+  // into the row.  Then every vector load of the segment in one round:
+  // inputs, window, taps, bias, and (for the rolling thread) the roll's
+  // sources.
+  const bool roller = seg == 0 && blockIdx.z == 0 && pr.slot > 0 && L > 0;
+  int rr[kTokThread], hr[kMaxWidth - 1], ir[kMaxStateLen];
+  {
+    const int lane = threadIdx.x & 63;
+    int t;
+    if (lane < kTokThread) t = base + lane;
+    else if (lane < kTokThread + kMaxWidth - 1) t = base - (W - 1) + (lane - kTokThread);
+    else t = pr.T - L + (lane - kTokThread - (kMaxWidth - 1));
+    t = t < 0 ? 0 : (t > end - 1 && lane < kTokThread ? end - 1 : (t > pr.T - 1 ? pr.T - 1 : t));
+    const int rl = global_row(p, pr.j0 + t);
 #pragma unroll
-  for (int i = 0; i < kTokThread; ++i)
-    rr[i] = global_row(p, pr.j0 + (base + i < end ? base + i : end - 1));
+    for (int i = 0; i < kTokThread; ++i) rr[i] = __builtin_amdgcn_readlane(rl, i);
 #pragma unroll
-  for (int m = 0; m < kMaxWidth - 1; ++m) {
-    const int t = base - (W - 1) + m;
-    hr[m] = global_row(p, pr.j0 + (t > 0 ? t : 0));
+    for (int m = 0; m < kMaxWidth - 1; ++m) hr[m] = __builtin_amdgcn_readlane(rl, kTokThread + m);
+#pragma unroll
+    for (int l = 0; l < kMaxStateLen; ++l)
+      ir[l] = __builtin_amdgcn_readlane(rl, kTokThread + kMaxWidth - 1 + l);
   }
   u32x2 xv[kTokThread], hv[kMaxWidth - 1], iv[kMaxWidth - 1];
   uint16_t wr[kMaxWidth][kCh];
@@ -216,7 +239,54 @@ conv_prefill_kernel(PrefillArgs p, float* __restrict__ y) {
 #pragma unroll
     for (int e = 0; e < kCh; ++e) wr[m][e] = p.conv_w[(size_t)(c + e) * W + (m < W ? m : W - 1)];
   const u32x2 br = *reinterpret_cast<const u32x2*>((p.conv_b ? p.conv_b : p.conv_w) + c);
+  // Gate pairs (token of the segment, v-head): spread over the channel
+  // blocks, kGP per thread; their stream rows, A_log and dt_bias join this
+  // round, a and b follow once the rows are known.
+  constexpr int kGP = 4;
+  const int Hv = p.Hv;
+  const int live_thr = (C / kCh - (int)blockIdx.y * kThreads) < kThreads
+                           ? (C / kCh - (int)blockIdx.y * kThreads) : kThreads;
+  const int npairs = kTokThread * Hv;
+  const int per_blk = (npairs + gridDim.y - 1) / gridDim.y;
+  int gidx[kGP], graw[kGP];
+  float gl[kGP], gd[kGP];
+#pragma unroll
+  for (int k = 0; k < kGP; ++k) {
+    const int q = (int)threadIdx.x + k * live_thr;
+    const int idx = (int)blockIdx.y * per_blk + q;
+    gidx[k] = (q < per_blk && idx < npairs) ? idx : -1;
+    const int ic = gidx[k] >= 0 ? gidx[k] : 0;
+    const int i = ic / Hv, h = ic - i * Hv;
+    const int t = base + i < end ? base + i : end - 1;
+    graw[k] = p.tix ? 0 : pr.j0 + t;
+    gl[k] = p.A_log[h];
+    gd[k] = p.dt_bias[h];
+  }
+  if (p.tix) {
+#pragma unroll
+    for (int k = 0; k < kGP; ++k) {
+      const int ic = gidx[k] >= 0 ? gidx[k] : 0;
+      const int i = ic / Hv;
+      const int t = base + i < end ? base + i : end - 1;
+      graw[k] = p.tix[pr.j0 + t];
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);
+  uint16_t graw_a[kGP], graw_b[kGP];
+  {
+    const bool rows_ok = p.num_actual_tokens > 0;
+    const uint16_t* sa = rows_ok ? p.a : reinterpret_cast<const uint16_t*>(p.A_log);
+    const uint16_t* sb = rows_ok ? p.b : sa;
+#pragma unroll
+    for (int k = 0; k < kGP; ++k) {
+      const int ic = gidx[k] >= 0 ? gidx[k] : 0;
+      const int h = ic - (ic / Hv) * Hv;
+      graw[k] = (graw[k] >= 0 && graw[k] < p.num_actual_tokens) ? graw[k] : -1;
+      const size_t gi = rows_ok ? (size_t)(graw[k] >= 0 ? graw[k] : 0) * Hv + h : (size_t)h;
+      graw_a[k] = sa[gi];
+      graw_b[k] = sb[gi];
+    }
+  }
 
   // taps and bias
   float w[kMaxWidth][kCh], wl[kCh], bias[kCh];
@@ -259,6 +329,26 @@ conv_prefill_kernel(PrefillArgs p, float* __restrict__ y) {
       acc = fmaf(wl[e], xt[e], acc);
       o[e] = p.act ? silu(acc) : acc;
     }
+    {
+      float ss = o[0] * o[0];
+      ss = fmaf(o[1], o[1], ss);
+      ss = fmaf(o[2], o[2], ss);
+      ss = fmaf(o[3], o[3], ss);
+      ss = group_sum<(LPH < 16 ? LPH : 16)>(ss);
+      if constexpr (LPH == 32) {
+        // every lane of a 16-lane row now holds the row's sum; a head is two
+        // rows: combine them with scalar reads instead of an LDS permute
+        const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ss), 0));
+        const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ss), 16));
+        const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ss), 32));
+        const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ss), 48));
+        ss = (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
+      }
+      const float inv = p.l2norm ? 1.f / sqrtf(ss + p.eps) : 1.f;
+      const float f = c < p.Hk * DK ? inv * p.scale : (c < 2 * p.Hk * DK ? inv : 1.f);
+#pragma unroll
+      for (int e = 0; e < kCh; ++e) o[e] *= f;
+    }
     *reinterpret_cast<float4*>(y + (size_t)(pr.j0 + t) * C + c) =
         make_float4(o[0], o[1], o[2], o[3]);
     // slide the window: drop the oldest sample, append x_t
@@ -273,39 +363,48 @@ conv_prefill_kernel(PrefillArgs p, float* __restrict__ y) {
       for (int e = 0; e < kCh; ++e)
         if (m == W - 2) win[m][e] = xt[e];
   }
+  // Gates of this thread's pairs: log-decay ga and write strength gb.
+#pragma unroll
+  for (int k = 0; k < kGP; ++k) {
+    if (gidx[k] < 0) continue;
+    const int i = gidx[k] / Hv, h = gidx[k] - i * Hv;
+    if (base + i >= end) continue;
+    const float av = graw[k] >= 0 ? bf2f(graw_a[k]) : 0.f;
+    const float bv = graw[k] >= 0 ? bf2f(graw_b[k]) : 0.f;
+    ga[(size_t)(pr.j0 + base + i) * Hv + h] = gate_log(av, gl[k], gd[k]);
+    gb[(size_t)(pr.j0 + base + i) * Hv + h] = 1.f / (1.f + expf(-bv));
+  }
+  // Pairs beyond kGP per thread (many v-heads on few channel blocks).
+  for (int q = (int)threadIdx.x + kGP * live_thr; q < per_blk; q += live_thr) {
+    const int idx = (int)blockIdx.y * per_blk + q;
+    if (idx >= npairs) break;
+    const int i = idx / Hv, h = idx - i * Hv;
+    if (base + i >= end) continue;
+    const int r = global_row(p, pr.j0 + base + i);
+    const float av = r >= 0 ? bf2f(p.a[(size_t)r * Hv + h]) : 0.f;
+    const float bv = r >= 0 ? bf2f(p.b[(size_t)r * Hv + h]) : 0.f;
+    ga[(size_t)(pr.j0 + base + i) * Hv + h] = gate_log(av, p.A_log[h], p.dt_bias[h]);
+    gb[(size_t)(pr.j0 + base + i) * Hv + h] = 1.f / (1.f + expf(-bv));
+  }
   // Roll: new column l <- (history ++ inputs)[T + l].  All sources are
-  // loaded (in column order) before the first store: vector loads complete
-  // in order, so the store of column l, which waits for its own source,
-  // also follows the read of column l.  Only this thread writes these
-  // channels, and only the thread of the row's first tokens reads history.
-  if (seg == 0 && blockIdx.z == 0 && pr.slot > 0 && L > 0) {
+  // loaded (in column order; their rows are known since the start) before
+  // the first ring store: vector loads complete in order, so the store of
+  // column l, which waits for its own source, also follows the read of
+  // column l.  Only this thread writes these channels, and only the thread
+  // of the row's first tokens reads history.
+  if (roller) {
     uint16_t* wring = p.conv_pool + (size_t)pr.slot * L * C + c;
-    int ir[kMaxStateLen];
-    // stream indices of the inputs the new columns take (clamped into the
-    // row), their global rows in one batch of loads, then the range checks
+    u32x2 rhv[kMaxStateLen], riv[kMaxStateLen], nv[kMaxStateLen];
 #pragma unroll
     for (int l = 0; l < kMaxStateLen; ++l) {
-      const int tin = pr.T + l - L;        // input position when >= 0
-      ir[l] = pr.j0 + (tin > 0 ? (tin < pr.T ? tin : pr.T - 1) : 0);
-    }
-    if (p.tix) {
-#pragma unroll
-      for (int l = 0; l < kMaxStateLen; ++l) ir[l] = p.tix[ir[l]];
-    }
-#pragma unroll
-    for (int l = 0; l < kMaxStateLen; ++l)
-      ir[l] = (ir[l] >= 0 && ir[l] < p.num_actual_tokens) ? ir[l] : -1;
-    u32x2 hv[kMaxStateLen], iv[kMaxStateLen], nv[kMaxStateLen];
-#pragma unroll
-    for (int l = 0; l < kMaxStateLen; ++l) {
-      hv[l] = *ring_col(pr.T + l);         // position pr.T + l of (history ++ inputs)
-      iv[l] = *in_ptr(ir[l]);
+      rhv[l] = *ring_col(pr.T + l);        // position pr.T + l of (history ++ inputs)
+      riv[l] = *in_ptr(ir[l]);
     }
 #pragma unroll
     for (int l = 0; l < kMaxStateLen; ++l) {
       const bool hist = pr.T + l < L;
       const bool live = hist ? pr.init : ir[l] >= 0;
-      nv[l] = live ? (hist ? hv[l] : iv[l]) : u32x2{0u, 0u};
+      nv[l] = live ? (hist ? rhv[l] : riv[l]) : u32x2{0u, 0u};
     }
 #pragma unroll
     for (int l = 0; l < kMaxStateLen; ++l)
@@ -313,46 +412,23 @@ conv_prefill_kernel(PrefillArgs p, float* __restrict__ y) {
   }
 }
 
+// k.q per (token, k-head) from the normalised conv output, for the token
+// recurrence (head dims below 64).
 template <int DK>
 __global__ void __launch_bounds__(kThreads)
-prep_prefill_kernel(PrefillArgs p, float* __restrict__ y, float* __restrict__ kq,
-                    float* __restrict__ ga, float* __restrict__ gb) {
+kq_prefill_kernel(PrefillArgs p, const float* __restrict__ y, float* __restrict__ kq) {
   const int j = blockIdx.x;
   const int lo = clampi(p.qsl[0], 0, p.stream_tokens);
   const int hi = clampi(p.qsl[p.num_rows], lo, p.stream_tokens);
   if (j < lo || j >= hi) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int Hk = p.Hk, C = p.C;
-  float* yj = y + (size_t)j * C;
+  const float* yj = y + (size_t)j * C;
   for (int i = wv; i < Hk; i += kThreads / 64) {
-    float* q = yj + i * DK;
-    float* k = yj + Hk * DK + i * DK;
-    float sq = 0.f, sk = 0.f;
-    for (int c = lane; c < DK; c += 64) {
-      sq = fmaf(q[c], q[c], sq);
-      sk = fmaf(k[c], k[c], sk);
-    }
-    sq = wave_sum(sq);
-    sk = wave_sum(sk);
-    const float iq = p.l2norm ? 1.f / sqrtf(sq + p.eps) : 1.f;
-    const float ik = p.l2norm ? 1.f / sqrtf(sk + p.eps) : 1.f;
     float dot = 0.f;
-    for (int c = lane; c < DK; c += 64) {
-      float qq = q[c] * iq * p.scale;
-      float kk = k[c] * ik;
-      q[c] = qq;
-      k[c] = kk;
-      dot = fmaf(kk, qq, dot);
-    }
+    for (int c = lane; c < DK; c += 64) dot = fmaf(yj[Hk * DK + i * DK + c], yj[i * DK + c], dot);
     dot = wave_sum(dot);
     if (lane == 0) kq[(size_t)j * Hk + i] = dot;
-  }
-  const int r = global_row(p, j);
-  for (int h = tid; h < p.Hv; h += kThreads) {
-    float av = r >= 0 ? bf2f(p.a[(size_t)r * p.Hv + h]) : 0.f;
-    float bv = r >= 0 ? bf2f(p.b[(size_t)r * p.Hv + h]) : 0.f;
-    ga[(size_t)j * p.Hv + h] = gate_log(av, p.A_log[h], p.dt_bias[h]);
-    gb[(size_t)j * p.Hv + h] = 1.f / (1.f + expf(-bv));
   }
 }
 
@@ -474,13 +550,15 @@ hipError_t launch_prefill_typed(const PrefillArgs& args, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g1(a.units, (a.C / kCh + kThreads - 1) / kThreads, kSeg / kTokThread);
-  hipLaunchKernelGGL(conv_prefill_kernel, g1, dim3(kThreads), 0, s, a, y);
+  hipLaunchKernelGGL(conv_prefill_kernel<DK>, g1, dim3(kThreads), 0, s, a, y, ga, gb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prep_prefill_kernel<DK>, dim3(a.stream_tokens), dim3(kThreads), 0, s,
-                     a, y, kq, ga, gb);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if constexpr (DK < 64) {
+    hipLaunchKernelGGL(kq_prefill_kernel<DK>, dim3(a.stream_tokens), dim3(kThreads), 0, s, a, y,
+                       kq);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if constexpr (DK >= 64) {
     ChunkWs cw{reinterpret_cast<float*>(ws + w.W), reinterpret_cast<float*>(ws + w.U),
                reinterpret_cast<float*>(ws + w.P), reinterpret_cast<float*>(ws + w.G)};
