@@ -19,14 +19,22 @@
 // and G for its chunk (all chunks in parallel).
 // chunk_state_kernel: one workgroup per (row, v-head, 32 state rows) carries
 // its rows of S through the row's chunks in MFMA accumulators and writes the
-// outputs through token_indx.  Dense products use v_mfma_f32_16x16x4f32
-// (A[i][k] at lane i+16k, B[k][j] at lane j+16k, D[i][j] at lane j+16*(i/4),
-// element i%4).
+// outputs through token_indx.
 //
-// Sums over the 64 tokens of a chunk take 16 MFMA steps m = 4M + e, lane group
-// kk = lane/16 adding token s = 16M + 4kk + e: token block M (16 tokens) is one
-// group of four steps, so blocks a triangular factor zeroes are skipped, and a
-// lane's A operand for a block is one float4.
+// chunk_prep's products use v_mfma_f32_16x16x4f32 (A[i][k] at lane i+16k,
+// B[k][j] at lane j+16k, D[i][j] at lane j+16*(i/4), element i%4); its sums
+// over the 64 tokens of a chunk take 16 steps m = 4M + e, lane group
+// kk = lane/16 adding token s = 16M + 4kk + e, so a token block M that a
+// triangular factor zeroes is skipped.
+//
+// chunk_state's products run on v_mfma_f32_16x16x32_bf16 (lane l holds
+// A[l%16][8(l/16)+e] and B[8(l/16)+e][l%16], e = 0..7; D as above) with each
+// fp32 operand split into two bf16 values, x = hi + lo + O(2^-17 |x|) with
+// hi = bf16(x) and lo = bf16(x - hi); a product is hi*hi + hi*lo + lo*hi in
+// fp32 accumulation, about 2^-16 relative error per term where one fp32
+// product has 2^-24, at a sixteenth of the fp32 MFMA's cycles per term.
+// chunk_prep writes W and P already split: a row of n floats holds n bf16
+// hi values, then n bf16 lo values.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -41,6 +49,92 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
 }
 
 __device__ __forceinline__ int slot_ok(int s, int n) { return (s > 0 && s < n) ? s : 0; }
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Split of a float pair, two bf16 per word (element 0 in the low half).
+struct Split2 {
+  unsigned hi, lo;
+};
+__device__ __forceinline__ Split2 split2(float x0, float x1) {
+  const v2bf h = {(__bf16)x0, (__bf16)x1};
+  const unsigned hb = __builtin_bit_cast(unsigned, h);
+  const v2bf l = {(__bf16)(x0 - __uint_as_float(hb << 16)),
+                  (__bf16)(x1 - __uint_as_float(hb & 0xffff0000u))};
+  return {hb, __builtin_bit_cast(unsigned, l)};
+}
+__device__ __forceinline__ void split1(float x, uint16_t& hi, uint16_t& lo) {
+  const __bf16 h = (__bf16)x;
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = __builtin_bit_cast(uint16_t, (__bf16)(x - (float)h));
+}
+
+// An MFMA operand of eight split values.
+struct Frag {
+  u32x4 hi, lo;
+};
+__device__ __forceinline__ Frag split8(v4f a, v4f b) {
+  const Split2 s0 = split2(a.x, a.y), s1 = split2(a.z, a.w);
+  const Split2 s2 = split2(b.x, b.y), s3 = split2(b.z, b.w);
+  return {u32x4{s0.hi, s1.hi, s2.hi, s3.hi}, u32x4{s0.lo, s1.lo, s2.lo, s3.lo}};
+}
+__device__ __forceinline__ v4f mfma_bf(u32x4 a, u32x4 b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
+                                                  __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+// c + a b with a, b split: the three terms above 2^-16, small ones first
+__device__ __forceinline__ v4f mfma3(const Frag& a, const Frag& b, v4f c) {
+  c = mfma_bf(a.lo, b.hi, c);
+  c = mfma_bf(a.hi, b.lo, c);
+  return mfma_bf(a.hi, b.hi, c);
+}
+
+// Split tiles in LDS: row r holds COLS bf16 hi values then COLS lo values
+// (4 COLS bytes, as many as COLS floats).
+// Row operands (A, or B read as rows of B^T): 16-byte chunk ch of row r sits
+// at chunk ch ^ (r mod 16).  An operand read (16 consecutive rows, one
+// chunk) then hits every bank once, and so does a float4-swizzled fp32 tile
+// of the same row length copied bit for bit (sw<COLS> below is the same map).
+template <int COLS>
+__device__ __forceinline__ int ch16(int r, int ch) {
+  return r * 4 * COLS + ((ch ^ (r & 15)) << 4);
+}
+template <int COLS>
+__device__ __forceinline__ Frag frag_rows(const char* t, int r, int ks, int lk) {
+  Frag f;
+  f.hi = *reinterpret_cast<const u32x4*>(t + ch16<COLS>(r, 4 * ks + lk));
+  f.lo = *reinterpret_cast<const u32x4*>(t + ch16<COLS>(r, COLS / 8 + 4 * ks + lk));
+  return f;
+}
+// Column operands (B[s][k] of a row-major tile, read with ds_read_b64_tr_b16):
+// 32-byte block b of row r sits at block b ^ kswz(r).  One transposed read
+// takes 4 rows x 32 bytes per 16 lanes, rows 8 apart in the next 16 lanes;
+// kswz separates all eight rows.
+__device__ __forceinline__ int kswz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
+template <int COLS>
+__device__ __forceinline__ int blk32(int r, int x) {  // x: bf16 index in the row
+  return r * 4 * COLS + (((x >> 4) ^ kswz(r)) << 5) + ((x & 15) << 1);
+}
+// B operand B[s][k] = T[s][k] for s = 32 ks + 8 (l/16) + e, k = 16 mt + l%16:
+// lane m of each 16 points at row 8 (l/16) + m/4 (then 4 rows on), columns
+// 4 (m%4) .. +3 of the tile; the read hands lane l element l%4 of the
+// pieces of lanes 4e + l/4, which is T[.. + e][16 mt + l%16].
+__device__ __forceinline__ u32x2 tr_read(const char* t, int off) {
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + off));
+  return __builtin_bit_cast(u32x2, v);
+}
+template <int COLS>
+__device__ __forceinline__ Frag frag_cols(const char* t, int ks, int mt, int li, int lk) {
+  const int r = 32 * ks + 8 * lk + (li >> 2), x = 16 * mt + 4 * (li & 3);
+  const u32x2 h0 = tr_read(t, blk32<COLS>(r, x)), h1 = tr_read(t, blk32<COLS>(r + 4, x));
+  const u32x2 l0 = tr_read(t, blk32<COLS>(r, COLS + x)), l1 = tr_read(t, blk32<COLS>(r + 4, COLS + x));
+  return {u32x4{h0.x, h0.y, h1.x, h1.y}, u32x4{l0.x, l0.y, l1.x, l1.y}};
+}
 
 // LDS tiles hold P floats per row (P a multiple of 64, no padding); the
 // float4 groups of row r are XOR-permuted by r mod 16.  Float4 reads of 16
@@ -126,6 +220,29 @@ struct Tile4 {
       *reinterpret_cast<v4f*>(lds + sw<COLS>(r, c)) = v[i];
     }
   }
+  // fp32 tile split into a row-operand tile (see ch16)
+  __device__ __forceinline__ void store_split(char* lds) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = (i * NT + (int)threadIdx.x) * 4;
+      const int r = e / COLS, c = e - r * COLS;
+      const Split2 a = split2(v[i].x, v[i].y), b = split2(v[i].z, v[i].w);
+      const int in = (c & 7) << 1;
+      *reinterpret_cast<u32x2*>(lds + ch16<COLS>(r, c >> 3) + in) = u32x2{a.hi, b.hi};
+      *reinterpret_cast<u32x2*>(lds + ch16<COLS>(r, (COLS + c) >> 3) + in) = u32x2{a.lo, b.lo};
+    }
+  }
+  // fp32 tile split into a column-operand tile (see blk32)
+  __device__ __forceinline__ void store_split_cols(char* lds) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = (i * NT + (int)threadIdx.x) * 4;
+      const int r = e / COLS, c = e - r * COLS;
+      const Split2 a = split2(v[i].x, v[i].y), b = split2(v[i].z, v[i].w);
+      *reinterpret_cast<u32x2*>(lds + blk32<COLS>(r, c)) = u32x2{a.hi, b.hi};
+      *reinterpret_cast<u32x2*>(lds + blk32<COLS>(r, COLS + c)) = u32x2{a.lo, b.lo};
+    }
+  }
   // row-major tile with row pitch PITCH (a multiple of 4)
   template <int PITCH>
   __device__ __forceinline__ void store_pitched(float* lds) const {
@@ -198,13 +315,14 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
     Gs[tid] = tid < nt ? glog[(size_t)(jb + tid) * Hv + h] : 0.f;
     Bs[tid] = tid < nt ? gbeta[(size_t)(jb + tid) * Hv + h] : 0.f;
   }
-  // P is zero right of its diagonal blocks
+  // P is zero right of its diagonal blocks: 16-byte piece g of a split row
+  // holds columns 8 (g mod 8) .. +7 (hi for g < 8, lo after)
   {
     float* Pg = ws.P + ((size_t)jb * Hv + h) * kC;
 #pragma unroll
     for (int i = 0; i < kC * kC / 4 / 256; ++i) {
       const int e = i * 256 + tid, t = e >> 4, g = e & 15;
-      if ((g >> 2) > (t >> 4) && t < nt)
+      if (((g & 7) >> 1) > (t >> 4) && t < nt)
         *reinterpret_cast<v4f*>(Pg + (size_t)t * Hv * kC + 4 * g) = v4f{0.f, 0.f, 0.f, 0.f};
     }
   }
@@ -244,8 +362,13 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
         const float dec = expf(Gs[t] - Gs[s < t ? s : t]);
         if (!qk)
           As[sw<kC>(t, s)] = s < t ? Bs[t] * dec * acc[r] : 0.f;
-        else if (t < nt)
-          ws.P[((size_t)(jb + t) * Hv + h) * kC + s] = s <= t ? dec * acc[r] : 0.f;
+        else if (t < nt) {
+          uint16_t hi, lo;
+          split1(s <= t ? dec * acc[r] : 0.f, hi, lo);
+          uint16_t* prow = reinterpret_cast<uint16_t*>(ws.P + ((size_t)(jb + t) * Hv + h) * kC);
+          prow[s] = hi;
+          prow[kC + s] = lo;
+        }
       }
     }
   }
@@ -355,9 +478,14 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
         if (t < nt) {
 #pragma unroll
           for (int q = 0; q < NW; ++q) {
-            const size_t o = ((size_t)(jb + t) * Hv + h) * DK + 16 * (NW * wv + q) + li;
-            ws.W[o] = aw[ti][q][r];
-            ws.U[o] = au[ti][q][r];
+            const size_t o = ((size_t)(jb + t) * Hv + h) * DK;
+            const int col = 16 * (NW * wv + q) + li;
+            uint16_t hi, lo;
+            split1(aw[ti][q][r], hi, lo);
+            uint16_t* wrow = reinterpret_cast<uint16_t*>(ws.W + o);
+            wrow[col] = hi;
+            wrow[DK + col] = lo;
+            ws.U[o + col] = au[ti][q][r];
           }
         }
       }
@@ -365,20 +493,20 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   if (tid < nt) ws.G[(size_t)(jb + tid) * Hv + h] = Gs[tid];
 }
 
-// Shared memory of chunk_state_kernel (floats); RB state rows per workgroup.
+// Shared memory of chunk_state_kernel (bytes); RB state rows per workgroup.
 template <int DK, int RB>
 struct StateLds {
-  static constexpr int UP = RB + 4;               // pitch of the U~ block
-  static constexpr int wl = 0;                    // [kC][DK] W of the chunk
-  static constexpr int ql = wl + kC * DK;         // [kC][DK] queries
-  static constexpr int kl = ql + kC * DK;         // [kC][DK] keys
-  static constexpr int pl = kl + kC * DK;         // [kC][kC] P
-  static constexpr int ul = pl + kC * kC;         // [kC][UP] U~ block (plain)
-  static constexpr int ss = ul + kC * UP;         // [RB][DK] state block
-  static constexpr int ut = ss + RB * DK;         // [RB][kC] U^T block
-  static constexpr int gc = ut + RB * kC;         // [kC] G
-  static constexpr int fs = gc + kC;              // [kC] e^{G_C - G_t}
-  static constexpr int total = fs + kC;
+  static constexpr int UP = RB + 4;                   // pitch of the U~ block (floats)
+  static constexpr int wl = 0;                        // [kC] split rows of W (row operand)
+  static constexpr int ql = wl + kC * DK * 4;         // [kC] split rows of Q (row operand)
+  static constexpr int kl = ql + kC * DK * 4;         // [kC] split rows of K (column operand)
+  static constexpr int pl = kl + kC * DK * 4;         // [kC] split rows of P (row operand)
+  static constexpr int ul = pl + kC * kC * 4;         // [kC][UP] fp32 U~ block (plain)
+  static constexpr int ss = ul + kC * UP * 4;         // [RB][DK] fp32 state block
+  static constexpr int ut = ss + RB * DK * 4;         // [RB][kC] fp32 U^T block
+  static constexpr int gc = ut + RB * kC * 4;         // [kC] G
+  static constexpr int fs = gc + kC * 4;              // [kC] e^{G_C - G_t}
+  static constexpr int total = fs + kC * 4;
 };
 
 constexpr int kStateThreads = 512;  // 8 waves, two per SIMD
@@ -386,25 +514,27 @@ constexpr int kStateRows = 32;      // state rows per workgroup
 
 // Wave w works on token tile tt = w % 4 and state-row tile jt = w / 4 for
 // U and the outputs, and on state tiles (jt, TPW*tt + q) for the update.
+// Every product contracts over 32-wide steps: k (W S0^T, Q S0^T) or tokens
+// (P U, U^T diag(F) K).
 template <int DK, int DV>
 __global__ void __launch_bounds__(kStateThreads)
 chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   static_assert(DK == DV && DK % 64 == 0, "dk == dv, multiple of 64");
   constexpr int NT = kStateThreads, RB = kStateRows;
-  extern __shared__ __align__(16) float sm[];
+  extern __shared__ __align__(16) char smb[];
   using Lay = StateLds<DK, RB>;
   constexpr int UP = Lay::UP;
-  constexpr int KQ = DK / 4;
+  constexpr int KS = DK / 32;   // k-steps
   constexpr int TPW = DK / 64;  // state column tiles per wave
-  float* Wl = sm + Lay::wl;
-  float* Ql = sm + Lay::ql;
-  float* Kl = sm + Lay::kl;
-  float* Pl = sm + Lay::pl;
-  float* Ul = sm + Lay::ul;
-  float* Ss = sm + Lay::ss;
-  float* UT = sm + Lay::ut;
-  float* Gc = sm + Lay::gc;
-  float* Fs = sm + Lay::fs;
+  char* Wl = smb + Lay::wl;
+  char* Ql = smb + Lay::ql;
+  char* Kl = smb + Lay::kl;
+  char* Pl = smb + Lay::pl;
+  float* Ul = reinterpret_cast<float*>(smb + Lay::ul);
+  float* Ss = reinterpret_cast<float*>(smb + Lay::ss);
+  float* UT = reinterpret_cast<float*>(smb + Lay::ut);
+  float* Gc = reinterpret_cast<float*>(smb + Lay::gc);
+  float* Fs = reinterpret_cast<float*>(smb + Lay::fs);
 
   const int Hv = p.Hv, Hk = p.Hk, C = p.C;
   const int row = blockIdx.x / Hv, h = head_of(blockIdx.x - row * Hv, Hv);
@@ -427,7 +557,8 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
                          : 0.f;
 
   const int nch = (pr.T + kC - 1) / kC;
-  // Operands of chunk c+1 are gathered while chunk c is computed.
+  // Operands of chunk c+1 are gathered while chunk c is computed (W and P
+  // arrive split, Q and K are split on their way to LDS).
   Tile4<kC, DK, NT> tw, tq, tk;
   Tile4<kC, kC, NT> tp;
   Tile4<kC, RB, NT> tu;
@@ -454,10 +585,10 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   gather(0);
   for (int c = 0; c < nch; ++c) {
     const int nt = min(kC, pr.T - c * kC);
-    tw.store_sw(Wl);
-    tq.store_sw(Ql);
-    tk.store_sw(Kl);
-    tp.store_sw(Pl);
+    tw.store_sw(reinterpret_cast<float*>(Wl));  // split bits, copied as they are
+    tq.store_split(Ql);
+    tk.store_split_cols(Kl);
+    tp.store_sw(reinterpret_cast<float*>(Pl));
     tu.template store_pitched<UP>(Ul);
     if (tid < kC) Gc[tid] = tg;
     int orow[4];
@@ -472,16 +603,18 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
 
     const float gC = Gc[kC - 1];
     if (tid < kC) Fs[tid] = expf(gC - Gc[tid]);
-    // B operand of S0^T products: S[j][k], j in row tile jt, this lane's k-run
-    float sb[KQ];
-    lds_run<DK>(sb, Ss, 16 * jt + li, lk * KQ);
+    // B operand of the S0^T products: S0[j][k], j = 16 jt + li, k in the
+    // lane's 8-runs of each k-step
+    Frag sb[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      sb[ks] = split8(ld4<DK>(Ss, 16 * jt + li, 32 * ks + 8 * lk),
+                      ld4<DK>(Ss, 16 * jt + li, 32 * ks + 8 * lk + 4));
     // (a) U = U~ - W S0^T on (token tile tt, row tile jt), kept as U^T
     {
-      float aw[KQ];
-      lds_run<DK>(aw, Wl, 16 * tt + li, lk * KQ);
       v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < KQ; ++m) acc = mfma4(aw[m], sb[m], acc);
+      for (int ks = 0; ks < KS; ++ks) acc = mfma3(frag_rows<DK>(Wl, 16 * tt + li, ks, lk), sb[ks], acc);
       v4f u;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -491,27 +624,25 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
       *reinterpret_cast<v4f*>(UT + sw<kC>(16 * jt + li, 16 * tt + 4 * lk)) = u;
     }
     lds_barrier();
-    // the next chunk's operands load during (b) and (c); their registers are
-    // free while (a) holds its operand runs
+    // the next chunk's operands load during (b) and (c)
     if (c + 1 < nch) gather(c + 1);
 
+    // U^T[j][s] for j = 16 jt + li and the lane's 8-runs of tokens: the B
+    // operand of P U and, scaled by F, the A operand of the update
+    v4f ur[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      ur[ks][0] = ld4<kC>(UT, 16 * jt + li, 32 * ks + 8 * lk);
+      ur[ks][1] = ld4<kC>(UT, 16 * jt + li, 32 * ks + 8 * lk + 4);
+    }
     // (b) outputs on (tt, jt): e^{G_t} (Q S0^T)[t] + (P U)[t]; P is zero
-    //     right of the diagonal block
+    //     right of the diagonal block, so tokens 32..63 matter from tt = 2 on
     {
-      float aqr[KQ];
-      lds_run<DK>(aqr, Ql, 16 * tt + li, lk * KQ);
       v4f aq = {0.f, 0.f, 0.f, 0.f}, ap = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < KQ; ++m) aq = mfma4(aqr[m], sb[m], aq);
-#pragma unroll
-      for (int M = 0; M < 4; ++M) {
-        if (M <= tt) {
-          const v4f a = ld4<kC>(Pl, 16 * tt + li, 16 * M + 4 * lk);
-          const v4f b = ld4<kC>(UT, 16 * jt + li, 16 * M + 4 * lk);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ap = mfma4(a[e], b[e], ap);
-        }
-      }
+      for (int ks = 0; ks < KS; ++ks) aq = mfma3(frag_rows<DK>(Ql, 16 * tt + li, ks, lk), sb[ks], aq);
+      ap = mfma3(frag_rows<kC>(Pl, 16 * tt + li, 0, lk), split8(ur[0][0], ur[0][1]), ap);
+      if (tt >= 2) ap = mfma3(frag_rows<kC>(Pl, 16 * tt + li, 1, lk), split8(ur[1][0], ur[1][1]), ap);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tt + 4 * lk + r;
@@ -523,13 +654,12 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
 
     // (c) S = e^{G_C} S0 + U^T diag(e^{G_C - G_t}) K on this wave's tiles
     {
-      float ua[16];
+      Frag ua[2];
 #pragma unroll
-      for (int M = 0; M < 4; ++M) {
-        const v4f a = ld4<kC>(UT, 16 * jt + li, 16 * M + 4 * lk);
-        const v4f f = *reinterpret_cast<const v4f*>(Fs + 16 * M + 4 * lk);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ua[4 * M + e] = a[e] * f[e];
+      for (int ks = 0; ks < 2; ++ks) {
+        const v4f f0 = *reinterpret_cast<const v4f*>(Fs + 32 * ks + 8 * lk);
+        const v4f f1 = *reinterpret_cast<const v4f*>(Fs + 32 * ks + 8 * lk + 4);
+        ua[ks] = split8(ur[ks][0] * f0, ur[ks][1] * f1);
       }
       const float eC = expf(gC);
 #pragma unroll
@@ -537,10 +667,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
         const int mt = TPW * tt + q;
         v4f acc = St[q] * eC;
 #pragma unroll
-        for (int M = 0; M < 4; ++M)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc = mfma4(ua[4 * M + e], Kl[sw<DK>(16 * M + 4 * lk + e, 16 * mt + li)], acc);
+        for (int ks = 0; ks < 2; ++ks) acc = mfma3(ua[ks], frag_cols<DK>(Kl, ks, mt, li, lk), acc);
         St[q] = acc;
       }
     }
@@ -557,27 +684,11 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
 
 }  // namespace
 
-size_t chunk_lds_prep(int dk) {
-  switch (dk) {
-    case 64: return sizeof(float) * PrepLds<64>::total;
-    case 128: return sizeof(float) * PrepLds<128>::total;
-    default: return 0;
-  }
-}
-
-size_t chunk_lds_state(int dk) {
-  switch (dk) {
-    case 64: return sizeof(float) * StateLds<64, kStateRows>::total;
-    case 128: return sizeof(float) * StateLds<128, kStateRows>::total;
-    default: return 0;
-  }
-}
-
 template <int DK, int DV>
 static hipError_t launch_chunked_typed(const PrefillArgs& a, const float* y, const float* glog,
                                        const float* gbeta, const ChunkWs& ws, hipStream_t s) {
   const size_t l1 = sizeof(float) * PrepLds<DK>::total;
-  const size_t l2 = sizeof(float) * StateLds<DK, kStateRows>::total;
+  const size_t l2 = StateLds<DK, kStateRows>::total;
   hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(chunk_prep_kernel<DK, DV>), l1);
   if (e != hipSuccess) return e;
   e = ensure_dynamic_lds(reinterpret_cast<const void*>(chunk_state_kernel<DK, DV>), l2);
