@@ -94,35 +94,31 @@ __device__ __forceinline__ v4f mfma3(const Frag& a, const Frag& b, v4f c) {
 }
 
 // Split tiles in LDS: row r holds COLS bf16 hi values then COLS lo values
-// (4 COLS bytes, as many as COLS floats).
-// Row operands (A, or B read as rows of B^T): 16-byte chunk ch of row r sits
-// at chunk ch ^ (r mod 16).  An operand read (16 consecutive rows, one
-// chunk) then hits every bank once, and so does a float4-swizzled fp32 tile
-// of the same row length copied bit for bit (sw<COLS> below is the same map).
-template <int COLS>
-__device__ __forceinline__ int ch16(int r, int ch) {
-  return r * 4 * COLS + ((ch ^ (r & 15)) << 4);
+// (4 COLS bytes, as many as COLS floats); its 16-byte chunk ch sits at chunk
+// ch ^ sig(r), sig a permutation of the row's low four bits.  Row operands
+// (A, or B read as rows of B^T: 16 consecutive rows, one chunk) then hit
+// every bank once, and so do column operands (B[s][k] read with
+// ds_read_b64_tr_b16: 16 lanes take rows s..s+3 at one 32-byte block, the
+// next 16 lanes rows s+8..s+11), since sig(r) >> 1 differs on all eight.
+__device__ __forceinline__ int sig(int r) {
+  return ((r & 3) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1);
 }
+template <int COLS>
+__device__ __forceinline__ int sp_off(int r, int x) {  // x: bf16 index in the row, x % 4 == 0
+  return r * 4 * COLS + (((x >> 3) ^ sig(r)) << 4) + ((x & 7) << 1);
+}
+// A operand A[t][k] (or B[k][t] = T[t][k]) for t = r0 + l%16, k = 32 ks + 8 (l/16) + e
 template <int COLS>
 __device__ __forceinline__ Frag frag_rows(const char* t, int r, int ks, int lk) {
   Frag f;
-  f.hi = *reinterpret_cast<const u32x4*>(t + ch16<COLS>(r, 4 * ks + lk));
-  f.lo = *reinterpret_cast<const u32x4*>(t + ch16<COLS>(r, COLS / 8 + 4 * ks + lk));
+  f.hi = *reinterpret_cast<const u32x4*>(t + sp_off<COLS>(r, 32 * ks + 8 * lk));
+  f.lo = *reinterpret_cast<const u32x4*>(t + sp_off<COLS>(r, COLS + 32 * ks + 8 * lk));
   return f;
-}
-// Column operands (B[s][k] of a row-major tile, read with ds_read_b64_tr_b16):
-// 32-byte block b of row r sits at block b ^ kswz(r).  One transposed read
-// takes 4 rows x 32 bytes per 16 lanes, rows 8 apart in the next 16 lanes;
-// kswz separates all eight rows.
-__device__ __forceinline__ int kswz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
-template <int COLS>
-__device__ __forceinline__ int blk32(int r, int x) {  // x: bf16 index in the row
-  return r * 4 * COLS + (((x >> 4) ^ kswz(r)) << 5) + ((x & 15) << 1);
 }
 // B operand B[s][k] = T[s][k] for s = 32 ks + 8 (l/16) + e, k = 16 mt + l%16:
 // lane m of each 16 points at row 8 (l/16) + m/4 (then 4 rows on), columns
-// 4 (m%4) .. +3 of the tile; the read hands lane l element l%4 of the
-// pieces of lanes 4e + l/4, which is T[.. + e][16 mt + l%16].
+// 4 (m%4) .. +3 of the tile; the transposed read hands lane l element l%4 of
+// the pieces of lanes 4e + l/4, which is T[.. + e][16 mt + l%16].
 __device__ __forceinline__ u32x2 tr_read(const char* t, int off) {
   typedef __attribute__((address_space(3))) v4s lds_v4s;
   const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + off));
@@ -131,9 +127,17 @@ __device__ __forceinline__ u32x2 tr_read(const char* t, int off) {
 template <int COLS>
 __device__ __forceinline__ Frag frag_cols(const char* t, int ks, int mt, int li, int lk) {
   const int r = 32 * ks + 8 * lk + (li >> 2), x = 16 * mt + 4 * (li & 3);
-  const u32x2 h0 = tr_read(t, blk32<COLS>(r, x)), h1 = tr_read(t, blk32<COLS>(r + 4, x));
-  const u32x2 l0 = tr_read(t, blk32<COLS>(r, COLS + x)), l1 = tr_read(t, blk32<COLS>(r + 4, COLS + x));
+  const u32x2 h0 = tr_read(t, sp_off<COLS>(r, x)), h1 = tr_read(t, sp_off<COLS>(r + 4, x));
+  const u32x2 l0 = tr_read(t, sp_off<COLS>(r, COLS + x));
+  const u32x2 l1 = tr_read(t, sp_off<COLS>(r + 4, COLS + x));
   return {u32x4{h0.x, h0.y, h1.x, h1.y}, u32x4{l0.x, l0.y, l1.x, l1.y}};
+}
+// Four consecutive values (columns c..c+3 of row r) into a split tile.
+template <int COLS>
+__device__ __forceinline__ void store_split4(char* t, int r, int c, v4f v) {
+  const Split2 a = split2(v.x, v.y), b = split2(v.z, v.w);
+  *reinterpret_cast<u32x2*>(t + sp_off<COLS>(r, c)) = u32x2{a.hi, b.hi};
+  *reinterpret_cast<u32x2*>(t + sp_off<COLS>(r, COLS + c)) = u32x2{a.lo, b.lo};
 }
 
 // LDS tiles hold P floats per row (P a multiple of 64, no padding); the
@@ -149,20 +153,6 @@ __device__ __forceinline__ int sw(int r, int c) {
 template <int P>
 __device__ __forceinline__ v4f ld4(const float* t, int r, int c) {
   return *reinterpret_cast<const v4f*>(t + sw<P>(r, c));
-}
-
-// N consecutive floats of row r from column c0 (a multiple of 4).
-template <int P, int N>
-__device__ __forceinline__ void lds_run(float (&dst)[N], const float* t, int r, int c0) {
-  static_assert(N % 4 == 0, "runs of float4");
-#pragma unroll
-  for (int i = 0; i < N / 4; ++i) {
-    const v4f v = ld4<P>(t, r, c0 + 4 * i);
-    dst[4 * i] = v.x;
-    dst[4 * i + 1] = v.y;
-    dst[4 * i + 2] = v.z;
-    dst[4 * i + 3] = v.w;
-  }
 }
 
 // Workgroups go to the XCDs round-robin by linear index.  With Hv a multiple
@@ -220,27 +210,23 @@ struct Tile4 {
       *reinterpret_cast<v4f*>(lds + sw<COLS>(r, c)) = v[i];
     }
   }
-  // fp32 tile split into a row-operand tile (see ch16)
+  // fp32 tile split into a split tile of row length COLS
   __device__ __forceinline__ void store_split(char* lds) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int e = (i * NT + (int)threadIdx.x) * 4;
       const int r = e / COLS, c = e - r * COLS;
-      const Split2 a = split2(v[i].x, v[i].y), b = split2(v[i].z, v[i].w);
-      const int in = (c & 7) << 1;
-      *reinterpret_cast<u32x2*>(lds + ch16<COLS>(r, c >> 3) + in) = u32x2{a.hi, b.hi};
-      *reinterpret_cast<u32x2*>(lds + ch16<COLS>(r, (COLS + c) >> 3) + in) = u32x2{a.lo, b.lo};
+      store_split4<COLS>(lds, r, c, v[i]);
     }
   }
-  // fp32 tile split into a column-operand tile (see blk32)
-  __device__ __forceinline__ void store_split_cols(char* lds) const {
+  // tile already split (a row of COLS floats' bytes holds COLS hi then COLS
+  // lo bf16 values), copied as it is into a split tile of row length COLS
+  __device__ __forceinline__ void store_raw_split(char* lds) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int e = (i * NT + (int)threadIdx.x) * 4;
       const int r = e / COLS, c = e - r * COLS;
-      const Split2 a = split2(v[i].x, v[i].y), b = split2(v[i].z, v[i].w);
-      *reinterpret_cast<u32x2*>(lds + blk32<COLS>(r, c)) = u32x2{a.hi, b.hi};
-      *reinterpret_cast<u32x2*>(lds + blk32<COLS>(r, COLS + c)) = u32x2{a.lo, b.lo};
+      *reinterpret_cast<v4f*>(lds + sp_off<COLS>(r, 2 * c)) = v[i];
     }
   }
   // row-major tile with row pitch PITCH (a multiple of 4)
@@ -255,19 +241,21 @@ struct Tile4 {
   }
 };
 
-// Shared-memory carve-up of chunk_prep_kernel (floats).
+// Shared-memory carve-up of chunk_prep_kernel (bytes).
 template <int DK>
 struct PrepLds {
-  static constexpr int MP = 20;                 // pitch of the 16x16 scratch
-  static constexpr int ks = 0;                  // [kC][DK] keys
-  static constexpr int qv = ks + kC * DK;       // [kC][DK] queries, then values
-  static constexpr int as = qv + kC * DK;       // [kC][kC] A
-  static constexpr int tt = as + kC * kC;       // [kC][kC] T
-  static constexpr int mw = tt + kC * kC;       // [4][16][MP] per-wave scratch
-  static constexpr int gs = mw + 4 * 16 * MP;   // [kC] cumulative log-decay
-  static constexpr int bs = gs + kC;            // [kC] beta
-  static constexpr int bg = bs + kC;            // [kC] beta e^G
-  static constexpr int total = bg + kC;
+  static constexpr int MP = 20;                     // pitch of the 16x16 scratch
+  static constexpr int ks = 0;                      // [kC] split rows of K
+  static constexpr int qv = ks + kC * DK * 4;       // [kC] split rows of Q, then of V
+  static constexpr int tg = qv + kC * DK * 4;       // [kC] split rows of T diag(b e^G)
+  static constexpr int tb = tg + kC * kC * 4;       // [kC] split rows of T diag(b)
+  static constexpr int as = tb + kC * kC * 4;       // [kC][kC] fp32 A
+  static constexpr int tt = as + kC * kC * 4;       // [kC][kC] fp32 T
+  static constexpr int mw = tt + kC * kC * 4;       // [4][16][MP] fp32 per-wave scratch
+  static constexpr int gs = mw + 4 * 16 * MP * 4;   // [kC] cumulative log-decay
+  static constexpr int bs = gs + kC * 4;            // [kC] beta
+  static constexpr int bg = bs + kC * 4;            // [kC] beta e^G
+  static constexpr int total = bg + kC * 4;
 };
 
 template <int DK, int DV>
@@ -275,17 +263,18 @@ __global__ void __launch_bounds__(256)
 chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __restrict__ glog,
                   const float* __restrict__ gbeta, ChunkWs ws) {
   static_assert(DK == DV && DK % 64 == 0, "dk == dv, multiple of 64");
-  extern __shared__ __align__(16) float sm[];
+  extern __shared__ __align__(16) char smb[];
   using Lay = PrepLds<DK>;
   constexpr int MP = Lay::MP;
-  constexpr int KQ = DK / 4;   // k-run per lane group, Gram products
-  float* Ks = sm + Lay::ks;
-  float* QV = sm + Lay::qv;
-  float* As = sm + Lay::as;
-  float* Tt = sm + Lay::tt;
-  float* Gs = sm + Lay::gs;
-  float* Bs = sm + Lay::bs;
-  float* BG = sm + Lay::bg;
+  char* Ks = smb + Lay::ks;
+  char* QV = smb + Lay::qv;
+  char* TG = smb + Lay::tg;
+  char* TB = smb + Lay::tb;
+  float* As = reinterpret_cast<float*>(smb + Lay::as);
+  float* Tt = reinterpret_cast<float*>(smb + Lay::tt);
+  float* Gs = reinterpret_cast<float*>(smb + Lay::gs);
+  float* Bs = reinterpret_cast<float*>(smb + Lay::bs);
+  float* BG = reinterpret_cast<float*>(smb + Lay::bg);
 
   const int row = p.unit_map[2 * blockIdx.y];
   if (row < 0) return;
@@ -298,7 +287,7 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   const int ih = h / p.G, Hk = p.Hk, Hv = p.Hv, C = p.C;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int li = lane & 15, lk = lane >> 4;
-  float* Mw = sm + Lay::mw + wv * 16 * MP;
+  float* Mw = reinterpret_cast<float*>(smb + Lay::mw) + wv * 16 * MP;
 
   // 1. keys, queries and values of the chunk gathered in one batch
   Tile4<kC, DV> tv;
@@ -308,8 +297,8 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
     tk.load(yb + Hk * DK + ih * DK, C, nt);
     tq.load(yb + ih * DK, C, nt);
     tv.load(yb + 2 * Hk * DK + h * DV, C, nt);
-    tk.store_sw(Ks);
-    tq.store_sw(QV);
+    tk.store_split(Ks);
+    tq.store_split(QV);
   }
   if (tid < kC) {
     Gs[tid] = tid < nt ? glog[(size_t)(jb + tid) * Hv + h] : 0.f;
@@ -341,21 +330,21 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   lds_barrier();
   // 3. K K^T and Q K^T on the ten 16x16 tiles (ti >= tj) that A and P use:
   //    twenty tile products, five per wave (waves 0 and 2 K K^T, 1 and 3
-  //    Q K^T; waves 0 and 1 the even tiles in row order, 2 and 3 the odd).
+  //    Q K^T; waves 0 and 1 the even tiles in row order, 2 and 3 the odd),
+  //    on split operands (B[k][s] = K[s][k] read as rows of K).
   {
     const bool qk = (wv & 1) != 0;
-    const float* Asrc = qk ? QV : Ks;
+    const char* Asrc = qk ? QV : Ks;
 #pragma unroll
     for (int it = 0; it < 5; ++it) {
       const int x = 2 * it + (wv >> 1);
       const int ti = x < 1 ? 0 : (x < 3 ? 1 : (x < 6 ? 2 : 3));
       const int tj = x - ti * (ti + 1) / 2;
-      float ar[KQ], br[KQ];
-      lds_run<DK>(ar, Asrc, 16 * ti + li, lk * KQ);
-      lds_run<DK>(br, Ks, 16 * tj + li, lk * KQ);
       v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < KQ; ++m) acc = mfma4(ar[m], br[m], acc);
+      for (int k = 0; k < DK / 32; ++k)
+        acc = mfma3(frag_rows<DK>(Asrc, 16 * ti + li, k, lk), frag_rows<DK>(Ks, 16 * tj + li, k, lk),
+                    acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * ti + 4 * lk + r, s = 16 * tj + li;
@@ -403,7 +392,7 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
     for (int cb = wv + 1; cb < 4; ++cb)
       *reinterpret_cast<v4f*>(Tt + sw<kC>(b0 + li, 16 * cb + 4 * lk)) = v4f{0.f, 0.f, 0.f, 0.f};
   }
-  tv.store_sw(QV);
+  tv.store_split(QV);
   lds_barrier();
   //    Blocks below the diagonal, one diagonal level at a time:
   //    T_ij = -T_ii M with M = sum_{k=j}^{i-1} A_ik T_kj (wave w: j = w).
@@ -432,9 +421,18 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
     }
     lds_barrier();
   }
-  // 5. W = T diag(b e^G) K and U~ = T diag(b) V.  Wave w computes column
-  //    tiles NW*w .. NW*w+NW-1 for every token tile; token block M feeds
-  //    token tiles ti >= M only (T is block lower triangular).
+  // 5. W = T diag(b e^G) K and U~ = T diag(b) V on split operands: the
+  //    scaled T as rows, K and V as columns.  Wave w computes column tiles
+  //    NW*w .. NW*w+NW-1 for every token tile; tokens 32..63 feed token
+  //    tiles 2 and 3 only (T is lower triangular).
+#pragma unroll
+  for (int i = 0; i < kC * kC / 4 / 256; ++i) {
+    const int e = (i * 256 + tid) * 4, r = e / kC, cc = e - r * kC;
+    const v4f tv4 = ld4<kC>(Tt, r, cc);
+    store_split4<kC>(TG, r, cc, tv4 * *reinterpret_cast<const v4f*>(BG + cc));
+    store_split4<kC>(TB, r, cc, tv4 * *reinterpret_cast<const v4f*>(Bs + cc));
+  }
+  lds_barrier();
   {
     constexpr int NW = DK / 64;
     v4f aw[4][NW], au[4][NW];
@@ -445,31 +443,27 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
         aw[ti][q] = v4f{0.f, 0.f, 0.f, 0.f};
         au[ti][q] = v4f{0.f, 0.f, 0.f, 0.f};
       }
+    Frag kb[2][NW], vb[2][NW];
 #pragma unroll
-    for (int M = 0; M < 4; ++M) {
-      const v4f g4 = *reinterpret_cast<const v4f*>(BG + 16 * M + 4 * lk);
-      const v4f b4 = *reinterpret_cast<const v4f*>(Bs + 16 * M + 4 * lk);
-      float kb[4][NW], vb[4][NW];
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+      for (int q = 0; q < NW; ++q) {
+        kb[ks][q] = frag_cols<DK>(Ks, ks, NW * wv + q, li, lk);
+        vb[ks][q] = frag_cols<DK>(QV, ks, NW * wv + q, li, lk);
+      }
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if (ks == 1 && ti < 2) continue;
+        const Frag ag = frag_rows<kC>(TG, 16 * ti + li, ks, lk);
+        const Frag ab = frag_rows<kC>(TB, 16 * ti + li, ks, lk);
 #pragma unroll
         for (int q = 0; q < NW; ++q) {
-          const int sidx = sw<DK>(16 * M + 4 * lk + e, 16 * (NW * wv + q) + li);
-          kb[e][q] = g4[e] * Ks[sidx];
-          vb[e][q] = b4[e] * QV[sidx];
+          aw[ti][q] = mfma3(ag, kb[ks][q], aw[ti][q]);
+          au[ti][q] = mfma3(ab, vb[ks][q], au[ti][q]);
         }
-#pragma unroll
-      for (int ti = M; ti < 4; ++ti) {
-        const v4f a = ld4<kC>(Tt, 16 * ti + li, 16 * M + 4 * lk);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int q = 0; q < NW; ++q) {
-            aw[ti][q] = mfma4(a[e], kb[e][q], aw[ti][q]);
-            au[ti][q] = mfma4(a[e], vb[e][q], au[ti][q]);
-          }
       }
-    }
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
@@ -585,10 +579,10 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   gather(0);
   for (int c = 0; c < nch; ++c) {
     const int nt = min(kC, pr.T - c * kC);
-    tw.store_sw(reinterpret_cast<float*>(Wl));  // split bits, copied as they are
+    tw.store_raw_split(Wl);
     tq.store_split(Ql);
-    tk.store_split_cols(Kl);
-    tp.store_sw(reinterpret_cast<float*>(Pl));
+    tk.store_split(Kl);
+    tp.store_raw_split(Pl);
     tu.template store_pitched<UP>(Ul);
     if (tid < kC) Gc[tid] = tg;
     int orow[4];
@@ -687,7 +681,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
 template <int DK, int DV>
 static hipError_t launch_chunked_typed(const PrefillArgs& a, const float* y, const float* glog,
                                        const float* gbeta, const ChunkWs& ws, hipStream_t s) {
-  const size_t l1 = sizeof(float) * PrepLds<DK>::total;
+  const size_t l1 = PrepLds<DK>::total;
   const size_t l2 = StateLds<DK, kStateRows>::total;
   hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(chunk_prep_kernel<DK, DV>), l1);
   if (e != hipSuccess) return e;
