@@ -241,21 +241,39 @@ struct Tile4 {
   }
 };
 
-// Shared-memory carve-up of chunk_prep_kernel (bytes).
+// A's ten lower 16x16 blocks (the rest is zero), block (bi, bj) at
+// bi (bi + 1) / 2 + bj; inside a block, row r at slot (r & 12) | ((r + r/4) & 3)
+// and float4 group g at g ^ (r/4 mod 4).  Scalar writes of an MFMA result
+// (rows 4kk + i, 16 columns) and float4 reads of 16 rows then hit every bank
+// once.  Offsets in floats; s % 4 == 0 for float4 reads.
+__device__ __forceinline__ int as_off(int t, int s) {
+  const int bi = t >> 4, bj = s >> 4, r = t & 15, c = s & 15;
+  const int slot = (r & 12) | ((r + (r >> 2)) & 3);
+  return (bi * (bi + 1) / 2 + bj) * 256 + slot * 16 + ((((c >> 2) ^ (r >> 2)) & 3) << 2) + (c & 3);
+}
+
+// Shared memory of chunk_prep_kernel (bytes), sized for two workgroups per
+// CU.  The second region holds Q for the Gram products, then T and the
+// per-wave scratch, then T diag(b e^G) and T diag(b); V never enters LDS
+// (each wave loads its own operands of U~ = T diag(b) V).
 template <int DK>
 struct PrepLds {
   static constexpr int MP = 20;                     // pitch of the 16x16 scratch
   static constexpr int ks = 0;                      // [kC] split rows of K
-  static constexpr int qv = ks + kC * DK * 4;       // [kC] split rows of Q, then of V
-  static constexpr int tg = qv + kC * DK * 4;       // [kC] split rows of T diag(b e^G)
-  static constexpr int tb = tg + kC * kC * 4;       // [kC] split rows of T diag(b)
-  static constexpr int as = tb + kC * kC * 4;       // [kC][kC] fp32 A
-  static constexpr int tt = as + kC * kC * 4;       // [kC][kC] fp32 T
-  static constexpr int mw = tt + kC * kC * 4;       // [4][16][MP] fp32 per-wave scratch
-  static constexpr int gs = mw + 4 * 16 * MP * 4;   // [kC] cumulative log-decay
+  static constexpr int r2 = ks + kC * DK * 4;       // second region:
+  static constexpr int qs = r2;                     //   [kC] split rows of Q
+  static constexpr int tt = r2;                     //   [kC][kC] fp32 T
+  static constexpr int mw = tt + kC * kC * 4;       //   [4][16][MP] fp32 scratch
+  static constexpr int tg = r2;                     //   [kC] split rows of T diag(b e^G)
+  static constexpr int tb = tg + kC * kC * 4;       //   [kC] split rows of T diag(b)
+  static constexpr int r2_bytes = 2 * kC * kC * 4 > kC * DK * 4 ? 2 * kC * kC * 4 : kC * DK * 4;
+  static_assert(mw + 4 * 16 * MP * 4 <= r2 + r2_bytes, "scratch fits");
+  static constexpr int as = r2 + r2_bytes;          // A, ten 16x16 fp32 blocks
+  static constexpr int gs = as + 10 * 256 * 4;      // [kC] cumulative log-decay
   static constexpr int bs = gs + kC * 4;            // [kC] beta
   static constexpr int bg = bs + kC * 4;            // [kC] beta e^G
   static constexpr int total = bg + kC * 4;
+  static_assert(total <= 80 * 1024, "two workgroups per CU");
 };
 
 template <int DK, int DV>
@@ -267,7 +285,7 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   using Lay = PrepLds<DK>;
   constexpr int MP = Lay::MP;
   char* Ks = smb + Lay::ks;
-  char* QV = smb + Lay::qv;
+  char* Qs = smb + Lay::qs;
   char* TG = smb + Lay::tg;
   char* TB = smb + Lay::tb;
   float* As = reinterpret_cast<float*>(smb + Lay::as);
@@ -289,16 +307,26 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   const int li = lane & 15, lk = lane >> 4;
   float* Mw = reinterpret_cast<float*>(smb + Lay::mw) + wv * 16 * MP;
 
-  // 1. keys, queries and values of the chunk gathered in one batch
-  Tile4<kC, DV> tv;
+  // 1. keys and queries of the chunk gathered in one batch, and this wave's
+  //    operands of U~ = T diag(b) V: V[s][16 (NW w + q) + l%16] for the
+  //    lane's tokens s = 32 ks + 8 (l/16) + e (rows past the chunk's tokens
+  //    are padding, read and dropped where used)
+  constexpr int NW = DK / 64;
+  float vr[2][NW][8];
   {
     Tile4<kC, DK> tk, tq;
     const float* yb = y + (size_t)jb * C;
     tk.load(yb + Hk * DK + ih * DK, C, nt);
     tq.load(yb + ih * DK, C, nt);
-    tv.load(yb + 2 * Hk * DK + h * DV, C, nt);
+    const float* vb = yb + 2 * Hk * DK + h * DV + 16 * NW * wv + li;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int q = 0; q < NW; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vr[ks][q][e] = vb[(size_t)(32 * ks + 8 * lk + e) * C + 16 * q];
     tk.store_split(Ks);
-    tq.store_split(QV);
+    tq.store_split(Qs);
   }
   if (tid < kC) {
     Gs[tid] = tid < nt ? glog[(size_t)(jb + tid) * Hv + h] : 0.f;
@@ -334,7 +362,7 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   //    on split operands (B[k][s] = K[s][k] read as rows of K).
   {
     const bool qk = (wv & 1) != 0;
-    const char* Asrc = qk ? QV : Ks;
+    const char* Asrc = qk ? Qs : Ks;
 #pragma unroll
     for (int it = 0; it < 5; ++it) {
       const int x = 2 * it + (wv >> 1);
@@ -350,7 +378,7 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
         const int t = 16 * ti + 4 * lk + r, s = 16 * tj + li;
         const float dec = expf(Gs[t] - Gs[s < t ? s : t]);
         if (!qk)
-          As[sw<kC>(t, s)] = s < t ? Bs[t] * dec * acc[r] : 0.f;
+          As[as_off(t, s)] = s < t ? Bs[t] * dec * acc[r] : 0.f;
         else if (t < nt) {
           uint16_t hi, lo;
           split1(s <= t ? dec * acc[r] : 0.f, hi, lo);
@@ -364,7 +392,7 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   lds_barrier();
   // 4. T = (I + A)^{-1} in 16x16 blocks.  Wave w inverts diagonal block w by
   //    forward substitution (lane j of each 16 solves column j) and clears
-  //    T's blocks right of it; the values replace the queries meanwhile.
+  //    T's blocks right of it; T replaces the queries.
   {
     const int b0 = 16 * wv;
     float X[16];
@@ -373,7 +401,7 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
       float x0 = (t == li) ? 1.f : 0.f, x1 = 0.f;
 #pragma unroll
       for (int g = 0; g < (t + 3) / 4; ++g) {
-        const v4f a = ld4<kC>(As, b0 + t, b0 + 4 * g);
+        const v4f a = *reinterpret_cast<const v4f*>(As + as_off(b0 + t, b0 + 4 * g));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int s = 4 * g + e;
@@ -392,7 +420,6 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
     for (int cb = wv + 1; cb < 4; ++cb)
       *reinterpret_cast<v4f*>(Tt + sw<kC>(b0 + li, 16 * cb + 4 * lk)) = v4f{0.f, 0.f, 0.f, 0.f};
   }
-  tv.store_split(QV);
   lds_barrier();
   //    Blocks below the diagonal, one diagonal level at a time:
   //    T_ij = -T_ii M with M = sum_{k=j}^{i-1} A_ik T_kj (wave w: j = w).
@@ -402,7 +429,7 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
     if (act) {
       v4f acc = {0.f, 0.f, 0.f, 0.f};
       for (int k = j; k < i; ++k) {
-        const v4f a = ld4<kC>(As, 16 * i + li, 16 * k + 4 * lk);
+        const v4f a = *reinterpret_cast<const v4f*>(As + as_off(16 * i + li, 16 * k + 4 * lk));
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           acc = mfma4(a[e], Tt[sw<kC>(16 * k + 4 * lk + e, 16 * j + li)], acc);
@@ -425,16 +452,25 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   //    scaled T as rows, K and V as columns.  Wave w computes column tiles
   //    NW*w .. NW*w+NW-1 for every token tile; tokens 32..63 feed token
   //    tiles 2 and 3 only (T is lower triangular).
+  //    The scaled T overwrites T: every thread reads its part first.
+  {
+    constexpr int kPer = kC * kC / 4 / 256;
+    v4f tr4[kPer];
 #pragma unroll
-  for (int i = 0; i < kC * kC / 4 / 256; ++i) {
-    const int e = (i * 256 + tid) * 4, r = e / kC, cc = e - r * kC;
-    const v4f tv4 = ld4<kC>(Tt, r, cc);
-    store_split4<kC>(TG, r, cc, tv4 * *reinterpret_cast<const v4f*>(BG + cc));
-    store_split4<kC>(TB, r, cc, tv4 * *reinterpret_cast<const v4f*>(Bs + cc));
+    for (int i = 0; i < kPer; ++i) {
+      const int e = (i * 256 + tid) * 4, r = e / kC, cc = e - r * kC;
+      tr4[i] = ld4<kC>(Tt, r, cc);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = (i * 256 + tid) * 4, r = e / kC, cc = e - r * kC;
+      store_split4<kC>(TG, r, cc, tr4[i] * *reinterpret_cast<const v4f*>(BG + cc));
+      store_split4<kC>(TB, r, cc, tr4[i] * *reinterpret_cast<const v4f*>(Bs + cc));
+    }
   }
   lds_barrier();
   {
-    constexpr int NW = DK / 64;
     v4f aw[4][NW], au[4][NW];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
@@ -449,7 +485,13 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
 #pragma unroll
       for (int q = 0; q < NW; ++q) {
         kb[ks][q] = frag_cols<DK>(Ks, ks, NW * wv + q, li, lk);
-        vb[ks][q] = frag_cols<DK>(QV, ks, NW * wv + q, li, lk);
+        v4f v0, v1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v0[e] = 32 * ks + 8 * lk + e < nt ? vr[ks][q][e] : 0.f;
+          v1[e] = 32 * ks + 8 * lk + 4 + e < nt ? vr[ks][q][4 + e] : 0.f;
+        }
+        vb[ks][q] = split8(v0, v1);
       }
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
