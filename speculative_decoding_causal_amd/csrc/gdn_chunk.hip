@@ -181,9 +181,11 @@ __device__ __forceinline__ PRow prow(const PrefillArgs& p, int row) {
 // Rows of ROWS x COLS floats gathered in one batch of float4 loads, then
 // written to LDS.  Thread x loads row x*4/COLS + i*NT*4/COLS of the tile:
 // one uniform base per i and one 32-bit lane offset.  Rows >= nrow are
-// loaded too and dropped (zeros kept): every array read this way holds a
-// chunk of padding rows past its last token, so the loads stay inside it,
-// and no load sits behind a branch.
+// loaded too and written as zeros: every array read this way holds a chunk
+// of padding rows past its last token, so the loads stay inside it.  No
+// load sits behind a branch and no value is tested before it is stored
+// (vector loads complete in order, so either would wait for every load
+// issued before it).
 template <int ROWS, int COLS, int NT = 256>
 struct Tile4 {
   static_assert((ROWS * COLS / 4) % NT == 0 && (NT * 4) % COLS == 0, "tile shape");
@@ -191,52 +193,45 @@ struct Tile4 {
   static constexpr int kRowStep = NT * 4 / COLS;     // rows between them
   v4f v[kPer];
   // base: row 0, column 0 of the tile (uniform); pitch: floats per row
-  __device__ __forceinline__ void load(const float* base, int pitch, int nrow) {
+  __device__ __forceinline__ void load(const float* base, int pitch) {
     const int r0 = (int)threadIdx.x * 4 / COLS, c0 = (int)threadIdx.x * 4 % COLS;
     const unsigned off = (unsigned)(r0 * pitch + c0);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const float* bi = base + (size_t)(i * kRowStep) * pitch;
-      const v4f x = *reinterpret_cast<const v4f*>(bi + off);
-      v[i] = r0 + i * kRowStep < nrow ? x : v4f{0.f, 0.f, 0.f, 0.f};
+      v[i] = *reinterpret_cast<const v4f*>(bi + off);
     }
   }
-  // swizzled tile of row length COLS
-  __device__ __forceinline__ void store_sw(float* lds) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int e = (i * NT + (int)threadIdx.x) * 4;
-      const int r = e / COLS, c = e - r * COLS;
-      *reinterpret_cast<v4f*>(lds + sw<COLS>(r, c)) = v[i];
-    }
+  __device__ __forceinline__ v4f row_or_zero(int i, int r, int nrow) const {
+    return r < nrow ? v[i] : v4f{0.f, 0.f, 0.f, 0.f};
   }
   // fp32 tile split into a split tile of row length COLS
-  __device__ __forceinline__ void store_split(char* lds) const {
+  __device__ __forceinline__ void store_split(char* lds, int nrow) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int e = (i * NT + (int)threadIdx.x) * 4;
       const int r = e / COLS, c = e - r * COLS;
-      store_split4<COLS>(lds, r, c, v[i]);
+      store_split4<COLS>(lds, r, c, row_or_zero(i, r, nrow));
     }
   }
   // tile already split (a row of COLS floats' bytes holds COLS hi then COLS
   // lo bf16 values), copied as it is into a split tile of row length COLS
-  __device__ __forceinline__ void store_raw_split(char* lds) const {
+  __device__ __forceinline__ void store_raw_split(char* lds, int nrow) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int e = (i * NT + (int)threadIdx.x) * 4;
       const int r = e / COLS, c = e - r * COLS;
-      *reinterpret_cast<v4f*>(lds + sp_off<COLS>(r, 2 * c)) = v[i];
+      *reinterpret_cast<v4f*>(lds + sp_off<COLS>(r, 2 * c)) = row_or_zero(i, r, nrow);
     }
   }
   // row-major tile with row pitch PITCH (a multiple of 4)
   template <int PITCH>
-  __device__ __forceinline__ void store_pitched(float* lds) const {
+  __device__ __forceinline__ void store_pitched(float* lds, int nrow) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int e = (i * NT + (int)threadIdx.x) * 4;
       const int r = e / COLS, c = e - r * COLS;
-      *reinterpret_cast<v4f*>(lds + r * PITCH + c) = v[i];
+      *reinterpret_cast<v4f*>(lds + r * PITCH + c) = row_or_zero(i, r, nrow);
     }
   }
 };
@@ -313,11 +308,17 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   //    are padding, read and dropped where used)
   constexpr int NW = DK / 64;
   float vr[2][NW][8];
+  float g_in = 0.f, b_in = 0.f;  // log-decay and beta of token tid (tid < kC)
+  if (tid < kC) {
+    const size_t gi = (size_t)(jb + min(tid, nt - 1)) * Hv + h;
+    g_in = glog[gi];
+    b_in = gbeta[gi];
+  }
   {
     Tile4<kC, DK> tk, tq;
     const float* yb = y + (size_t)jb * C;
-    tk.load(yb + Hk * DK + ih * DK, C, nt);
-    tq.load(yb + ih * DK, C, nt);
+    tk.load(yb + Hk * DK + ih * DK, C);
+    tq.load(yb + ih * DK, C);
     const float* vb = yb + 2 * Hk * DK + h * DV + 16 * NW * wv + li;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -325,12 +326,13 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
       for (int q = 0; q < NW; ++q)
 #pragma unroll
         for (int e = 0; e < 8; ++e) vr[ks][q][e] = vb[(size_t)(32 * ks + 8 * lk + e) * C + 16 * q];
-    tk.store_split(Ks);
-    tq.store_split(Qs);
+    __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first use
+    tk.store_split(Ks, nt);
+    tq.store_split(Qs, nt);
   }
   if (tid < kC) {
-    Gs[tid] = tid < nt ? glog[(size_t)(jb + tid) * Hv + h] : 0.f;
-    Bs[tid] = tid < nt ? gbeta[(size_t)(jb + tid) * Hv + h] : 0.f;
+    Gs[tid] = tid < nt ? g_in : 0.f;
+    Bs[tid] = tid < nt ? b_in : 0.f;
   }
   // P is zero right of its diagonal blocks: 16-byte piece g of a split row
   // holds columns 8 (g mod 8) .. +7 (hi for g < 8, lo after)
@@ -599,37 +601,38 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   Tile4<kC, kC, NT> tp;
   Tile4<kC, RB, NT> tu;
   float tg;     // G of token lane % 64
-  int tx[4];    // global rows of this lane's output tokens (-1: none)
+  int tx[4];    // global rows of this lane's output tokens (tested where used)
   auto gather = [&](int c) {
     const int jb = pr.j0 + c * kC;
     const int nt = min(kC, pr.T - c * kC);
     const float* yb = y + (size_t)jb * C;
-    tw.load(ws.W + ((size_t)jb * Hv + h) * DK, Hv * DK, nt);
-    tq.load(yb + ih * DK, C, nt);
-    tk.load(yb + Hk * DK + ih * DK, C, nt);
-    tp.load(ws.P + ((size_t)jb * Hv + h) * kC, Hv * kC, nt);
-    tu.load(ws.U + ((size_t)jb * Hv + h) * DV + RB * blk, Hv * DV, nt);
+    tw.load(ws.W + ((size_t)jb * Hv + h) * DK, Hv * DK);
+    tq.load(yb + ih * DK, C);
+    tk.load(yb + Hk * DK + ih * DK, C);
+    tp.load(ws.P + ((size_t)jb * Hv + h) * kC, Hv * kC);
+    tu.load(ws.U + ((size_t)jb * Hv + h) * DV + RB * blk, Hv * DV);
     tg = ws.G[(size_t)(jb + min(lane, nt - 1)) * Hv + h];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = 16 * tt + 4 * lk + r;
-      const int j = jb + min(t, nt - 1);
-      const int gr = p.tix ? p.tix[j] : j;
-      tx[r] = (t < nt && gr >= 0 && gr < p.num_actual_tokens) ? gr : -1;
+      const int j = jb + min(16 * tt + 4 * lk + r, nt - 1);
+      tx[r] = p.tix ? p.tix[j] : j;
     }
   };
   gather(0);
   for (int c = 0; c < nch; ++c) {
     const int nt = min(kC, pr.T - c * kC);
-    tw.store_raw_split(Wl);
-    tq.store_split(Ql);
-    tk.store_split(Kl);
-    tp.store_raw_split(Pl);
-    tu.template store_pitched<UP>(Ul);
+    tw.store_raw_split(Wl, nt);
+    tq.store_split(Ql, nt);
+    tk.store_split(Kl, nt);
+    tp.store_raw_split(Pl, nt);
+    tu.template store_pitched<UP>(Ul, nt);
     if (tid < kC) Gc[tid] = tg;
     int orow[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) orow[r] = tx[r];
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * tt + 4 * lk + r;
+      orow[r] = (t < nt && tx[r] >= 0 && tx[r] < p.num_actual_tokens) ? tx[r] : -1;
+    }
 #pragma unroll
     for (int q = 0; q < TPW; ++q)
 #pragma unroll
