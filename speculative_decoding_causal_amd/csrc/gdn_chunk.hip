@@ -33,8 +33,8 @@
 // hi = bf16(x) and lo = bf16(x - hi); a product is hi*hi + hi*lo + lo*hi in
 // fp32 accumulation, about 2^-16 relative error per term where one fp32
 // product has 2^-24, at a sixteenth of the fp32 MFMA's cycles per term.
-// chunk_prep writes W and P already split: a row of n floats holds n bf16
-// hi values, then n bf16 lo values.
+// Every tile arrives split: a row of n floats holds n bf16 hi values, then
+// n bf16 lo values (q and k from the conv kernel, W and P from chunk_prep).
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -56,17 +56,6 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Split of a float pair, two bf16 per word (element 0 in the low half).
-struct Split2 {
-  unsigned hi, lo;
-};
-__device__ __forceinline__ Split2 split2(float x0, float x1) {
-  const v2bf h = {(__bf16)x0, (__bf16)x1};
-  const unsigned hb = __builtin_bit_cast(unsigned, h);
-  const v2bf l = {(__bf16)(x0 - __uint_as_float(hb << 16)),
-                  (__bf16)(x1 - __uint_as_float(hb & 0xffff0000u))};
-  return {hb, __builtin_bit_cast(unsigned, l)};
-}
 __device__ __forceinline__ void split1(float x, uint16_t& hi, uint16_t& lo) {
   const __bf16 h = (__bf16)x;
   hi = __builtin_bit_cast(uint16_t, h);
@@ -205,15 +194,6 @@ struct Tile4 {
   __device__ __forceinline__ v4f row_or_zero(int i, int r, int nrow) const {
     return r < nrow ? v[i] : v4f{0.f, 0.f, 0.f, 0.f};
   }
-  // fp32 tile split into a split tile of row length COLS
-  __device__ __forceinline__ void store_split(char* lds, int nrow) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int e = (i * NT + (int)threadIdx.x) * 4;
-      const int r = e / COLS, c = e - r * COLS;
-      store_split4<COLS>(lds, r, c, row_or_zero(i, r, nrow));
-    }
-  }
   // tile already split (a row of COLS floats' bytes holds COLS hi then COLS
   // lo bf16 values), copied as it is into a split tile of row length COLS
   __device__ __forceinline__ void store_raw_split(char* lds, int nrow) const {
@@ -224,14 +204,24 @@ struct Tile4 {
       *reinterpret_cast<v4f*>(lds + sp_off<COLS>(r, 2 * c)) = row_or_zero(i, r, nrow);
     }
   }
-  // row-major tile with row pitch PITCH (a multiple of 4)
-  template <int PITCH>
-  __device__ __forceinline__ void store_pitched(float* lds, int nrow) const {
+  // the same with every row kept (rows past the tokens only reach results
+  // that are dropped)
+  __device__ __forceinline__ void store_raw_split(char* lds) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int e = (i * NT + (int)threadIdx.x) * 4;
       const int r = e / COLS, c = e - r * COLS;
-      *reinterpret_cast<v4f*>(lds + r * PITCH + c) = row_or_zero(i, r, nrow);
+      *reinterpret_cast<v4f*>(lds + sp_off<COLS>(r, 2 * c)) = v[i];
+    }
+  }
+  // row-major tile with row pitch PITCH (a multiple of 4)
+  template <int PITCH>
+  __device__ __forceinline__ void store_pitched(float* lds) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = (i * NT + (int)threadIdx.x) * 4;
+      const int r = e / COLS, c = e - r * COLS;
+      *reinterpret_cast<v4f*>(lds + r * PITCH + c) = v[i];
     }
   }
 };
@@ -327,8 +317,8 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
 #pragma unroll
         for (int e = 0; e < 8; ++e) vr[ks][q][e] = vb[(size_t)(32 * ks + 8 * lk + e) * C + 16 * q];
     __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first use
-    tk.store_split(Ks, nt);
-    tq.store_split(Qs, nt);
+    tk.store_raw_split(Ks, nt);  // K's padding rows would reach W through 0 * x
+    tq.store_raw_split(Qs);
   }
   if (tid < kC) {
     Gs[tid] = tid < nt ? g_in : 0.f;
@@ -541,10 +531,10 @@ struct StateLds {
   static constexpr int pl = kl + kC * DK * 4;         // [kC] split rows of P (row operand)
   static constexpr int ul = pl + kC * kC * 4;         // [kC][UP] fp32 U~ block (plain)
   static constexpr int ss = ul + kC * UP * 4;         // [RB][DK] fp32 state block
-  static constexpr int ut = ss + RB * DK * 4;         // [RB][kC] fp32 U^T block
-  static constexpr int gc = ut + RB * kC * 4;         // [kC] G
-  static constexpr int fs = gc + kC * 4;              // [kC] e^{G_C - G_t}
-  static constexpr int total = fs + kC * 4;
+  static constexpr int ut = ss + RB * DK * 4;         // [RB] split rows of U^T
+  static constexpr int uf = ut + RB * kC * 4;         // [RB] split rows of U^T diag(F)
+  static constexpr int gc = uf + RB * kC * 4;         // [kC] G
+  static constexpr int total = gc + kC * 4;
 };
 
 constexpr int kStateThreads = 512;  // 8 waves, two per SIMD
@@ -570,9 +560,9 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   char* Pl = smb + Lay::pl;
   float* Ul = reinterpret_cast<float*>(smb + Lay::ul);
   float* Ss = reinterpret_cast<float*>(smb + Lay::ss);
-  float* UT = reinterpret_cast<float*>(smb + Lay::ut);
+  char* UTs = smb + Lay::ut;
+  char* UFs = smb + Lay::uf;
   float* Gc = reinterpret_cast<float*>(smb + Lay::gc);
-  float* Fs = reinterpret_cast<float*>(smb + Lay::fs);
 
   const int Hv = p.Hv, Hk = p.Hk, C = p.C;
   const int row = blockIdx.x / Hv, h = head_of(blockIdx.x - row * Hv, Hv);
@@ -595,8 +585,8 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
                          : 0.f;
 
   const int nch = (pr.T + kC - 1) / kC;
-  // Operands of chunk c+1 are gathered while chunk c is computed (W and P
-  // arrive split, Q and K are split on their way to LDS).
+  // Operands of chunk c+1 are gathered while chunk c is computed; W, P, Q
+  // and K arrive split.
   Tile4<kC, DK, NT> tw, tq, tk;
   Tile4<kC, kC, NT> tp;
   Tile4<kC, RB, NT> tu;
@@ -621,11 +611,14 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   gather(0);
   for (int c = 0; c < nch; ++c) {
     const int nt = min(kC, pr.T - c * kC);
-    tw.store_raw_split(Wl, nt);
-    tq.store_split(Ql, nt);
-    tk.store_split(Kl, nt);
-    tp.store_raw_split(Pl, nt);
-    tu.template store_pitched<UP>(Ul, nt);
+    // Rows past the chunk's tokens reach only dropped results (U and the
+    // outputs are tested per token), except through K: 0 * x there would
+    // carry a NaN of padding rows into the state.
+    tw.store_raw_split(Wl);
+    tq.store_raw_split(Ql);
+    tk.store_raw_split(Kl, nt);
+    tp.store_raw_split(Pl);
+    tu.template store_pitched<UP>(Ul);
     if (tid < kC) Gc[tid] = tg;
     int orow[4];
 #pragma unroll
@@ -641,7 +634,6 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
     lds_barrier();
 
     const float gC = Gc[kC - 1];
-    if (tid < kC) Fs[tid] = expf(gC - Gc[tid]);
     // B operand of the S0^T products: S0[j][k], j = 16 jt + li, k in the
     // lane's 8-runs of each k-step
     Frag sb[KS];
@@ -649,39 +641,36 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
     for (int ks = 0; ks < KS; ++ks)
       sb[ks] = split8(ld4<DK>(Ss, 16 * jt + li, 32 * ks + 8 * lk),
                       ld4<DK>(Ss, 16 * jt + li, 32 * ks + 8 * lk + 4));
-    // (a) U = U~ - W S0^T on (token tile tt, row tile jt), kept as U^T
+    // (a) U = U~ - W S0^T on (token tile tt, row tile jt), kept split as
+    //     U^T (B operand of P U) and U^T diag(F), F_t = e^{G_C - G_t} (A
+    //     operand of the update)
     {
       v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) acc = mfma3(frag_rows<DK>(Wl, 16 * tt + li, ks, lk), sb[ks], acc);
-      v4f u;
+      const int t0 = 16 * tt + 4 * lk;
+      v4f u, f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tt + 4 * lk + r;
-        u[r] = t < nt ? Ul[t * UP + 16 * jt + li] - acc[r] : 0.f;
+        u[r] = t0 + r < nt ? Ul[(t0 + r) * UP + 16 * jt + li] - acc[r] : 0.f;
+        f[r] = expf(gC - Gc[t0 + r]);
       }
-      *reinterpret_cast<v4f*>(UT + sw<kC>(16 * jt + li, 16 * tt + 4 * lk)) = u;
+      store_split4<kC>(UTs, 16 * jt + li, t0, u);
+      store_split4<kC>(UFs, 16 * jt + li, t0, u * f);
     }
     lds_barrier();
     // the next chunk's operands load during (b) and (c)
     if (c + 1 < nch) gather(c + 1);
 
-    // U^T[j][s] for j = 16 jt + li and the lane's 8-runs of tokens: the B
-    // operand of P U and, scaled by F, the A operand of the update
-    v4f ur[2][2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      ur[ks][0] = ld4<kC>(UT, 16 * jt + li, 32 * ks + 8 * lk);
-      ur[ks][1] = ld4<kC>(UT, 16 * jt + li, 32 * ks + 8 * lk + 4);
-    }
     // (b) outputs on (tt, jt): e^{G_t} (Q S0^T)[t] + (P U)[t]; P is zero
     //     right of the diagonal block, so tokens 32..63 matter from tt = 2 on
     {
       v4f aq = {0.f, 0.f, 0.f, 0.f}, ap = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) aq = mfma3(frag_rows<DK>(Ql, 16 * tt + li, ks, lk), sb[ks], aq);
-      ap = mfma3(frag_rows<kC>(Pl, 16 * tt + li, 0, lk), split8(ur[0][0], ur[0][1]), ap);
-      if (tt >= 2) ap = mfma3(frag_rows<kC>(Pl, 16 * tt + li, 1, lk), split8(ur[1][0], ur[1][1]), ap);
+      ap = mfma3(frag_rows<kC>(Pl, 16 * tt + li, 0, lk), frag_rows<kC>(UTs, 16 * jt + li, 0, lk), ap);
+      if (tt >= 2)
+        ap = mfma3(frag_rows<kC>(Pl, 16 * tt + li, 1, lk), frag_rows<kC>(UTs, 16 * jt + li, 1, lk), ap);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tt + 4 * lk + r;
@@ -693,13 +682,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
 
     // (c) S = e^{G_C} S0 + U^T diag(e^{G_C - G_t}) K on this wave's tiles
     {
-      Frag ua[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const v4f f0 = *reinterpret_cast<const v4f*>(Fs + 32 * ks + 8 * lk);
-        const v4f f1 = *reinterpret_cast<const v4f*>(Fs + 32 * ks + 8 * lk + 4);
-        ua[ks] = split8(ur[ks][0] * f0, ur[ks][1] * f1);
-      }
+      const Frag ua[2] = {frag_rows<kC>(UFs, 16 * jt + li, 0, lk), frag_rows<kC>(UFs, 16 * jt + li, 1, lk)};
       const float eC = expf(gC);
 #pragma unroll
       for (int q = 0; q < TPW; ++q) {

@@ -96,4 +96,19 @@ __device__ __forceinline__ int clampi(int v, int lo, int hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }
 
+// A float pair split into bf16 pairs, x = hi + lo + O(2^-17 |x|) with
+// hi = bf16(x) and lo = bf16(x - hi); two values per word, the first in the
+// low half.  The operands of the chunked prefill's bf16 products.
+struct Split2 {
+  unsigned hi, lo;
+};
+__device__ __forceinline__ Split2 split2(float x0, float x1) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  const v2bf h = {(__bf16)x0, (__bf16)x1};
+  const unsigned hb = __builtin_bit_cast(unsigned, h);
+  const v2bf l = {(__bf16)(x0 - __uint_as_float(hb << 16)),
+                  (__bf16)(x1 - __uint_as_float(hb & 0xffff0000u))};
+  return {hb, __builtin_bit_cast(unsigned, l)};
+}
+
 }  // namespace gdn

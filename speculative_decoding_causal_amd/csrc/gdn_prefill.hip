@@ -7,7 +7,8 @@
 //   1. conv_prefill: one thread per (4 channels, 16 tokens of a row)
 //      slides the width-W window along the row and writes the fp32 conv
 //      output to the workspace at the token's non-spec stream index, q and
-//      k L2-normalised (q scaled) by a reduction over the lanes of a head;
+//      k L2-normalised (q scaled) by a reduction over the lanes of a head
+//      and, for the chunked form, split into bf16 hi and lo values;
 //      the workgroups of a unit also evaluate the gates of every v-head at
 //      the token's global row (log-decay and beta).  The thread of the
 //      row's first tokens is the only one that reads the ring history and
@@ -349,8 +350,17 @@ conv_prefill_kernel(PrefillArgs p, float* __restrict__ y, float* __restrict__ ga
 #pragma unroll
       for (int e = 0; e < kCh; ++e) o[e] *= f;
     }
-    *reinterpret_cast<float4*>(y + (size_t)(pr.j0 + t) * C + c) =
-        make_float4(o[0], o[1], o[2], o[3]);
+    float* yrow = y + (size_t)(pr.j0 + t) * C;
+    if (DK >= 64 && c < 2 * p.Hk * DK) {
+      // q and k of the chunked form leave split: a head's DK floats hold
+      // its DK hi then its DK lo bf16 values
+      const Split2 s0 = split2(o[0], o[1]), s1 = split2(o[2], o[3]);
+      unsigned* hb = reinterpret_cast<unsigned*>(yrow + (c / DK) * DK) + (c % DK) / 2;
+      *reinterpret_cast<u32x2*>(hb) = u32x2{s0.hi, s1.hi};
+      *reinterpret_cast<u32x2*>(hb + DK / 2) = u32x2{s0.lo, s1.lo};
+    } else {
+      *reinterpret_cast<float4*>(yrow + c) = make_float4(o[0], o[1], o[2], o[3]);
+    }
     // slide the window: drop the oldest sample, append x_t
 #pragma unroll
     for (int m = 0; m < kMaxWidth - 2; ++m)
