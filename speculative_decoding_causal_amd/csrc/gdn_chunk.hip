@@ -43,6 +43,7 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kC = 64;  // tokens per chunk
+constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -368,7 +369,7 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * ti + 4 * lk + r, s = 16 * tj + li;
-        const float dec = expf(Gs[t] - Gs[s < t ? s : t]);
+        const float dec = __builtin_amdgcn_exp2f((Gs[t] - Gs[s < t ? s : t]) * kLog2e);
         if (!qk)
           As[as_off(t, s)] = s < t ? Bs[t] * dec * acc[r] : 0.f;
         else if (t < nt) {
@@ -530,7 +531,7 @@ struct StateLds {
   static constexpr int kl = ql + kC * DK * 4;         // [kC] split rows of K (column operand)
   static constexpr int pl = kl + kC * DK * 4;         // [kC] split rows of P (row operand)
   static constexpr int ul = pl + kC * kC * 4;         // [kC][UP] fp32 U~ block (plain)
-  static constexpr int ss = ul + kC * UP * 4;         // [RB][DK] fp32 state block
+  static constexpr int ss = ul + kC * UP * 4;         // [RB] split rows of S0
   static constexpr int ut = ss + RB * DK * 4;         // [RB] split rows of U^T
   static constexpr int uf = ut + RB * kC * 4;         // [RB] split rows of U^T diag(F)
   static constexpr int gc = uf + RB * kC * 4;         // [kC] G
@@ -559,7 +560,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   char* Kl = smb + Lay::kl;
   char* Pl = smb + Lay::pl;
   float* Ul = reinterpret_cast<float*>(smb + Lay::ul);
-  float* Ss = reinterpret_cast<float*>(smb + Lay::ss);
+  char* Ss = smb + Lay::ss;
   char* UTs = smb + Lay::ut;
   char* UFs = smb + Lay::uf;
   float* Gc = reinterpret_cast<float*>(smb + Lay::gc);
@@ -619,18 +620,29 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
     tk.store_raw_split(Kl, nt);
     tp.store_raw_split(Pl);
     tu.template store_pitched<UP>(Ul);
-    if (tid < kC) Gc[tid] = tg;
+    if (tid < kC) Gc[tid] = tg * kLog2e;  // G in log2 units
     int orow[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * tt + 4 * lk + r;
       orow[r] = (t < nt && tx[r] >= 0 && tx[r] < p.num_actual_tokens) ? tx[r] : -1;
     }
+    // S0 split: lanes 2m and 2m+1 hold adjacent columns of a row; the even
+    // lane writes their hi pair, the odd lane their lo pair
 #pragma unroll
     for (int q = 0; q < TPW; ++q)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        Ss[sw<DK>(16 * jt + 4 * lk + r, 16 * (TPW * tt + q) + li)] = St[q][r];
+      for (int r = 0; r < 4; ++r) {
+        uint16_t hs, ls;
+        split1(St[q][r], hs, ls);
+        const unsigned hv = hs, lv = ls;
+        const unsigned hp = (unsigned)__builtin_amdgcn_mov_dpp((int)hv, 0xB1, 0xF, 0xF, false);
+        const unsigned lp = (unsigned)__builtin_amdgcn_mov_dpp((int)lv, 0xB1, 0xF, 0xF, false);
+        const int row = 16 * jt + 4 * lk + r, col = 16 * (TPW * tt + q) + li;
+        const bool odd = (li & 1) != 0;
+        *reinterpret_cast<unsigned*>(Ss + sp_off<DK>(row, odd ? DK + col - 1 : col)) =
+            odd ? (lp | (lv << 16)) : (hv | (hp << 16));
+      }
     lds_barrier();
 
     const float gC = Gc[kC - 1];
@@ -638,9 +650,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
     // lane's 8-runs of each k-step
     Frag sb[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      sb[ks] = split8(ld4<DK>(Ss, 16 * jt + li, 32 * ks + 8 * lk),
-                      ld4<DK>(Ss, 16 * jt + li, 32 * ks + 8 * lk + 4));
+    for (int ks = 0; ks < KS; ++ks) sb[ks] = frag_rows<DK>(Ss, 16 * jt + li, ks, lk);
     // (a) U = U~ - W S0^T on (token tile tt, row tile jt), kept split as
     //     U^T (B operand of P U) and U^T diag(F), F_t = e^{G_C - G_t} (A
     //     operand of the update)
@@ -653,7 +663,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         u[r] = t0 + r < nt ? Ul[(t0 + r) * UP + 16 * jt + li] - acc[r] : 0.f;
-        f[r] = expf(gC - Gc[t0 + r]);
+        f[r] = __builtin_amdgcn_exp2f(gC - Gc[t0 + r]);
       }
       store_split4<kC>(UTs, 16 * jt + li, t0, u);
       store_split4<kC>(UFs, 16 * jt + li, t0, u * f);
@@ -676,14 +686,14 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
         const int t = 16 * tt + 4 * lk + r;
         if (orow[r] >= 0)
           p.out[((size_t)orow[r] * Hv + h) * DV + RB * blk + 16 * jt + li] =
-              f2bf(fmaf(expf(Gc[t]), aq[r], ap[r]));
+              f2bf(fmaf(__builtin_amdgcn_exp2f(Gc[t]), aq[r], ap[r]));
       }
     }
 
     // (c) S = e^{G_C} S0 + U^T diag(e^{G_C - G_t}) K on this wave's tiles
     {
       const Frag ua[2] = {frag_rows<kC>(UFs, 16 * jt + li, 0, lk), frag_rows<kC>(UFs, 16 * jt + li, 1, lk)};
-      const float eC = expf(gC);
+      const float eC = __builtin_amdgcn_exp2f(gC);
 #pragma unroll
       for (int q = 0; q < TPW; ++q) {
         const int mt = TPW * tt + q;
