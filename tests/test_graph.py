@@ -7,7 +7,9 @@ Reading: a step is captured once at padded shapes (scalars are frozen in the
 graph) and replayed with batches of fewer real rows.  Pad rows carry NULL (0)
 slots and their tokens sit in rows past the real ones, so they read and write
 no pool; the real rows must equal an eager call on the unpadded batch bit for
-bit, replay after replay, with eager work between the replays."""
+bit, replay after replay, with eager work between the replays.  Prefill rows
+keep a fixed row count and token budget: the last prefill row is a pad row
+that takes the tokens the real rows leave over."""
 from __future__ import annotations
 
 import numpy as np
@@ -22,43 +24,65 @@ pytestmark = [pytest.mark.gpu,
 
 Hk, Hv, DK, K, SLOTS = 4, 8, 128, 3, 96
 NS_PAD, ND_PAD = 8, 6
+NP_PAD, PF_TOK = 3, 200  # prefill rows (the last one pads) and their token budget
 
 
-def scenario(seed, ns, nd):
-    """Padded metadata for ns real spec rows and nd real decodes, and the
+def scenario(seed, ns, nd, pf=None):
+    """Padded metadata for ns real spec rows, nd real decodes and (with pf,
+    a list of at most NP_PAD - 1 lengths) real prefill rows, and the
     unpadded case with the same real rows."""
     rng = np.random.default_rng(seed)
-    t_pad = ND_PAD + NS_PAD * K
-    t_real = nd + ns * K
+    pf = None if pf is None else list(pf)
+    npf, pf_real = (0, 0) if pf is None else (NP_PAD, sum(pf))
+    pf_tok = PF_TOK if pf is not None else 0
+    t_pad = ND_PAD + pf_tok + NS_PAD * K
+    t_real = nd + pf_real + ns * K
     case = helpers.small_case(seed=seed, Hk=Hk, Hv=Hv, dk=DK, dv=DK, K=K, T=t_pad,
                               num_slots=SLOTS)
-    slots = rng.choice(np.arange(1, SLOTS), ns * K + nd, replace=False).astype(np.int32)
+    n_pf_rows = 0 if pf is None else len(pf)
+    slots = rng.choice(np.arange(1, SLOTS), ns * K + nd + n_pf_rows,
+                       replace=False).astype(np.int32)
     rows = rng.permutation(t_real).astype(np.int32)      # real tokens -> rows [0, t_real)
     pad_rows = np.arange(t_real, t_pad, dtype=np.int32)  # pad tokens -> rows past them
+    spec_rows, dec_rows, pf_rows = rows[:ns * K], rows[ns * K:ns * K + nd], rows[ns * K + nd:]
+    spec_pad = pad_rows[:(NS_PAD - ns) * K]
+    dec_pad = pad_rows[(NS_PAD - ns) * K:(NS_PAD - ns) * K + ND_PAD - nd]
+    pf_pad = pad_rows[(NS_PAD - ns) * K + ND_PAD - nd:]
     # spec rows
     ssi = np.zeros((NS_PAD, K), np.int32)
     ssi[:ns] = slots[:ns * K].reshape(ns, K)
     nacc = np.ones(NS_PAD, np.int32)
     nacc[:ns] = rng.integers(1, K + 1, ns)
     sqsl = np.arange(0, NS_PAD * K + 1, K, dtype=np.int32)
-    stix = np.concatenate([rows[:ns * K], pad_rows[:(NS_PAD - ns) * K]]).astype(np.int32)
-    # decode rows
-    cache = np.zeros(ND_PAD, np.int32)
-    cache[:nd] = slots[ns * K:]
-    his = np.zeros(ND_PAD, np.uint8)
+    stix = np.concatenate([spec_rows, spec_pad]).astype(np.int32)
+    # non-spec rows: decodes, then the prefill rows (real ones, empty pads,
+    # and a last pad row holding the tokens left over)
+    nrows = ND_PAD + npf
+    cache = np.zeros(nrows, np.int32)
+    cache[:nd] = slots[ns * K:ns * K + nd]
+    cache[ND_PAD:ND_PAD + n_pf_rows] = slots[ns * K + nd:]
+    his = np.zeros(nrows, np.uint8)
     his[:nd] = rng.integers(0, 2, nd)
-    dtix = np.concatenate([rows[ns * K:], pad_rows[(NS_PAD - ns) * K:]]).astype(np.int32)
-    dqsl = np.arange(ND_PAD + 1, dtype=np.int32)
+    his[ND_PAD:ND_PAD + n_pf_rows] = rng.integers(0, 2, n_pf_rows)
+    lens = [1] * ND_PAD
+    if pf is not None:
+        lens += pf + [0] * (NP_PAD - 1 - len(pf)) + [PF_TOK - pf_real]
+    dqsl = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    dtix = np.concatenate([dec_rows, dec_pad, pf_rows, pf_pad]).astype(np.int32)
     padded = dict(sqsl=sqsl, ssi=ssi, nacc=nacc, stix=stix, dqsl=dqsl, cache=cache, his=his,
-                  dtix=dtix, t=t_pad)
+                  dtix=dtix, t=t_pad, npf=npf, pf_tok=pf_tok)
     real = dict(case)
     for k in ("mixed_qkv", "a", "b"):
         real[k] = case[k][:t_real]
     real["num_actual_tokens"] = t_real
     real["spec"] = (helpers.spec_meta(sqsl[:ns + 1], ssi[:ns], nacc[:ns], stix[:ns * K])
                     if ns else None)
-    real["nonspec"] = (helpers.nonspec_meta([1] * nd, cache[:nd], his=his[:nd], tix=dtix[:nd])
-                       if nd else None)
+    rl = [1] * nd + ([] if pf is None else pf)
+    rc = np.concatenate([cache[:nd], cache[ND_PAD:ND_PAD + n_pf_rows]])
+    rh = np.concatenate([his[:nd], his[ND_PAD:ND_PAD + n_pf_rows]])
+    rt = np.concatenate([dec_rows, pf_rows]).astype(np.int32)
+    real["nonspec"] = (helpers.nonspec_meta(rl, rc, his=rh, tix=rt, num_decodes=nd)
+                       if rl else None)
     return case, padded, real
 
 
@@ -69,9 +93,16 @@ class Static:
         self.g = Gpu(case)
         self.cfg = cfg_of(case)
         self.meta = {k: (i32(v) if v.dtype == np.int32 else u8(v))
-                     for k, v in padded.items() if k != "t"}
-        self.t = padded["t"]
+                     for k, v in padded.items() if isinstance(v, np.ndarray)}
+        self.t, self.npf, self.pf_tok = padded["t"], padded["npf"], padded["pf_tok"]
         self.with_decodes = with_decodes
+        self.ws = None
+        if self.npf:
+            import speculative_decoding_causal_amd as gdn
+            d = case["dims"]
+            nbytes = gdn.gdn_workspace_bytes(self.cfg, d["L"], d["num_slots"],
+                                             ND_PAD + self.pf_tok, self.npf)
+            self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
 
     def load(self, case, padded):
         g = self.g
@@ -84,6 +115,7 @@ class Static:
         g.ssm.copy_(f32(case["ssm_state"]))
         for k, t in self.meta.items():
             t.copy_(i32(padded[k]) if padded[k].dtype == np.int32 else u8(padded[k]))
+        assert (padded["npf"], padded["pf_tok"]) == (self.npf, self.pf_tok)
 
     def call(self):
         import speculative_decoding_causal_amd as gdn
@@ -99,10 +131,12 @@ class Static:
                                    num_actual_tokens=NS_PAD * K)
         else:
             gdn.gdn_attention(self.cfg, g.qkv, g.a, g.b, g.w, None, g.A_log, g.dt_bias, g.conv,
-                              g.ssm, g.out, num_decodes=ND_PAD, num_non_spec_tokens=ND_PAD,
+                              g.ssm, g.out, num_decodes=ND_PAD, num_prefills=self.npf,
+                              num_non_spec_tokens=ND_PAD + self.pf_tok,
                               query_start_loc=m["dqsl"],
                               non_spec_state_indices=m["cache"], has_initial_state=m["his"],
-                              non_spec_token_indx=m["dtix"], num_actual_tokens=self.t, **spec)
+                              non_spec_token_indx=m["dtix"], num_actual_tokens=self.t,
+                              workspace=self.ws, **spec)
 
 
 def _run_graph(with_decodes, plan):
@@ -117,11 +151,13 @@ def _run_graph(with_decodes, plan):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         st.call()
-    for seed, ns, nd in plan:
-        case, padded, real = scenario(seed, ns, nd)
+    for step in plan:
+        seed, ns, nd = step[:3]
+        case, padded, real = scenario(*step)
         st.load(case, padded)
         torch.cuda.synchronize()
-        say(f"graph replay: {ns} spec rows, {nd} decodes (padded to {NS_PAD}, {ND_PAD})")
+        pf = f", prefills {step[3]}" if len(step) > 3 else ""
+        say(f"graph replay: {ns} spec rows, {nd} decodes{pf} (padded to {NS_PAD}, {ND_PAD})")
         graph.replay()
         torch.cuda.synchronize()
         eager = Gpu(real)
@@ -143,3 +179,10 @@ def test_graph_padded_spec_replays():
 
 def test_graph_padded_decodes_and_spec_replays():
     _run_graph(True, [(310, 8, 6), (311, 3, 4), (312, 6, 0), (313, 0, 5), (314, 8, 6)])
+
+
+def test_graph_padded_prefills_replays():
+    # decodes + prefill rows (chunked form, dk = 128) + spec rows in one
+    # captured step; the real prefill rows change length replay by replay
+    _run_graph(True, [(330, 8, 6, [130, 64]), (331, 3, 4, [65]), (332, 5, 0, []),
+                      (333, 0, 2, [1, 199]), (334, 8, 6, [200])])
