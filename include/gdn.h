@@ -199,6 +199,10 @@ int gdn_spec_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
  * (GDN_ERR_CONSERVATION); when both streams are non-empty both token_indx
  * tensors are required.  Prefill rows need a workspace of
  * gdn_workspace_bytes(dims, num_non_spec_tokens, num_prefills) bytes.
+ * Launch order: with spec rows, the prefill kernels and then one row kernel
+ * for the spec rows and the decodes together; without, the decodes' row
+ * kernel and then the prefill kernels.  Rows use disjoint slots, so the
+ * order is not observable.
  */
 int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
                   const gdn_bf16* a, const gdn_bf16* b,

@@ -196,7 +196,10 @@ void fill_layer(gdn::RowArgs& r, const Layer& L) {
   r.out = L.out;
 }
 
-int run_spec(const Layer& L, const SpecBatch& s, hipStream_t stream) {
+// Spec rows; `dec` (optional) are decode rows that share the launch, their
+// workgroups after the spec rows' (rows of one call use disjoint slots).
+int run_spec(const Layer& L, const SpecBatch& s, hipStream_t stream,
+             const gdn::RowArgs* dec = nullptr) {
   if (s.num_spec_decodes == 0) return GDN_OK;
   gdn::RowArgs r;
   fill_layer(r, L);
@@ -211,9 +214,22 @@ int run_spec(const Layer& L, const SpecBatch& s, hipStream_t stream) {
   r.nacc = s.nacc;
   r.tix = s.tix;
   r.stage = gdn::kFused;
+  if (dec) {
+    r.more.kind = dec->kind;
+    r.more.num_rows = dec->num_rows;
+    r.more.num_tokens = dec->num_tokens;
+    r.more.row_stride = dec->row_stride;
+    r.more.max_row_tokens = dec->max_row_tokens;
+    r.more.qsl = dec->qsl;
+    r.more.cache_idx = dec->cache_idx;
+    r.more.ssi = dec->ssi;
+    r.more.nacc = dec->nacc;
+    r.more.his = dec->his;
+    r.more.tix = dec->tix;
+  }
   if (int e = lds_ok(r, L.d)) return e;
   return launch(gdn::launch_rows(r, L.d->head_k_dim, L.d->head_v_dim, stream),
-                "spec row kernel");
+                dec ? "spec and decode row kernel" : "spec row kernel");
 }
 
 }  // namespace
@@ -337,20 +353,28 @@ int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
   Layer L{dims, mixed_qkv, a, b, conv_weight, conv_bias, A_log, dt_bias,
           conv_state, ssm_state, core_attn_out, num_actual_tokens};
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // Decode rows share the spec rows' launch when there are both (one grid,
+  // and the decodes' short workgroups fill the spec rows' dispatch tail).
+  gdn::RowArgs dec;
   if (num_decodes > 0) {
-    gdn::RowArgs r;
-    fill_layer(r, L);
-    r.kind = gdn::kNonSpec;
-    r.num_rows = num_decodes;
-    r.num_tokens = num_non_spec_tokens;
-    r.max_row_tokens = 1;
-    r.qsl = query_start_loc;
-    r.cache_idx = non_spec_state_indices;
-    r.his = has_initial_state;
-    r.tix = non_spec_token_indx;
-    r.stage = gdn::kFused;
-    if (int e = lds_ok(r, dims)) return e;
-    if (int e = launch(gdn::launch_rows(r, dims->head_k_dim, dims->head_v_dim, st),
+    fill_layer(dec, L);
+    dec.kind = gdn::kNonSpec;
+    dec.num_rows = num_decodes;
+    dec.num_tokens = num_non_spec_tokens;
+    dec.row_stride = 0;
+    dec.max_row_tokens = 1;
+    dec.qsl = query_start_loc;
+    dec.cache_idx = non_spec_state_indices;
+    dec.ssi = nullptr;
+    dec.nacc = nullptr;
+    dec.his = has_initial_state;
+    dec.tix = non_spec_token_indx;
+    dec.stage = gdn::kFused;
+  }
+  const bool merged = num_decodes > 0 && s.num_spec_decodes > 0;
+  if (num_decodes > 0 && !merged) {
+    if (int e = lds_ok(dec, dims)) return e;
+    if (int e = launch(gdn::launch_rows(dec, dims->head_k_dim, dims->head_v_dim, st),
                        "decode row kernel"))
       return e;
   }
@@ -393,7 +417,7 @@ int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
                        "prefill kernels"))
       return e;
   }
-  return run_spec(L, s, st);
+  return run_spec(L, s, st, merged ? &dec : nullptr);
 }
 
 static int stage_rows(const gdn_dims* dims, const gdn_rows* rows, int num_actual_tokens,

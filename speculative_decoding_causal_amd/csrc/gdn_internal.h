@@ -53,7 +53,24 @@ struct RowArgs {
   const uint8_t* his;
   const int* tix;
   int stage;
+  // A second set of rows in the same launch (none when num_rows is 0): its
+  // rows follow the first set's in the grid, with their own kind and metadata.
+  struct RowSet {
+    int kind = 0, num_rows = 0, num_tokens = 0, row_stride = 0, max_row_tokens = 0;
+    const int* qsl = nullptr;
+    const int* cache_idx = nullptr;
+    const int* ssi = nullptr;
+    const int* nacc = nullptr;
+    const uint8_t* his = nullptr;
+    const int* tix = nullptr;
+  } more;
 };
+
+// Tokens per row the LDS layout of a launch is sized for (both sets).
+__host__ __device__ inline int launch_row_tokens(const RowArgs& a) {
+  return a.more.num_rows > 0 && a.more.max_row_tokens > a.max_row_tokens ? a.more.max_row_tokens
+                                                                          : a.max_row_tokens;
+}
 
 // Rows of at most kMaxRowTokens tokens (spec rows and decodes), one
 // workgroup per (row, k-head): conv + ring roll, gates, norms, recurrence.

@@ -312,7 +312,7 @@ __device__ __forceinline__ void conv_chan(const float (&w)[kMaxWidth], float bia
 // the tokens per row for the register gathers of the conv phase.
 template <int DK, int DV, int R, int NT, int WPE, int LM, int KT, int RB, bool FUSED>
 __global__ void __launch_bounds__(NT, WPE)
-gdn_rows_kernel(RowArgs p) {
+gdn_rows_kernel(RowArgs pa) {
   static_assert(R % RB == 0, "row batch");
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int LPR = DK / 16;    // lanes per state row
@@ -321,12 +321,28 @@ gdn_rows_kernel(RowArgs p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int Hk = p.Hk, G = p.G, C = p.C, L = p.L;
-  const int row = blockIdx.x / Hk;
+  const int Hk = pa.Hk, G = pa.G, C = pa.C, L = pa.L;
+  int row = blockIdx.x / Hk;
   const int ih = blockIdx.x - row * Hk;
   const int NCH = 2 * DK + G * DV;
   const int NR = G * DV;
-  const int Tm = p.max_row_tokens;
+  const int Tm = launch_row_tokens(pa);
+  // rows of the second set take its kind and metadata (uniform selects)
+  RowArgs p = pa;
+  if (row >= pa.num_rows) {
+    row -= pa.num_rows;
+    p.kind = pa.more.kind;
+    p.num_rows = pa.more.num_rows;
+    p.num_tokens = pa.more.num_tokens;
+    p.row_stride = pa.more.row_stride;
+    p.max_row_tokens = pa.more.max_row_tokens;
+    p.qsl = pa.more.qsl;
+    p.cache_idx = pa.more.cache_idx;
+    p.ssi = pa.more.ssi;
+    p.nacc = pa.more.nacc;
+    p.his = pa.more.his;
+    p.tix = pa.more.tix;
+  }
 
   const RowPlan rp = plan_row(p, row);
   const int T = rp.T;
@@ -607,7 +623,7 @@ gdn_rows_kernel(RowArgs p) {
 
 template <int DK, int DV, int R, int NT, int WPE, int LM, int KT>
 hipError_t launch_typed(const RowArgs& a, hipStream_t s) {
-  const Lds lay = lds_layout(DK, DV, a.G, a.L, a.max_row_tokens);
+  const Lds lay = lds_layout(DK, DV, a.G, a.L, launch_row_tokens(a));
   constexpr int RB = DK == 128 ? GDN_ROWS_RB128 : R;
   auto kern = a.stage == kFused ? gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT, RB, true>
                                 : gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT, RB, false>;
@@ -615,7 +631,8 @@ hipError_t launch_typed(const RowArgs& a, hipStream_t s) {
     hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lay.total);
     if (e != hipSuccess) return e;
   }
-  dim3 grid(static_cast<unsigned>(a.num_rows) * static_cast<unsigned>(a.Hk));
+  const int rows = a.num_rows + (a.more.num_rows > 0 ? a.more.num_rows : 0);
+  dim3 grid(static_cast<unsigned>(rows) * static_cast<unsigned>(a.Hk));
   hipLaunchKernelGGL(kern, grid, dim3(NT), lay.total, s, a);
   return hipGetLastError();
 }
@@ -623,19 +640,20 @@ hipError_t launch_typed(const RowArgs& a, hipStream_t s) {
 // Short rows on a short ring take the small register gathers.
 template <int DK, int DV, int R, int NT, int WPE>
 hipError_t launch_sized(const RowArgs& a, hipStream_t s) {
-  if (a.L <= 6 && a.max_row_tokens <= 4) return launch_typed<DK, DV, R, NT, WPE, 6, 4>(a, s);
-  if (a.L <= 8 && a.max_row_tokens <= 4) return launch_typed<DK, DV, R, NT, WPE, 8, 4>(a, s);
+  const int tm = launch_row_tokens(a);
+  if (a.L <= 6 && tm <= 4) return launch_typed<DK, DV, R, NT, WPE, 6, 4>(a, s);
+  if (a.L <= 8 && tm <= 4) return launch_typed<DK, DV, R, NT, WPE, 8, 4>(a, s);
   return launch_typed<DK, DV, R, NT, WPE, kMaxStateLen, kMaxRowTokens>(a, s);
 }
 
 }  // namespace
 
 size_t rows_lds_bytes(const RowArgs& a, int dk, int dv) {
-  return static_cast<size_t>(lds_layout(dk, dv, a.G, a.L, a.max_row_tokens).total);
+  return static_cast<size_t>(lds_layout(dk, dv, a.G, a.L, launch_row_tokens(a)).total);
 }
 
 hipError_t launch_rows(const RowArgs& a, int dk, int dv, hipStream_t s) {
-  if (a.num_rows <= 0) return hipSuccess;
+  if (a.num_rows <= 0 && a.more.num_rows <= 0) return hipSuccess;
   if (dk != dv) return hipErrorInvalidValue;
   switch (dk) {
     case 16: return launch_sized<16, 16, 1, 256, 4>(a, s);
