@@ -190,7 +190,8 @@ int gdn_spec_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
  * c = non_spec_state_indices[i] serves both pools; the history is read when
  * has_initial_state[i] != 0 (all rows when NULL) and c > 0.  The conv window
  * is the ring tail, the ring rolls by T_i, and only the final state is stored
- * (when c > 0).  Prefill rows run the chunked form of the recurrence.
+ * (when c > 0).  Prefill rows run the chunked form of the recurrence; a
+ * prefill row may hold no tokens (it then touches no pool).
  *
  * Spec rows: exactly as gdn_spec_attention.  spec_state_indices and
  * num_accepted_tokens must be given together or not at all (GDN_ERR_SPEC_PAIR).
@@ -274,7 +275,8 @@ int gdn_delta_rule_only(const gdn_dims* dims, const float* conv_out,
  * gdn_check_metadata_host - validate metadata VALUES on host copies of the
  * tensors (same meaning as in gdn_attention; any group may be absent by
  * passing 0 rows).  Checks: query_start_loc starts at 0 and is
- * non-decreasing; decode rows hold one token; spec rows hold 1..max_spec_len
+ * non-decreasing (a prefill row may be empty); decode rows hold one token;
+ * spec rows hold 1..max_spec_len
  * tokens; 1 <= n_acc <= T_b and (rolled history) n_acc + W - 2 <= state_len; slots
  * < num_slots; token rows in [0, num_actual_tokens) and distinct across both
  * streams; slots of different rows disjoint.  Returns GDN_OK or

@@ -334,9 +334,9 @@ int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
       return fail(GDN_ERR_MISSING_OPTIONAL, "non-spec rows need query_start_loc");
     if (!non_spec_state_indices)
       return fail(GDN_ERR_MISSING_OPTIONAL, "non-spec rows need non_spec_state_indices");
-    if (num_non_spec_tokens < num_decodes + num_prefills)
-      return fail(GDN_ERR_DIMS, "num_non_spec_tokens %d < rows %d (every row has a token)",
-                  num_non_spec_tokens, ns_rows);
+    if (num_non_spec_tokens < num_decodes)
+      return fail(GDN_ERR_DIMS, "num_non_spec_tokens %d < decodes %d (a decode has a token)",
+                  num_non_spec_tokens, num_decodes);
   }
   if ((long long)num_non_spec_tokens + num_spec_tokens != num_actual_tokens)
     return fail(GDN_ERR_CONSERVATION, "non-spec tokens %d + spec tokens %d != %d",
@@ -550,7 +550,7 @@ int gdn_check_metadata_host(const gdn_dims* dims, int32_t num_actual_tokens,
     if (query_start_loc[0] != 0) return fail(GDN_ERR_METADATA, "query_start_loc[0] != 0");
     for (int i = 0; i < ns_rows; ++i, ++owner) {
       int T = query_start_loc[i + 1] - query_start_loc[i];
-      if (T < 1) return fail(GDN_ERR_METADATA, "non-spec row %d has %d tokens", i, T);
+      if (T < 0) return fail(GDN_ERR_METADATA, "query_start_loc decreases at row %d", i);
       if (i < num_decodes && T != 1)
         return fail(GDN_ERR_METADATA, "decode row %d has %d tokens", i, T);
       if (int e = claim_slot(non_spec_state_indices[i], owner, "non-spec")) return e;

@@ -154,7 +154,8 @@ def assert_out_close(gpu, ref, rows=None, what="core_attn_out"):
     g = synth.from_bf16(gpu if rows is None else gpu[rows]).astype(np.float64)
     r = synth.from_bf16(ref if rows is None else ref[rows]).astype(np.float64)
     err = np.abs(g - r)
-    bad = err > OUT_ATOL + OUT_RTOL * np.abs(r)
+    # written so that a NaN or an infinity on either side is a failure
+    bad = ~(err <= OUT_ATOL + OUT_RTOL * np.abs(r))
     if bad.any():
         idx = np.argwhere(bad)[:5]
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; "
@@ -167,7 +168,7 @@ def assert_states_close(gpu, ref, what="ssm_state"):
     r = ref.reshape(-1, ref.shape[-2] * ref.shape[-1]).astype(np.float64)
     err = np.abs(g - r).max(axis=1)
     scale = np.abs(r).max(axis=1)
-    bad = err > STATE_RTOL * scale + 1e-30
+    bad = ~(err <= STATE_RTOL * scale + 1e-30)  # NaN anywhere in a tile fails it
     if bad.any():
         i = int(np.argmax(bad))
         raise AssertionError(f"{what}: {bad.sum()} of {len(bad)} tiles outside 1e-3 relative; "

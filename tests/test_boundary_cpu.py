@@ -155,6 +155,17 @@ def test_metadata_checker_rejects(change, needle):
     assert needle in gdn.gdn_last_error()
 
 
+def test_metadata_checker_empty_prefill_row():
+    # a prefill row may hold no tokens (a graph pad row); query_start_loc
+    # must not decrease
+    m = good_meta()
+    m.update(num_prefills=2, query_start_loc=[0, 1, 1, 4], non_spec_state_indices=[9, 0, 10])
+    assert check(**m) == gdn.GDN_OK
+    m.update(query_start_loc=[0, 1, 4, 3])
+    assert check(**m) == gdn.GDN_ERR_METADATA
+    assert "decreases" in gdn.gdn_last_error()
+
+
 def test_metadata_checker_window_bound():
     # n_acc - 1 + W - 1 must fit the ring: with L = 3 (W = 4) only n_acc = 1
     m = good_meta()
