@@ -592,7 +592,11 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   Tile4<kC, kC, NT> tp;
   Tile4<kC, RB, NT> tu;
   float tg;     // G of token lane % 64
-  int tx[4];    // global rows of this lane's output tokens (tested where used)
+  int tx[4];    // token_indx of this lane's output tokens (taken and tested where used)
+  // Without token_indx the loads below read G's words instead (any readable
+  // address: the value is dropped), so that no load sits behind a branch
+  // and the waits for earlier loads stay exact.
+  const int* tix = p.tix ? p.tix : reinterpret_cast<const int*>(ws.G);
   auto gather = [&](int c) {
     const int jb = pr.j0 + c * kC;
     const int nt = min(kC, pr.T - c * kC);
@@ -604,10 +608,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
     tu.load(ws.U + ((size_t)jb * Hv + h) * DV + RB * blk, Hv * DV);
     tg = ws.G[(size_t)(jb + min(lane, nt - 1)) * Hv + h];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = jb + min(16 * tt + 4 * lk + r, nt - 1);
-      tx[r] = p.tix ? p.tix[j] : j;
-    }
+    for (int r = 0; r < 4; ++r) tx[r] = tix[jb + min(16 * tt + 4 * lk + r, nt - 1)];
   };
   gather(0);
   for (int c = 0; c < nch; ++c) {
@@ -625,7 +626,8 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * tt + 4 * lk + r;
-      orow[r] = (t < nt && tx[r] >= 0 && tx[r] < p.num_actual_tokens) ? tx[r] : -1;
+      const int gr = p.tix ? tx[r] : pr.j0 + c * kC + min(t, nt - 1);
+      orow[r] = (t < nt && gr >= 0 && gr < p.num_actual_tokens) ? gr : -1;
     }
     // S0 split: lanes 2m and 2m+1 hold adjacent columns of a row; the even
     // lane writes their hi pair, the odd lane their lo pair
@@ -669,8 +671,9 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
       store_split4<kC>(UFs, 16 * jt + li, t0, u * f);
     }
     lds_barrier();
-    // the next chunk's operands load during (b) and (c)
-    if (c + 1 < nch) gather(c + 1);
+    // The next chunk's operands load during (b) and (c); the last chunk
+    // gathers itself again, so no load sits behind a branch.
+    gather(c + 1 < nch ? c + 1 : c);
 
     // (b) outputs on (tt, jt): e^{G_t} (Q S0^T)[t] + (P U)[t]; P is zero
     //     right of the diagonal block, so tokens 32..63 matter from tt = 2 on
