@@ -21,20 +21,18 @@
 // its rows of S through the row's chunks in MFMA accumulators and writes the
 // outputs through token_indx.
 //
-// chunk_prep's products use v_mfma_f32_16x16x4f32 (A[i][k] at lane i+16k,
-// B[k][j] at lane j+16k, D[i][j] at lane j+16*(i/4), element i%4); its sums
-// over the 64 tokens of a chunk take 16 steps m = 4M + e, lane group
-// kk = lane/16 adding token s = 16M + 4kk + e, so a token block M that a
-// triangular factor zeroes is skipped.
-//
-// chunk_state's products run on v_mfma_f32_16x16x32_bf16 (lane l holds
-// A[l%16][8(l/16)+e] and B[8(l/16)+e][l%16], e = 0..7; D as above) with each
-// fp32 operand split into two bf16 values, x = hi + lo + O(2^-17 |x|) with
-// hi = bf16(x) and lo = bf16(x - hi); a product is hi*hi + hi*lo + lo*hi in
-// fp32 accumulation, about 2^-16 relative error per term where one fp32
-// product has 2^-24, at a sixteenth of the fp32 MFMA's cycles per term.
-// Every tile arrives split: a row of n floats holds n bf16 hi values, then
-// n bf16 lo values (q and k from the conv kernel, W and P from chunk_prep).
+// The blocks of T below its diagonal are solved on v_mfma_f32_16x16x4f32
+// (A[i][k] at lane i+16k, B[k][j] at lane j+16k, D[i][j] at lane
+// j+16*(i/4), element i%4).  Every other product (K K^T, Q K^T, W, U~ in
+// chunk_prep; all of chunk_state) runs on v_mfma_f32_16x16x32_bf16 (lane l
+// holds A[l%16][8(l/16)+e] and B[8(l/16)+e][l%16], e = 0..7; D as above)
+// with each fp32 operand split into two bf16 values, x = hi + lo +
+// O(2^-17 |x|) with hi = bf16(x) and lo = bf16(x - hi); a product is
+// hi*hi + hi*lo + lo*hi in fp32 accumulation, about 2^-16 relative error
+// per term where one fp32 product has 2^-24, at a sixteenth of the fp32
+// MFMA's cycles per term.  Tiles in memory are stored split: a row of n
+// floats holds n bf16 hi values, then n bf16 lo values (q and k from the
+// conv kernel, W and P from chunk_prep).
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
