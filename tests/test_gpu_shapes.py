@@ -1,0 +1,85 @@
+"""HIP path against the oracle on the shapes and layer options the other
+parity tests leave out: spec rows of more than 4 tokens (up to 14, the most
+a 16-column ring holds with width 4), rings longer than the rows need, a
+conv bias, the identity activation and unnormalised q/k.
+
+Each shape picks a different specialisation of the row kernel (register
+gathers sized for rings of at most 6 or 8 columns and rows of at most 4
+tokens, or the general one), so every one of them runs here."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import synth
+from tests import helpers
+from tests.gpu_util import (Gpu, assert_out_close, assert_states_close, gpu_available, say)
+from tests.test_gpu_parity import check_spec_case
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU and libgdn.so")]
+
+
+@pytest.mark.parametrize("K", [6, 8, 14])
+def test_spec_long_rows(K):
+    # ring of W-1+K-1 columns (16 for K = 14), NULL slots, permuted tokens
+    case = synth.make_case("small", seed=20 + K, K=K, Ns=6, Hv=32, num_slots=128, null_p=0.1,
+                           permute_tokens=True)
+    check_spec_case(case)
+
+
+@pytest.mark.parametrize("K,L", [(4, 7), (4, 8), (3, 12)])
+def test_spec_ring_longer_than_needed(K, L):
+    # n_acc may then reach past K - 1 columns of history; the window offset
+    # and the roll still follow n_acc
+    case = synth.make_case("small", seed=30 + L, K=K, L=L, Ns=10, Hv=32, num_slots=128,
+                           null_p=0.0, permute_tokens=True)
+    check_spec_case(case)
+
+
+def _options(case, bias, activation, l2norm, seed):
+    rng = np.random.default_rng(seed)
+    d = case["dims"]
+    d["activation"] = activation
+    d["use_qk_l2norm"] = l2norm
+    C = synth.conv_dim(d["Hk"], d["Hv"], d["dk"], d["dv"])
+    if bias:
+        case["conv_bias"] = synth.to_bf16(0.5 * rng.standard_normal(C).astype(np.float32))
+    if not l2norm:
+        # unnormalised keys: keep |k|^2 below 1 so the recurrence stays stable
+        w = synth.from_bf16(case["conv_weight"]) / 16.0
+        case["conv_weight"] = synth.to_bf16(w)
+        if bias:
+            case["conv_bias"] = synth.to_bf16(synth.from_bf16(case["conv_bias"]) / 16.0)
+    return case
+
+
+OPTIONS = [(True, 1, 1), (False, 0, 1), (True, 0, 1), (True, 1, 0), (False, 0, 0)]
+
+
+@pytest.mark.parametrize("bias,activation,l2norm", OPTIONS)
+def test_spec_layer_options(bias, activation, l2norm):
+    case = synth.make_case("small", seed=40, K=3, Ns=8, Hv=32, num_slots=64, null_p=0.2,
+                           permute_tokens=True)
+    check_spec_case(_options(case, bias, activation, l2norm, 41))
+
+
+@pytest.mark.parametrize("bias,activation,l2norm", OPTIONS)
+@pytest.mark.parametrize("dk", [32, 128])
+def test_mixed_layer_options(bias, activation, l2norm, dk):
+    # decodes, prefill rows (the token recurrence for dk = 32, the chunked
+    # form for 128) and spec rows in one call
+    case = synth.make_case("mixed", seed=50, Ns=6, K=3, Nd=5, prefill_lens=(70, 130),
+                           Hk=4, Hv=8, dk=dk, dv=dk, num_slots=64)
+    case = _options(case, bias, activation, l2norm, 51)
+    o1, r1, s1, _ = helpers.run_nonspec(case)
+    c = helpers.clone(case)
+    c["conv_state"], c["ssm_state"] = r1, s1
+    out_ref, conv_ref, ssm_ref, _ = helpers.run_spec(c, out=o1)
+    g = Gpu(case)
+    say(f"mixed dk={dk} bias={bias} act={activation} l2norm={l2norm}")
+    g.attention()
+    assert_out_close(g.host_out(), out_ref)
+    slots = synth.referenced_slots(case)
+    np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
+    assert_states_close(g.host_ssm(slots), ssm_ref[slots])
