@@ -65,10 +65,11 @@ def test_spec_layer_options(bias, activation, l2norm):
 
 
 @pytest.mark.parametrize("bias,activation,l2norm", OPTIONS)
-@pytest.mark.parametrize("dk", [32, 128])
+@pytest.mark.parametrize("dk", [16, 32, 64, 128])
 def test_mixed_layer_options(bias, activation, l2norm, dk):
-    # decodes, prefill rows (the token recurrence for dk = 32, the chunked
-    # form for 128) and spec rows in one call
+    # decodes, prefill rows (the token recurrence below dk = 64, the chunked
+    # form from 64) and spec rows in one call, at every head size the row
+    # kernel is built for
     case = synth.make_case("mixed", seed=50, Ns=6, K=3, Nd=5, prefill_lens=(70, 130),
                            Hk=4, Hv=8, dk=dk, dv=dk, num_slots=64)
     case = _options(case, bias, activation, l2norm, 51)
