@@ -36,7 +36,7 @@ def per_token_case(seed, Ns, K, T_extra=0, null_p=0.2, Hk=4, Hv=8, dk=128):
     return case
 
 
-@pytest.mark.parametrize("K", [2, 3, 4])
+@pytest.mark.parametrize("K", [2, 3, 4, 8])
 def test_per_token_spec_parity(K):
     check_spec_case(per_token_case(400 + K, Ns=12, K=K))
 

@@ -84,3 +84,28 @@ def test_mixed_layer_options(bias, activation, l2norm, dk):
     slots = synth.referenced_slots(case)
     np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
     assert_states_close(g.host_ssm(slots), ssm_ref[slots])
+
+
+@pytest.mark.parametrize("Hk,Hv", [(2, 8), (1, 8), (4, 4)])
+def test_spec_head_groups(Hk, Hv):
+    # 4 and 8 v-heads per k-head (the row kernel then takes its 512 or 1024
+    # state rows in several passes) and one
+    case = synth.make_case("small", seed=60 + Hv // Hk, K=3, Ns=6, Hk=Hk, Hv=Hv, num_slots=64,
+                           null_p=0.15, permute_tokens=True)
+    check_spec_case(case)
+
+
+def test_mixed_four_v_heads_per_k_head():
+    case = synth.make_case("mixed", seed=70, Ns=5, K=4, Nd=4, prefill_lens=(65, 140),
+                           Hk=2, Hv=8, num_slots=64)
+    o1, r1, s1, _ = helpers.run_nonspec(case)
+    c = helpers.clone(case)
+    c["conv_state"], c["ssm_state"] = r1, s1
+    out_ref, conv_ref, ssm_ref, _ = helpers.run_spec(c, out=o1)
+    g = Gpu(case)
+    say("mixed, 4 v-heads per k-head")
+    g.attention()
+    assert_out_close(g.host_out(), out_ref)
+    slots = synth.referenced_slots(case)
+    np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
+    assert_states_close(g.host_ssm(slots), ssm_ref[slots])
