@@ -99,7 +99,7 @@ int conv_dim(const gdn_dims* d) {
 }
 
 void fill_common(gdn::RowArgs& a, const gdn_dims* d, int num_actual_tokens) {
-  std::memset(&a, 0, sizeof a);
+  a = gdn::RowArgs{};
   a.Hk = d->num_k_heads;
   a.Hv = d->num_v_heads;
   a.G = d->num_v_heads / d->num_k_heads;
