@@ -120,6 +120,23 @@ __device__ __forceinline__ Frag frag_cols(const char* t, int ks, int mt, int li,
   const u32x2 l1 = tr_read(t, sp_off<COLS>(r + 4, COLS + x));
   return {u32x4{h0.x, h0.y, h1.x, h1.y}, u32x4{l0.x, l0.y, l1.x, l1.y}};
 }
+// The S0 tile is read only as rows (16 rows at one chunk) and written by
+// lane pairs, one word per lane, four rows 4 apart per instruction; its
+// chunk c of row r sits at c ^ (r mod 16), lo chunks also flipping bit 1,
+// so the four rows' hi and lo chunk pairs fall on eight different bank
+// groups.
+template <int COLS>
+__device__ __forceinline__ int s0_off(int r, int x) {
+  const int flip = x >= COLS ? 2 : 0;
+  return r * 4 * COLS + (((x >> 3) ^ (r & 15) ^ flip) << 4) + ((x & 7) << 1);
+}
+template <int COLS>
+__device__ __forceinline__ Frag frag_rows_s0(const char* t, int r, int ks, int lk) {
+  Frag f;
+  f.hi = *reinterpret_cast<const u32x4*>(t + s0_off<COLS>(r, 32 * ks + 8 * lk));
+  f.lo = *reinterpret_cast<const u32x4*>(t + s0_off<COLS>(r, COLS + 32 * ks + 8 * lk));
+  return f;
+}
 // Four consecutive values (columns c..c+3 of row r) into a split tile.
 template <int COLS>
 __device__ __forceinline__ void store_split4(char* t, int r, int c, v4f v) {
@@ -640,7 +657,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
         const unsigned lp = (unsigned)__builtin_amdgcn_mov_dpp((int)lv, 0xB1, 0xF, 0xF, false);
         const int row = 16 * jt + 4 * lk + r, col = 16 * (TPW * tt + q) + li;
         const bool odd = (li & 1) != 0;
-        *reinterpret_cast<unsigned*>(Ss + sp_off<DK>(row, odd ? DK + col - 1 : col)) =
+        *reinterpret_cast<unsigned*>(Ss + s0_off<DK>(row, odd ? DK + col - 1 : col)) =
             odd ? (lp | (lv << 16)) : (hv | (hp << 16));
       }
     lds_barrier();
@@ -650,7 +667,7 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
     // lane's 8-runs of each k-step
     Frag sb[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) sb[ks] = frag_rows<DK>(Ss, 16 * jt + li, ks, lk);
+    for (int ks = 0; ks < KS; ++ks) sb[ks] = frag_rows_s0<DK>(Ss, 16 * jt + li, ks, lk);
     // (a) U = U~ - W S0^T on (token tile tt, row tile jt), kept split as
     //     U^T (B operand of P U) and U^T diag(F), F_t = e^{G_C - G_t} (A
     //     operand of the update)
