@@ -137,6 +137,24 @@ __device__ __forceinline__ Frag frag_rows_s0(const char* t, int r, int ks, int l
   f.lo = *reinterpret_cast<const u32x4*>(t + s0_off<COLS>(r, COLS + 32 * ks + 8 * lk));
   return f;
 }
+// The scaled T tiles of chunk_prep are read only as rows and written four
+// consecutive rows per instruction, 8 bytes per lane: chunk c of row r sits
+// at c ^ rev4(r mod 16), so rows r and r+1 (bit 0 -> chunk bit 3) land on
+// different halves of the banks.
+__device__ __forceinline__ int rev4(int r) {
+  return ((r & 1) << 3) | ((r & 2) << 1) | ((r & 4) >> 1) | ((r & 8) >> 3);
+}
+template <int COLS>
+__device__ __forceinline__ int t_off(int r, int x) {
+  return r * 4 * COLS + (((x >> 3) ^ rev4(r)) << 4) + ((x & 7) << 1);
+}
+template <int COLS>
+__device__ __forceinline__ Frag frag_rows_t(const char* t, int r, int ks, int lk) {
+  Frag f;
+  f.hi = *reinterpret_cast<const u32x4*>(t + t_off<COLS>(r, 32 * ks + 8 * lk));
+  f.lo = *reinterpret_cast<const u32x4*>(t + t_off<COLS>(r, COLS + 32 * ks + 8 * lk));
+  return f;
+}
 // Four consecutive values (columns c..c+3 of row r) into a split tile.
 template <int COLS>
 __device__ __forceinline__ void store_split4(char* t, int r, int c, v4f v) {
@@ -473,8 +491,14 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int e = (i * 256 + tid) * 4, r = e / kC, cc = e - r * kC;
-      store_split4<kC>(TG, r, cc, tr4[i] * *reinterpret_cast<const v4f*>(BG + cc));
-      store_split4<kC>(TB, r, cc, tr4[i] * *reinterpret_cast<const v4f*>(Bs + cc));
+      const v4f g4 = tr4[i] * *reinterpret_cast<const v4f*>(BG + cc);
+      const v4f b4 = tr4[i] * *reinterpret_cast<const v4f*>(Bs + cc);
+      const Split2 g0 = split2(g4.x, g4.y), g1 = split2(g4.z, g4.w);
+      const Split2 b0 = split2(b4.x, b4.y), b1 = split2(b4.z, b4.w);
+      *reinterpret_cast<u32x2*>(TG + t_off<kC>(r, cc)) = u32x2{g0.hi, g1.hi};
+      *reinterpret_cast<u32x2*>(TG + t_off<kC>(r, kC + cc)) = u32x2{g0.lo, g1.lo};
+      *reinterpret_cast<u32x2*>(TB + t_off<kC>(r, cc)) = u32x2{b0.hi, b1.hi};
+      *reinterpret_cast<u32x2*>(TB + t_off<kC>(r, kC + cc)) = u32x2{b0.lo, b1.lo};
     }
   }
   lds_barrier();
@@ -506,8 +530,8 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         if (ks == 1 && ti < 2) continue;
-        const Frag ag = frag_rows<kC>(TG, 16 * ti + li, ks, lk);
-        const Frag ab = frag_rows<kC>(TB, 16 * ti + li, ks, lk);
+        const Frag ag = frag_rows_t<kC>(TG, 16 * ti + li, ks, lk);
+        const Frag ab = frag_rows_t<kC>(TB, 16 * ti + li, ks, lk);
 #pragma unroll
         for (int q = 0; q < NW; ++q) {
           aw[ti][q] = mfma3(ag, kb[ks][q], aw[ti][q]);
