@@ -196,13 +196,11 @@ void fill_layer(gdn::RowArgs& r, const Layer& L) {
   r.out = L.out;
 }
 
-// Spec rows; `dec` (optional) are decode rows that share the launch as its
-// first row set, the spec rows following them in the grid (rows of one call
-// use disjoint slots; measured on the mixed batch, decodes first finish
-// 3% sooner than spec rows first).
-int run_spec(const Layer& L, const SpecBatch& s, hipStream_t stream,
-             const gdn::RowArgs* dec = nullptr) {
-  if (s.num_spec_decodes == 0) return GDN_OK;
+// Row-kernel arguments of the spec rows.  With `dec` (decode rows) the two
+// share one launch: the decodes are its first row set and the spec rows
+// follow them in the grid (rows of one call use disjoint slots; measured on
+// the mixed batch, decodes first finish 3% sooner than spec rows first).
+gdn::RowArgs spec_rows(const Layer& L, const SpecBatch& s, const gdn::RowArgs* dec = nullptr) {
   gdn::RowArgs r{};
   fill_layer(r, L);
   r.kind = gdn::kSpec;
@@ -231,9 +229,15 @@ int run_spec(const Layer& L, const SpecBatch& s, hipStream_t stream,
     m.more.tix = r.tix;
     r = m;
   }
+  return r;
+}
+
+int run_spec(const Layer& L, const SpecBatch& s, hipStream_t stream) {
+  if (s.num_spec_decodes == 0) return GDN_OK;
+  const gdn::RowArgs r = spec_rows(L, s);
   if (int e = lds_ok(r, L.d)) return e;
   return launch(gdn::launch_rows(r, L.d->head_k_dim, L.d->head_v_dim, stream),
-                dec ? "spec and decode row kernel" : "spec row kernel");
+                "spec row kernel");
 }
 
 }  // namespace
@@ -376,8 +380,17 @@ int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
     dec.stage = gdn::kFused;
   }
   const bool merged = num_decodes > 0 && s.num_spec_decodes > 0;
-  if (num_decodes > 0 && !merged) {
+  // every row launch is checked before anything is enqueued
+  gdn::RowArgs rows_after{};
+  if (s.num_spec_decodes > 0) {
+    rows_after = spec_rows(L, s, merged ? &dec : nullptr);
+    if (int e = lds_ok(rows_after, dims)) return e;
+  }
+  const bool decodes_alone = num_decodes > 0 && !merged;
+  if (decodes_alone) {
     if (int e = lds_ok(dec, dims)) return e;
+  }
+  if (decodes_alone) {
     if (int e = launch(gdn::launch_rows(dec, dims->head_k_dim, dims->head_v_dim, st),
                        "decode row kernel"))
       return e;
@@ -421,7 +434,9 @@ int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
                        "prefill kernels"))
       return e;
   }
-  return run_spec(L, s, st, merged ? &dec : nullptr);
+  if (s.num_spec_decodes == 0) return GDN_OK;
+  return launch(gdn::launch_rows(rows_after, dims->head_k_dim, dims->head_v_dim, st),
+                merged ? "decode and spec row kernel" : "spec row kernel");
 }
 
 static int stage_rows(const gdn_dims* dims, const gdn_rows* rows, int num_actual_tokens,

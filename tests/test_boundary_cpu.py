@@ -110,6 +110,18 @@ def test_bad_counts_rejected():
     assert spec_call(dims(), qkv=None) == gdn.GDN_ERR_NULL
 
 
+def test_row_kernel_lds_checked_before_any_launch():
+    # 8 v-heads on one k-head with 14-token spec rows need more LDS than a
+    # CU has: the call is rejected before the prefill kernels are enqueued
+    # (with no GPU here, a launch would have failed with GDN_ERR_HIP instead)
+    d = dims(num_k_heads=1, num_v_heads=8, state_len=16)
+    need = L.gdn_workspace_bytes(ctypes.byref(d), 6, 1)
+    rc = attn_call(d, nat=6 + 2 * 14, nd=2, npf=1, nns=6, Ns=2, Ts=28, K=14, ws=FAKE,
+                   ws_bytes=need)
+    assert rc == gdn.GDN_ERR_UNSUPPORTED, gdn.gdn_last_error()
+    assert "LDS" in gdn.gdn_last_error()
+
+
 def test_status_strings():
     for code in range(0, -10, -1):
         assert gdn.gdn_status_string(code) != "unknown status"
