@@ -390,6 +390,11 @@ int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
   if (decodes_alone) {
     if (int e = lds_ok(dec, dims)) return e;
   }
+  if (num_prefills > 0 && dims->head_k_dim >= 64) {
+    if (int e = launch(gdn::prepare_chunked(dims->head_k_dim, dims->head_v_dim),
+                       "chunked prefill set-up"))
+      return e;
+  }
   if (decodes_alone) {
     if (int e = launch(gdn::launch_rows(dec, dims->head_k_dim, dims->head_v_dim, st),
                        "decode row kernel"))

@@ -780,6 +780,24 @@ static hipError_t launch_chunked_typed(const PrefillArgs& a, const float* y, con
   return hipGetLastError();
 }
 
+hipError_t prepare_chunked(int dk, int dv) {
+  if (dk != dv) return hipErrorInvalidValue;
+  switch (dk) {
+    case 64:
+    case 128: {
+      const size_t l1 = dk == 64 ? PrepLds<64>::total : PrepLds<128>::total;
+      const size_t l2 = dk == 64 ? StateLds<64, kStateRows>::total : StateLds<128, kStateRows>::total;
+      const void* prep = dk == 64 ? reinterpret_cast<const void*>(chunk_prep_kernel<64, 64>)
+                                  : reinterpret_cast<const void*>(chunk_prep_kernel<128, 128>);
+      const void* state = dk == 64 ? reinterpret_cast<const void*>(chunk_state_kernel<64, 64>)
+                                   : reinterpret_cast<const void*>(chunk_state_kernel<128, 128>);
+      hipError_t e = ensure_dynamic_lds(prep, l1);
+      return e != hipSuccess ? e : ensure_dynamic_lds(state, l2);
+    }
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_chunked(const PrefillArgs& a, int dk, int dv, const float* y, const float* glog,
                           const float* gbeta, const ChunkWs& ws, hipStream_t s) {
   if (dk != dv) return hipErrorInvalidValue;

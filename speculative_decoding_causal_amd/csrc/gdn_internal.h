@@ -119,5 +119,8 @@ struct ChunkWs {
 };
 hipError_t launch_chunked(const PrefillArgs& a, int dk, int dv, const float* y, const float* glog,
                           const float* gbeta, const ChunkWs& ws, hipStream_t s);
+// Raises the chunk kernels' LDS limit (once per device); callers run it
+// before enqueuing anything, so a failure leaves every buffer untouched.
+hipError_t prepare_chunked(int dk, int dv);
 
 }  // namespace gdn
