@@ -2,7 +2,8 @@
 
 Thin ctypes binding over ``libgdn.so`` (HIP kernels for gfx950 behind a C
 ABI declared in ``include/gdn.h``).  This module only marshals arguments:
-dtype / contiguity / device checks, sizes derived from tensor shapes, the
+dtype / contiguity / device checks, size checks of every tensor the kernels
+index (plain pointers carry no size), sizes derived from tensor shapes, the
 current HIP stream.  Every step of the computation runs in the library's
 kernels; there is no CPU fallback, and importing fails loudly when the
 library has not been built.
@@ -190,6 +191,51 @@ def _check_pools(cfg: GdnConfig, conv_state, ssm_state):
         raise ValueError(f"ssm_state must be {list(want)}, got {list(ssm_state.shape)}")
 
 
+def _need(t, name, shape=None, at_least=None):
+    """Size check of a tensor the kernels index (plain pointers carry no
+    size, so a short tensor would be read or written past its end)."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
+    if at_least is not None and t.numel() < at_least:
+        raise ValueError(f"{name} holds {t.numel()} values; the call needs {at_least}")
+
+
+def _check_layer(cfg: GdnConfig, nat, mixed_qkv, a, b, conv_weight, conv_bias, A_log, dt_bias,
+                 core_attn_out):
+    C, Hv = cfg.conv_dim, cfg.num_v_heads
+    if mixed_qkv.dim() != 2 or mixed_qkv.shape[1] != C or mixed_qkv.shape[0] < nat:
+        raise ValueError(f"mixed_qkv must be [>= {nat}, {C}], got {list(mixed_qkv.shape)}")
+    _need(a, "a", at_least=nat * Hv)
+    _need(b, "b", at_least=nat * Hv)
+    _need(conv_weight, "conv_weight", shape=(C, cfg.conv_width))
+    _need(conv_bias, "conv_bias", shape=(C,))
+    _need(A_log, "A_log", shape=(Hv,))
+    _need(dt_bias, "dt_bias", shape=(Hv,))
+    _need(core_attn_out, "core_attn_out", at_least=nat * Hv * cfg.head_v_dim)
+
+
+def _check_spec_meta(Ns, K, Ts, ssi, nacc, scache, stix):
+    if Ns <= 0:
+        return
+    _need(ssi, "spec_state_indices", at_least=Ns * K)
+    _need(nacc, "num_accepted_tokens", at_least=Ns)
+    _need(scache, "spec_cache_indices", at_least=Ns)
+    _need(stix, "spec_token_indx", at_least=Ts)
+
+
+def _check_nonspec_meta(rows, tokens, qsl, nsi, his, ntix):
+    if rows <= 0:
+        return
+    _need(qsl, "query_start_loc", at_least=rows + 1)
+    _need(nsi, "non_spec_state_indices", at_least=rows)
+    _need(his, "has_initial_state", at_least=rows)
+    _need(ntix, "non_spec_token_indx", at_least=tokens)
+
+
 def _host_count(x, given):
     if given is not None:
         return int(given)
@@ -211,16 +257,20 @@ def gdn_spec_attention(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias,
     dev = mixed_qkv.device
     _check_pools(cfg, conv_state, ssm_state)
     dims = cfg.dims(conv_state)
+    nat = int(mixed_qkv.shape[0] if num_actual_tokens is None else num_actual_tokens)
+    _check_layer(cfg, nat, mixed_qkv, a, b, conv_weight, conv_bias, A_log, dt_bias,
+                 core_attn_out)
     Ns = int(spec_query_start_loc.shape[0]) - 1 if spec_query_start_loc is not None else 0
     K = int(spec_state_indices.shape[1]) if spec_state_indices is not None else 1
     T = _host_count(spec_query_start_loc, num_spec_tokens) if Ns > 0 else 0
+    _check_spec_meta(Ns, K, T, spec_state_indices, num_accepted_tokens, spec_cache_indices,
+                     spec_token_indx)
     rc = _lib.gdn_spec_attention(
         ctypes.byref(dims), _ptr(mixed_qkv, _BF16, "mixed_qkv", dev), _ptr(a, _BF16, "a", dev),
         _ptr(b, _BF16, "b", dev), _ptr(conv_weight, _BF16, "conv_weight", dev),
         _ptr(conv_bias, _BF16, "conv_bias", dev), _ptr(A_log, torch.float32, "A_log", dev),
         _ptr(dt_bias, torch.float32, "dt_bias", dev), _ptr(conv_state, _BF16, "conv_state", dev),
-        _ptr(ssm_state, torch.float32, "ssm_state", dev),
-        int(mixed_qkv.shape[0] if num_actual_tokens is None else num_actual_tokens), Ns, T, K,
+        _ptr(ssm_state, torch.float32, "ssm_state", dev), nat, Ns, T, K,
         _ptr(spec_query_start_loc, _I32, "spec_query_start_loc", dev),
         _ptr(spec_cache_indices, _I32, "spec_cache_indices", dev),
         _ptr(spec_state_indices, _I32, "spec_state_indices", dev),
@@ -253,9 +303,17 @@ def gdn_attention(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias, A_log
     dev = mixed_qkv.device
     _check_pools(cfg, conv_state, ssm_state)
     dims = cfg.dims(conv_state)
+    nat = int(mixed_qkv.shape[0] if num_actual_tokens is None else num_actual_tokens)
+    _check_layer(cfg, nat, mixed_qkv, a, b, conv_weight, conv_bias, A_log, dt_bias,
+                 core_attn_out)
     Ns = int(spec_query_start_loc.shape[0]) - 1 if spec_query_start_loc is not None else 0
     K = int(spec_state_indices.shape[1]) if spec_state_indices is not None else 1
     Ts = _host_count(spec_query_start_loc, num_spec_tokens) if Ns > 0 else 0
+    _check_spec_meta(Ns, K, Ts, spec_state_indices, num_accepted_tokens, spec_cache_indices,
+                     spec_token_indx)
+    _check_nonspec_meta(int(num_decodes) + int(num_prefills), int(num_non_spec_tokens),
+                        query_start_loc, non_spec_state_indices, has_initial_state,
+                        non_spec_token_indx)
     ws_ptr = _ptr(workspace, None, "workspace", dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = _lib.gdn_attention(
@@ -263,8 +321,7 @@ def gdn_attention(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias, A_log
         _ptr(b, _BF16, "b", dev), _ptr(conv_weight, _BF16, "conv_weight", dev),
         _ptr(conv_bias, _BF16, "conv_bias", dev), _ptr(A_log, torch.float32, "A_log", dev),
         _ptr(dt_bias, torch.float32, "dt_bias", dev), _ptr(conv_state, _BF16, "conv_state", dev),
-        _ptr(ssm_state, torch.float32, "ssm_state", dev),
-        int(mixed_qkv.shape[0] if num_actual_tokens is None else num_actual_tokens),
+        _ptr(ssm_state, torch.float32, "ssm_state", dev), nat,
         int(num_decodes), int(num_prefills), int(num_non_spec_tokens),
         _ptr(query_start_loc, _I32, "query_start_loc", dev),
         _ptr(non_spec_state_indices, _I32, "non_spec_state_indices", dev),
@@ -286,6 +343,13 @@ def _rows(kind, query_start_loc, num_tokens, max_row_tokens, cache_indices=None,
           state_indices=None, num_accepted_tokens=None, has_initial_state=None,
           token_indx=None, dev=None) -> GdnRows:
     n = int(query_start_loc.shape[0]) - 1
+    if n > 0:
+        per_row = int(max_row_tokens) if int(kind) == GDN_ROWS_SPEC else 1
+        _need(cache_indices, "cache_indices", at_least=n)
+        _need(state_indices, "state_indices", at_least=n * per_row)
+        _need(num_accepted_tokens, "num_accepted_tokens", at_least=n)
+        _need(has_initial_state, "has_initial_state", at_least=n)
+        _need(token_indx, "token_indx", at_least=int(num_tokens))
     return GdnRows(int(kind), n, int(num_tokens), int(max_row_tokens),
                    _ptr(query_start_loc, _I32, "query_start_loc", dev),
                    _ptr(cache_indices, _I32, "cache_indices", dev),
@@ -301,6 +365,14 @@ def gdn_conv_only(cfg: GdnConfig, mixed_qkv, conv_weight, conv_bias, conv_state,
                   has_initial_state=None, token_indx=None, stream=None) -> None:
     dev = mixed_qkv.device
     dims = cfg.dims(conv_state)
+    C, nat = cfg.conv_dim, int(mixed_qkv.shape[0])
+    if mixed_qkv.dim() != 2 or mixed_qkv.shape[1] != C:
+        raise ValueError(f"mixed_qkv must be [num_tokens, {C}], got {list(mixed_qkv.shape)}")
+    if conv_state.dim() != 3 or conv_state.shape[2] != C:
+        raise ValueError(f"conv_state must be [num_slots, state_len, {C}]")
+    _need(conv_weight, "conv_weight", shape=(C, cfg.conv_width))
+    _need(conv_bias, "conv_bias", shape=(C,))
+    _need(conv_out, "conv_out", at_least=nat * C)
     rows = _rows(kind, query_start_loc, num_tokens, max_row_tokens, cache_indices,
                  state_indices, num_accepted_tokens, has_initial_state, token_indx, dev)
     rc = _lib.gdn_conv_only(ctypes.byref(dims), _ptr(mixed_qkv, _BF16, "mixed_qkv", dev),
@@ -321,6 +393,17 @@ def gdn_delta_rule_only(cfg: GdnConfig, conv_out, a, b, A_log, dt_bias, ssm_stat
     dev = conv_out.device
     dims = cfg.dims(state_len=state_len if state_len is not None else cfg.conv_width - 1,
                     num_slots=int(ssm_state.shape[0]))
+    C, Hv, nat = cfg.conv_dim, cfg.num_v_heads, int(conv_out.shape[0])
+    if conv_out.dim() != 2 or conv_out.shape[1] != C:
+        raise ValueError(f"conv_out must be [num_tokens, {C}], got {list(conv_out.shape)}")
+    want = (ssm_state.shape[0], Hv, cfg.head_v_dim, cfg.head_k_dim)
+    if tuple(ssm_state.shape) != want:
+        raise ValueError(f"ssm_state must be {list(want)}, got {list(ssm_state.shape)}")
+    _need(a, "a", at_least=nat * Hv)
+    _need(b, "b", at_least=nat * Hv)
+    _need(A_log, "A_log", shape=(Hv,))
+    _need(dt_bias, "dt_bias", shape=(Hv,))
+    _need(core_attn_out, "core_attn_out", at_least=nat * Hv * cfg.head_v_dim)
     rows = _rows(kind, query_start_loc, num_tokens, max_row_tokens, cache_indices,
                  state_indices, num_accepted_tokens, has_initial_state, token_indx, dev)
     rc = _lib.gdn_delta_rule_only(

@@ -183,3 +183,113 @@ def test_metadata_checker_window_bound():
     m = good_meta()
     assert check(state_len=3, **m) == gdn.GDN_ERR_METADATA
     assert "window" in gdn.gdn_last_error()
+
+
+# ---- binding size checks (CPU tensors: the size checks run before the
+# device check, so a well-sized call stops at "must be a GPU tensor") ----
+
+def _layer(nat=10, Ns=3, K=3, Nd=2, Np=1, ntok=4):
+    import torch
+    cfg = gdn.GdnConfig(num_k_heads=2, num_v_heads=4, head_k_dim=16, head_v_dim=16)
+    C, Hv, dv = cfg.conv_dim, cfg.num_v_heads, cfg.head_v_dim
+    bf, i32 = torch.bfloat16, torch.int32
+    t = dict(mixed_qkv=torch.zeros(nat, C, dtype=bf), a=torch.zeros(nat, Hv, dtype=bf),
+             b=torch.zeros(nat, Hv, dtype=bf), conv_weight=torch.zeros(C, 4, dtype=bf),
+             conv_bias=None, A_log=torch.zeros(Hv), dt_bias=torch.zeros(Hv),
+             conv_state=torch.zeros(8, 5, C, dtype=bf), ssm_state=torch.zeros(8, Hv, dv, 16),
+             core_attn_out=torch.zeros(nat, Hv, dv, dtype=bf))
+    spec = dict(spec_query_start_loc=torch.arange(0, 3 * Ns + 1, 3, dtype=i32),
+                spec_state_indices=torch.zeros(Ns, K, dtype=i32),
+                num_accepted_tokens=torch.ones(Ns, dtype=i32),
+                spec_token_indx=torch.arange(3 * Ns, dtype=i32), num_spec_tokens=3 * Ns)
+    nonspec = dict(num_decodes=Nd, num_prefills=Np, num_non_spec_tokens=ntok,
+                   query_start_loc=torch.tensor([0, 1, 2, ntok], dtype=i32),
+                   non_spec_state_indices=torch.zeros(Nd + Np, dtype=i32),
+                   has_initial_state=torch.ones(Nd + Np, dtype=torch.uint8),
+                   non_spec_token_indx=torch.arange(9, 9 + ntok, dtype=i32) % nat)
+    return cfg, t, spec, nonspec
+
+
+def _spec_call(cfg, t, spec):
+    gdn.gdn_spec_attention(cfg, t["mixed_qkv"], t["a"], t["b"], t["conv_weight"],
+                           t["conv_bias"], t["A_log"], t["dt_bias"], t["conv_state"],
+                           t["ssm_state"], spec["spec_query_start_loc"],
+                           spec["spec_state_indices"], spec["num_accepted_tokens"],
+                           t["core_attn_out"], spec_token_indx=spec["spec_token_indx"],
+                           num_spec_tokens=spec["num_spec_tokens"])
+
+
+def _mixed_call(cfg, t, spec, nonspec):
+    gdn.gdn_attention(cfg, t["mixed_qkv"], t["a"], t["b"], t["conv_weight"], t["conv_bias"],
+                      t["A_log"], t["dt_bias"], t["conv_state"], t["ssm_state"],
+                      t["core_attn_out"], **spec, **nonspec)
+
+
+def test_binding_well_sized_call_reaches_device_check():
+    cfg, t, spec, nonspec = _layer()
+    with pytest.raises(ValueError, match="GPU tensor"):
+        _spec_call(cfg, t, spec)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        _mixed_call(cfg, t, spec, nonspec)
+
+
+@pytest.mark.parametrize("name,shape", [
+    ("mixed_qkv", (9, 192)), ("mixed_qkv", (10, 191)), ("a", (9, 4)), ("b", (10, 3)),
+    ("conv_weight", (192, 3)), ("A_log", (3,)), ("dt_bias", (5,)),
+    ("core_attn_out", (10, 4, 15))])
+def test_binding_rejects_short_layer_tensor(name, shape):
+    import torch
+    cfg, t, spec, nonspec = _layer()
+    t[name] = torch.zeros(shape, dtype=t[name].dtype)
+    for call in (lambda: _spec_call(cfg, t, spec), lambda: _mixed_call(cfg, t, spec, nonspec)):
+        with pytest.raises(ValueError, match=name):
+            call()
+
+
+@pytest.mark.parametrize("name,n", [("spec_state_indices", 2), ("num_accepted_tokens", 2),
+                                    ("spec_token_indx", 8)])
+def test_binding_rejects_short_spec_metadata(name, n):
+    # 3 spec rows of 3 tokens; the first n entries (rows of spec_state_indices)
+    cfg, t, spec, nonspec = _layer()
+    spec[name] = spec[name][:n].clone()
+    with pytest.raises(ValueError, match=name):
+        _spec_call(cfg, t, spec)
+
+
+@pytest.mark.parametrize("name,n", [("query_start_loc", 3), ("non_spec_state_indices", 2),
+                                    ("has_initial_state", 2), ("non_spec_token_indx", 3)])
+def test_binding_rejects_short_nonspec_metadata(name, n):
+    cfg, t, spec, nonspec = _layer()
+    nonspec[name] = nonspec[name][:n].clone()
+    with pytest.raises(ValueError, match=name):
+        _mixed_call(cfg, t, spec, nonspec)
+
+
+def test_binding_stage_entry_points_check_sizes():
+    import torch
+    cfg, t, spec, _ = _layer()
+    C = cfg.conv_dim
+    rows = dict(kind=gdn.GDN_ROWS_SPEC, query_start_loc=spec["spec_query_start_loc"],
+                num_tokens=9, max_row_tokens=3, state_indices=spec["spec_state_indices"],
+                num_accepted_tokens=spec["num_accepted_tokens"],
+                token_indx=spec["spec_token_indx"])
+    conv_out = torch.zeros(10, C)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        gdn.gdn_conv_only(cfg, t["mixed_qkv"], t["conv_weight"], None, t["conv_state"],
+                          conv_out, **rows)
+    with pytest.raises(ValueError, match="conv_out"):
+        gdn.gdn_conv_only(cfg, t["mixed_qkv"], t["conv_weight"], None, t["conv_state"],
+                          conv_out[:9], **rows)
+    with pytest.raises(ValueError, match="state_indices"):
+        gdn.gdn_conv_only(cfg, t["mixed_qkv"], t["conv_weight"], None, t["conv_state"],
+                          conv_out, **{**rows, "state_indices": spec["spec_state_indices"][:2]})
+    with pytest.raises(ValueError, match="GPU tensor"):
+        gdn.gdn_delta_rule_only(cfg, conv_out, t["a"], t["b"], t["A_log"], t["dt_bias"],
+                                t["ssm_state"], t["core_attn_out"], state_len=5, **rows)
+    with pytest.raises(ValueError, match="core_attn_out"):
+        gdn.gdn_delta_rule_only(cfg, conv_out, t["a"], t["b"], t["A_log"], t["dt_bias"],
+                                t["ssm_state"], t["core_attn_out"][:9], state_len=5, **rows)
+    with pytest.raises(ValueError, match="ssm_state"):
+        gdn.gdn_delta_rule_only(cfg, conv_out, t["a"], t["b"], t["A_log"], t["dt_bias"],
+                                t["ssm_state"][:, :, :, :8], t["core_attn_out"], state_len=5,
+                                **rows)
