@@ -492,7 +492,11 @@ gdn_rows_kernel(RowArgs pa) {
     const float bv = r >= 0 ? bf2f(p.b[(size_t)r * p.Hv + h]) : 0.f;
     gate_pair(av, bv, p.A_log[h], p.dt_bias[h], &ga[idx], &gb[idx]);
   }
-  __syncthreads();
+  // The phases hand data over through LDS only: every global address a
+  // thread writes (its ring channels, its state rows, an output) is read, if
+  // at all, by that same thread, so the barriers order LDS alone and wait
+  // neither for the state loads nor for the ring stores still in flight.
+  lds_barrier();
   for (int j = wv; j < T; j += NT / 64) {
     float sq = 0.f, sk = 0.f;
     for (int c = lane; c < DK; c += 64) {
@@ -515,7 +519,7 @@ gdn_rows_kernel(RowArgs pa) {
     dot = wave_sum(dot);
     if (lane == 0) kq[j] = dot;
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- phase 3: recurrence over the state rows -----------------------------
   // Rows are taken RB at a time through all the row's tokens, so the first
@@ -610,7 +614,7 @@ gdn_rows_kernel(RowArgs pa) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- phase 4: outputs ----------------------------------------------------
   uint16_t* out = p.out;
