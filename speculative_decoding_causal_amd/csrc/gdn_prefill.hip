@@ -181,7 +181,10 @@ conv_prefill_kernel(PrefillArgs p, float* __restrict__ y, float* __restrict__ ga
   static_assert(LPH >= 4 && LPH <= 32, "head dim");
   const int C = p.C, L = p.L, W = p.W;
   const int c = (blockIdx.y * kThreads + threadIdx.x) * kCh;
-  if (c >= C) return;
+  // Threads past the last channel stay for the lane-by-lane row gather
+  // below (its values are read from lanes 0 .. 34 of every wave) and leave
+  // after it; until then they only form addresses, loading nothing.
+  const bool chan_live = c < C;
   const int row = p.unit_map[2 * blockIdx.x], seg = p.unit_map[2 * blockIdx.x + 1];
   if (row < 0) return;
   const PrefillRow pr = prefill_row(p, row);
@@ -202,8 +205,8 @@ conv_prefill_kernel(PrefillArgs p, float* __restrict__ y, float* __restrict__ ga
   };
 
   // Global rows of the positions this thread reads, one per lane in one
-  // coalesced load, then made uniform lane by lane: lanes 0..31 the
-  // segment's tokens, 32..34 the window before them, 35..50 the inputs the
+  // coalesced load, then made uniform lane by lane: lanes 0..15 the
+  // segment's tokens, 16..18 the window before them, 19..34 the inputs the
   // rolled ring takes (row positions T-L .. T-1); every position is clamped
   // into the row.  Then every vector load of the segment in one round:
   // inputs, window, taps, bias, and (for the rolling thread) the roll's
@@ -226,6 +229,7 @@ conv_prefill_kernel(PrefillArgs p, float* __restrict__ y, float* __restrict__ ga
     for (int l = 0; l < kMaxStateLen; ++l)
       ir[l] = __builtin_amdgcn_readlane(rl, kTokThread + kMaxWidth - 1 + l);
   }
+  if (!chan_live) return;
   u32x2 xv[kTokThread], hv[kMaxWidth - 1], iv[kMaxWidth - 1];
   uint16_t wr[kMaxWidth][kCh];
 #pragma unroll

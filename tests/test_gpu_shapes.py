@@ -109,3 +109,23 @@ def test_mixed_four_v_heads_per_k_head():
     slots = synth.referenced_slots(case)
     np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
     assert_states_close(g.host_ssm(slots), ssm_ref[slots])
+
+
+# (dk, Hk, Hv) whose conv channels end part-way into a wave: C/4 = 16, 96,
+# 96 and 24 threads, so the last wave has 16, 32, 32 and 24 live lanes,
+# fewer than the 35 lanes conv_prefill reads token rows from
+@pytest.mark.parametrize("dk,Hk,Hv", [(16, 1, 2), (64, 2, 2), (128, 1, 1), (32, 1, 1)])
+def test_mixed_partial_channel_wave(dk, Hk, Hv):
+    case = synth.make_case("mixed", seed=80 + dk, Ns=4, K=3, Nd=3, prefill_lens=(64, 17),
+                           Hk=Hk, Hv=Hv, dk=dk, dv=dk, num_slots=64)
+    o1, r1, s1, _ = helpers.run_nonspec(case)
+    c = helpers.clone(case)
+    c["conv_state"], c["ssm_state"] = r1, s1
+    out_ref, conv_ref, ssm_ref, _ = helpers.run_spec(c, out=o1)
+    g = Gpu(case)
+    say(f"mixed, partial channel wave dk={dk} Hk={Hk} Hv={Hv}")
+    g.attention()
+    assert_out_close(g.host_out(), out_ref)
+    slots = synth.referenced_slots(case)
+    np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
+    assert_states_close(g.host_ssm(slots), ssm_ref[slots])

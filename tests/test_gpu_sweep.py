@@ -1,0 +1,80 @@
+"""Seeded random sweep of the HIP path against the oracle: each case draws
+its head size, head grouping, K, ring length, row count, ragged row lengths,
+NULL-slot density and token order (spec batches), or its decodes and
+prefill lengths around the 64-token chunk edges (mixed batches), so that
+combinations the targeted tests pin one axis at a time also meet.  Every
+draw is printed before it runs; the seeds are fixed, so a failure names a
+case that reruns exactly."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import synth
+from tests import helpers
+from tests.gpu_util import (Gpu, assert_out_close, assert_states_close, gpu_available, say)
+from tests.test_gpu_parity import check_spec_case
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU and libgdn.so")]
+
+W = 4
+
+
+def _heads(rng, dk):
+    Hk = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4]))
+    return Hk, Hk * G
+
+
+def spec_draw(seed):
+    rng = np.random.default_rng(7000 + seed)
+    dk = int(rng.choice([16, 32, 64, 128]))
+    Hk, Hv = _heads(rng, dk)
+    K = int(rng.integers(1, 7))
+    L = min(W - 1 + K - 1 + int(rng.choice([0, 1, 3])), 16)
+    Ns = int(rng.integers(1, 11))
+    ragged = bool(rng.integers(0, 2))
+    lens = [int(x) for x in rng.integers(1, K + 1, size=Ns)] if ragged else None
+    return dict(dk=dk, dv=dk, Hk=Hk, Hv=Hv, K=K, L=L, Ns=Ns, lens=lens,
+                null_p=float(rng.choice([0.0, 0.15])), num_slots=128,
+                permute=bool(rng.integers(0, 2)))
+
+
+def mixed_draw(seed):
+    rng = np.random.default_rng(9000 + seed)
+    dk = int(rng.choice([16, 32, 64, 128]))
+    Hk, Hv = _heads(rng, dk)
+    K = int(rng.integers(2, 5))
+    Np = int(rng.integers(1, 3))
+    plens = tuple(int(x) for x in rng.choice([1, 17, 63, 64, 65, 130], size=Np))
+    return dict(dk=dk, dv=dk, Hk=Hk, Hv=Hv, K=K, Ns=int(rng.integers(1, 9)),
+                Nd=int(rng.integers(0, 9)), prefill_lens=plens, num_slots=128)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_spec_sweep(seed):
+    d = spec_draw(seed)
+    say(f"spec sweep {seed}: {d}")
+    over = {k: v for k, v in d.items() if k not in ("permute", "lens")}
+    if d["lens"] is not None:
+        over["lens"] = d["lens"]
+    case = synth.make_case("small", seed=seed, permute_tokens=d["permute"], **over)
+    check_spec_case(case)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_mixed_sweep(seed):
+    d = mixed_draw(seed)
+    say(f"mixed sweep {seed}: {d}")
+    case = synth.make_case("mixed", seed=seed, **d)
+    o1, r1, s1, _ = helpers.run_nonspec(case)
+    c = helpers.clone(case)
+    c["conv_state"], c["ssm_state"] = r1, s1
+    out_ref, conv_ref, ssm_ref, _ = helpers.run_spec(c, out=o1)
+    g = Gpu(case)
+    g.attention()
+    assert_out_close(g.host_out(), out_ref)
+    slots = synth.referenced_slots(case)
+    np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
+    assert_states_close(g.host_ssm(slots), ssm_ref[slots])
