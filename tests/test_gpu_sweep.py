@@ -12,7 +12,8 @@ import pytest
 
 import synth
 from tests import helpers
-from tests.gpu_util import (Gpu, assert_out_close, assert_states_close, gpu_available, say)
+from tests.gpu_util import (Gpu, assert_out_close, assert_states_close, gpu_available, say,
+                            spec_rows_of)
 from tests.test_gpu_parity import check_spec_case
 
 pytestmark = [pytest.mark.gpu,
@@ -73,6 +74,95 @@ def test_mixed_sweep(seed):
     c["conv_state"], c["ssm_state"] = r1, s1
     out_ref, conv_ref, ssm_ref, _ = helpers.run_spec(c, out=o1)
     g = Gpu(case)
+    g.attention()
+    assert_out_close(g.host_out(), out_ref)
+    slots = synth.referenced_slots(case)
+    np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
+    assert_states_close(g.host_ssm(slots), ssm_ref[slots])
+
+
+# ---- wider draws: layer options, the per-k-head input layout, long rows ----
+
+def _options(case, rng):
+    """Conv bias, identity activation and unnormalised q/k, each with p=1/2
+    (unnormalised keys are scaled so that |k|^2 < 1 keeps the recurrence
+    stable)."""
+    d = case["dims"]
+    d["activation"] = int(rng.integers(0, 2))
+    d["use_qk_l2norm"] = int(rng.integers(0, 2))
+    C = synth.conv_dim(d["Hk"], d["Hv"], d["dk"], d["dv"])
+    bias = bool(rng.integers(0, 2))
+    if bias:
+        case["conv_bias"] = synth.to_bf16(0.5 * rng.standard_normal(C).astype(np.float32))
+    if not d["use_qk_l2norm"]:
+        case["conv_weight"] = synth.to_bf16(synth.from_bf16(case["conv_weight"]) / 16.0)
+        if bias:
+            case["conv_bias"] = synth.to_bf16(synth.from_bf16(case["conv_bias"]) / 16.0)
+    return dict(act=d["activation"], l2norm=d["use_qk_l2norm"], bias=bias)
+
+
+def _gpu(case, per_k_head):
+    """The HIP path on the case, reading mixed_qkv in the per-k-head order
+    (repacked, reorder_input off) when asked; pools and outputs keep the
+    grouped channel order either way."""
+    if not per_k_head:
+        return Gpu(case)
+    import dataclasses
+    from tests.test_layout import per_k_head as repack
+    d = case["dims"]
+    inter = dict(case)
+    inter["mixed_qkv"] = repack(case["mixed_qkv"], d["Hk"], d["Hv"], d["dk"], d["dv"])
+    g = Gpu(inter)
+    g.cfg = dataclasses.replace(g.cfg, reorder_input=False)
+    return g
+
+
+def wide_spec_draw(seed):
+    rng = np.random.default_rng(11000 + seed)
+    dk = int(rng.choice([16, 32, 64, 128]))
+    Hk, Hv = _heads(rng, dk)
+    K = int(rng.choice([1, 2, 3, 4, 6, 8, 11, 14]))
+    L = min(W - 1 + K - 1 + int(rng.choice([0, 0, 2])), 16)
+    Ns = int(rng.integers(1, 9))
+    lens = [int(x) for x in rng.integers(1, K + 1, size=Ns)] if rng.integers(0, 2) else None
+    return rng, dict(dk=dk, dv=dk, Hk=Hk, Hv=Hv, K=K, L=L, Ns=Ns, lens=lens,
+                     null_p=float(rng.choice([0.0, 0.2])), num_slots=128,
+                     permute=bool(rng.integers(0, 2)), per_k_head=bool(rng.integers(0, 2)))
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_spec_sweep_wide(seed):
+    rng, d = wide_spec_draw(seed)
+    over = {k: v for k, v in d.items() if k not in ("permute", "lens", "per_k_head")}
+    if d["lens"] is not None:
+        over["lens"] = d["lens"]
+    case = synth.make_case("small", seed=seed, permute_tokens=d["permute"], **over)
+    opts = _options(case, rng)
+    say(f"wide spec sweep {seed}: {d} {opts}")
+    sp = case["spec"]
+    out_ref, conv_ref, ssm_ref, _ = helpers.run_spec(case, sp)
+    g = _gpu(case, d["per_k_head"])
+    g.spec()
+    rows = list(range(sp["num_spec_decodes"]))
+    glob, slots = spec_rows_of(sp, rows)
+    assert_out_close(g.host_out(), out_ref, glob)
+    np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
+    assert_states_close(g.host_ssm(slots), ssm_ref[slots])
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_mixed_sweep_wide(seed):
+    rng = np.random.default_rng(13000 + seed)
+    d = mixed_draw(100 + seed)
+    case = synth.make_case("mixed", seed=100 + seed, **d)
+    opts = _options(case, rng)
+    pkh = bool(rng.integers(0, 2))
+    say(f"wide mixed sweep {seed}: {d} {opts} per_k_head={pkh}")
+    o1, r1, s1, _ = helpers.run_nonspec(case)
+    c = helpers.clone(case)
+    c["conv_state"], c["ssm_state"] = r1, s1
+    out_ref, conv_ref, ssm_ref, _ = helpers.run_spec(c, out=o1)
+    g = _gpu(case, pkh)
     g.attention()
     assert_out_close(g.host_out(), out_ref)
     slots = synth.referenced_slots(case)
