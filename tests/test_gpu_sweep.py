@@ -168,3 +168,46 @@ def test_mixed_sweep_wide(seed):
     slots = synth.referenced_slots(case)
     np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
     assert_states_close(g.host_ssm(slots), ssm_ref[slots])
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_per_token_slots_sweep(seed):
+    # the per-token conv-slot contract (one window per token slot, L = W-1)
+    from tests.test_gpu_per_token import per_token_case
+    rng = np.random.default_rng(15000 + seed)
+    dk = int(rng.choice([16, 32, 64, 128]))
+    Hk, Hv = _heads(rng, dk)
+    K = int(rng.choice([1, 2, 3, 4, 6, 8]))
+    Ns = int(rng.integers(1, 9))
+    null_p = float(rng.choice([0.0, 0.2]))
+    say(f"per-token slots sweep {seed}: dk={dk} Hk={Hk} Hv={Hv} K={K} Ns={Ns} null_p={null_p}")
+    check_spec_case(per_token_case(15000 + seed, Ns=Ns, K=K, null_p=null_p, Hk=Hk, Hv=Hv, dk=dk))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_stage_composition_sweep(seed):
+    # gdn_conv_only then gdn_delta_rule_only give the fused spec step bit for
+    # bit (the stage kernels read their stage at run time)
+    import torch
+    import speculative_decoding_causal_amd as gdn
+    from tests.gpu_util import dev
+    from tests.test_gpu_invariants import _stage
+    d = spec_draw(100 + seed)
+    over = {k: v for k, v in d.items() if k not in ("permute", "lens")}
+    if d["lens"] is not None:
+        over["lens"] = d["lens"]
+    case = synth.make_case("small", seed=100 + seed, permute_tokens=d["permute"], **over)
+    sp = case["spec"]
+    say(f"stage composition sweep {seed}: {d}")
+    fused = Gpu(case)
+    fused.spec()
+    staged = Gpu(case)
+    T = sp["num_spec_tokens"]
+    y = torch.zeros(staged.qkv.shape[0], staged.cfg.conv_dim, dtype=torch.float32, device=dev())
+    meta = dict(qsl=sp["spec_query_start_loc"], ssi=sp["spec_state_indices"],
+                nacc=sp["num_accepted_tokens"], tix=sp.get("spec_token_indx"),
+                cache=sp.get("spec_cache_indices"))
+    _stage(staged, gdn.GDN_ROWS_SPEC, meta, T, y, sp["spec_state_indices"].shape[1])
+    np.testing.assert_array_equal(fused.host_out(), staged.host_out())
+    np.testing.assert_array_equal(fused.host_conv(), staged.host_conv())
+    np.testing.assert_array_equal(fused.host_ssm(), staged.host_ssm())
