@@ -236,7 +236,8 @@ def make_case(name: str, seed: int = 0, permute_tokens: bool = False,
         lens = [K] * Ns + ns_lens
         per_row = compose_rows(rng, kinds, lens)
         T = int(sum(lens))
-        spec["spec_token_indx"] = np.concatenate(per_row[:Ns]).astype(np.int32)
+        spec["spec_token_indx"] = (np.concatenate(per_row[:Ns]).astype(np.int32) if Ns
+                                   else np.zeros(0, np.int32))
         qsl = np.zeros(Nd + Np + 1, np.int32)
         qsl[1:] = np.cumsum(ns_lens)
         his = np.ones(Nd + Np, np.uint8)

@@ -211,3 +211,27 @@ def test_stage_composition_sweep(seed):
     np.testing.assert_array_equal(fused.host_out(), staged.host_out())
     np.testing.assert_array_equal(fused.host_conv(), staged.host_conv())
     np.testing.assert_array_equal(fused.host_ssm(), staged.host_ssm())
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_nonspec_only_sweep(seed):
+    # decodes and prefills with no spec rows: the decodes launch alone, before
+    # the prefill kernels; prefill lengths up to past 1024 tokens
+    rng = np.random.default_rng(17000 + seed)
+    dk = int(rng.choice([16, 32, 64, 128]))
+    Hk, Hv = _heads(rng, dk)
+    Np = int(rng.integers(1, 4))
+    plens = tuple(int(x) for x in rng.choice([1, 2, 63, 64, 65, 129, 300, 1025], size=Np))
+    d = dict(dk=dk, dv=dk, Hk=Hk, Hv=Hv, K=2, Ns=0, Nd=int(rng.integers(0, 9)),
+             prefill_lens=plens, num_slots=64)
+    say(f"non-spec only sweep {seed}: {d}")
+    case = synth.make_case("mixed", seed=17000 + seed, **d)
+    out_ref, conv_ref, ssm_ref, _ = helpers.run_nonspec(case)
+    g = Gpu(case)
+    g.attention(spec=None)
+    ns = case["nonspec"]
+    rows = ns["token_indx"]
+    assert_out_close(g.host_out()[rows], out_ref[rows])
+    slots = synth.referenced_slots(case)
+    np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
+    assert_states_close(g.host_ssm(slots), ssm_ref[slots])
