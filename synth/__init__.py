@@ -246,7 +246,8 @@ def make_case(name: str, seed: int = 0, permute_tokens: bool = False,
         nonspec = dict(num_decodes=Nd, num_prefills=Np,
                        num_non_spec_tokens=int(qsl[-1]), query_start_loc=qsl,
                        cache_indices=ns_slots, has_initial_state=his,
-                       token_indx=np.concatenate(per_row[Ns:]).astype(np.int32))
+                       token_indx=(np.concatenate(per_row[Ns:]).astype(np.int32)
+                                   if Nd + Np else np.zeros(0, np.int32)))
         case.update(_params(rng, d, T))
         case["spec"] = spec
         case["nonspec"] = nonspec

@@ -293,3 +293,86 @@ def test_binding_stage_entry_points_check_sizes():
         gdn.gdn_delta_rule_only(cfg, conv_out, t["a"], t["b"], t["A_log"], t["dt_bias"],
                                 t["ssm_state"][:, :, :, :8], t["core_attn_out"], state_len=5,
                                 **rows)
+
+
+# ---- metadata checker fuzz: seeded valid batches pass; one corruption each
+# is rejected with its own message ----
+
+def _fuzz_batch(seed):
+    import synth
+    rng = np.random.default_rng(21000 + seed)
+    Ns, K, Nd = int(rng.integers(1, 7)), int(rng.integers(1, 5)), int(rng.integers(0, 5))
+    plens = tuple(int(x) for x in rng.integers(1, 40, size=int(rng.integers(0, 3))))
+    case = synth.make_case("mixed", seed=seed, with_pools=False, Ns=Ns, K=K, Nd=Nd,
+                           prefill_lens=plens, Hk=2, Hv=4, dk=16, dv=16, num_slots=64)
+    sp, ns, d = case["spec"], case["nonspec"], case["dims"]
+    cfg = gdn.GdnConfig(d["Hk"], d["Hv"], d["dk"], d["dv"])
+    meta = dict(num_decodes=ns["num_decodes"], num_prefills=ns["num_prefills"],
+                query_start_loc=ns["query_start_loc"].copy(),
+                non_spec_state_indices=ns["cache_indices"].copy(),
+                non_spec_token_indx=ns["token_indx"].copy(),
+                spec_query_start_loc=sp["spec_query_start_loc"].copy(),
+                spec_state_indices=sp["spec_state_indices"].copy(),
+                num_accepted_tokens=sp["num_accepted_tokens"].copy(),
+                spec_token_indx=sp["spec_token_indx"].copy())
+    nat = int(case["mixed_qkv"].shape[0])
+    return rng, cfg, d, nat, meta
+
+
+def _fuzz_check(cfg, d, nat, meta):
+    return gdn.gdn_check_metadata_host(cfg, d["L"], d["num_slots"], nat, **meta)
+
+
+def _corrupt(rng, d, nat, m):
+    """One violation; returns the text the checker's message must hold."""
+    sq, ssi, nacc = m["spec_query_start_loc"], m["spec_state_indices"], m["num_accepted_tokens"]
+    tix, ntix = m["spec_token_indx"], m["non_spec_token_indx"]
+    Ns = len(nacc)
+    slot_rows = [r for r in range(Ns) if (ssi[r] > 0).any()]
+    kinds = ["nacc_low", "nacc_high", "slot_range", "tix_outside"]
+    if len(slot_rows) >= 2:
+        kinds.append("slot_shared")
+    if len(tix) + len(ntix) >= 2:
+        kinds.append("tix_twice")
+    if m["num_decodes"] > 0:
+        kinds += ["decode_len", "qsl_decreases"]
+    kind = kinds[int(rng.integers(0, len(kinds)))]
+    b = int(rng.integers(0, Ns))
+    if kind == "nacc_low":
+        nacc[b] = 0
+        return "num_accepted_tokens"
+    if kind == "nacc_high":
+        nacc[b] = int(sq[b + 1] - sq[b]) + 1
+        return "num_accepted_tokens"
+    if kind == "slot_range":
+        ssi[b, 0] = d["num_slots"]
+        return "num_slots"
+    if kind == "slot_shared":
+        r0, r1 = slot_rows[0], slot_rows[1]
+        ssi[r1, int(np.argmax(ssi[r1] > 0))] = int(ssi[r0][ssi[r0] > 0][0])
+        return "two rows"
+    if kind == "tix_twice":
+        if len(tix) >= 2:
+            tix[1] = tix[0]
+        else:
+            ntix[0] = tix[0]
+        return "mapped twice"
+    if kind == "tix_outside":
+        tix[0] = nat
+        return "outside"
+    q = m["query_start_loc"]
+    if kind == "decode_len":
+        q[1:] += 1                          # the first decode row holds two tokens
+        m["non_spec_token_indx"] = np.append(ntix, nat - 1)
+        return "decode row"
+    q[1] = -1                               # kind == "qsl_decreases"
+    return "decreases"
+
+
+@pytest.mark.parametrize("seed", range(120))
+def test_metadata_checker_fuzz(seed):
+    rng, cfg, d, nat, meta = _fuzz_batch(seed)
+    assert _fuzz_check(cfg, d, nat, meta) == gdn.GDN_OK, gdn.gdn_last_error()
+    needle = _corrupt(rng, d, nat, meta)
+    assert _fuzz_check(cfg, d, nat, meta) == gdn.GDN_ERR_METADATA
+    assert needle in gdn.gdn_last_error(), (needle, gdn.gdn_last_error())

@@ -235,3 +235,18 @@ def test_nonspec_only_sweep(seed):
     slots = synth.referenced_slots(case)
     np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
     assert_states_close(g.host_ssm(slots), ssm_ref[slots])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_spec_many_rows_sweep(seed):
+    # hundreds of rows on small heads: grids far larger than one per CU,
+    # slot and token indices in the thousands
+    rng = np.random.default_rng(19000 + seed)
+    dk = int(rng.choice([16, 32]))
+    Hk, Hv = _heads(rng, dk)
+    K = int(rng.integers(1, 5))
+    Ns = int(rng.integers(100, 301))
+    d = dict(dk=dk, dv=dk, Hk=Hk, Hv=Hv, K=K, Ns=Ns, num_slots=Ns * K + 9,
+             null_p=float(rng.choice([0.0, 0.1])))
+    say(f"many-row spec sweep {seed}: {d}")
+    check_spec_case(synth.make_case("small", seed=19000 + seed, permute_tokens=True, **d))
