@@ -250,3 +250,38 @@ def test_spec_many_rows_sweep(seed):
              null_p=float(rng.choice([0.0, 0.1])))
     say(f"many-row spec sweep {seed}: {d}")
     check_spec_case(synth.make_case("small", seed=19000 + seed, permute_tokens=True, **d))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_conv_width_sweep(seed):
+    # conv widths 1 .. 4 (width 1 has no history ring: L = 0 is allowed)
+    rng = np.random.default_rng(23000 + seed)
+    Wc = int(rng.integers(1, 5))
+    dk = int(rng.choice([16, 32, 64, 128]))
+    Hk, Hv = _heads(rng, dk)
+    if seed % 2 == 0:
+        K = int(rng.integers(1, 5))
+        L = min(Wc - 1 + K - 1 + int(rng.choice([0, 2])), 16)
+        d = dict(dk=dk, dv=dk, Hk=Hk, Hv=Hv, K=K, L=L, W=Wc, Ns=int(rng.integers(1, 9)),
+                 null_p=0.1, num_slots=64)
+        say(f"conv width sweep {seed} (spec): {d}")
+        check_spec_case(synth.make_case("small", seed=23000 + seed, permute_tokens=True, **d))
+        return
+    plens = tuple(int(x) for x in rng.choice([1, 2, 3, 17, 64, 65], size=int(rng.integers(1, 3))))
+    K = int(rng.integers(1, 4))
+    d = dict(dk=dk, dv=dk, Hk=Hk, Hv=Hv, K=K, L=Wc - 1 + K - 1, W=Wc, Ns=int(rng.integers(0, 5)),
+             Nd=int(rng.integers(0, 5)), prefill_lens=plens, num_slots=64)
+    say(f"conv width sweep {seed} (mixed): {d}")
+    case = synth.make_case("mixed", seed=23000 + seed, **d)
+    o1, r1, s1, _ = helpers.run_nonspec(case)
+    c = helpers.clone(case)
+    c["conv_state"], c["ssm_state"] = r1, s1
+    out_ref, conv_ref, ssm_ref, _ = (helpers.run_spec(c, out=o1) if d["Ns"] else
+                                     (o1, r1, s1, None))
+    g = Gpu(case)
+    g.attention(spec="case" if d["Ns"] else None)
+    rows = np.concatenate([case["nonspec"]["token_indx"], case["spec"]["spec_token_indx"]])
+    assert_out_close(g.host_out()[rows], out_ref[rows])
+    slots = synth.referenced_slots(case)
+    np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
+    assert_states_close(g.host_ssm(slots), ssm_ref[slots])
