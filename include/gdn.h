@@ -43,7 +43,8 @@
  *    out-of-range access (results are then unspecified).  gdn_check_metadata_host
  *    checks them on host copies.
  *  - Pools: conv_state [num_slots, state_len, C] bf16 (channel-contiguous
- *    ring, column 0 oldest); ssm_state [num_slots, Hv, dv, dk] fp32.  A slot
+ *    ring, column 0 oldest; may be NULL when state_len is 0, a width-1 conv
+ *    that keeps no history); ssm_state [num_slots, Hv, dv, dk] fp32.  A slot
  *    value <= 0 is NULL_BLOCK_ID / pad slot: nothing is read (zeros are used)
  *    and nothing is written [P1 "Changes"; P2 review thread].  Rows of one
  *    call must use disjoint slots.

@@ -160,14 +160,17 @@ int check_spec(const SpecBatch& s, int num_actual_tokens) {
   return GDN_OK;
 }
 
-int check_layer_ptrs(const void* qkv, const void* a, const void* b, const void* w,
-                     const void* A_log, const void* dt_bias, const void* conv_state,
-                     const void* ssm_state, const void* out) {
+// conv_state may be NULL when state_len is 0 (a width-1 conv keeps no
+// history: the pool has no bytes and is never touched).
+int check_layer_ptrs(const gdn_dims* d, const void* qkv, const void* a, const void* b,
+                     const void* w, const void* A_log, const void* dt_bias,
+                     const void* conv_state, const void* ssm_state, const void* out) {
   if (!qkv) return fail(GDN_ERR_NULL, "mixed_qkv is NULL");
   if (!a || !b) return fail(GDN_ERR_NULL, "gate tensors a/b are NULL");
   if (!w) return fail(GDN_ERR_NULL, "conv_weight is NULL");
   if (!A_log || !dt_bias) return fail(GDN_ERR_NULL, "A_log/dt_bias is NULL");
-  if (!conv_state || !ssm_state) return fail(GDN_ERR_NULL, "state pool is NULL");
+  if ((!conv_state && d->state_len > 0) || !ssm_state)
+    return fail(GDN_ERR_NULL, "state pool is NULL");
   if (!out) return fail(GDN_ERR_NULL, "core_attn_out is NULL");
   return GDN_OK;
 }
@@ -292,7 +295,7 @@ int gdn_spec_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
   if (num_spec_decodes == 0) return GDN_OK;
   if (dims->conv_layout == GDN_CONV_PER_TOKEN_SLOTS && spec_cache_indices)
     return fail(GDN_ERR_DIMS, "spec_cache_indices is not used with per-token conv slots");
-  if (int e = check_layer_ptrs(mixed_qkv, a, b, conv_weight, A_log, dt_bias, conv_state,
+  if (int e = check_layer_ptrs(dims, mixed_qkv, a, b, conv_weight, A_log, dt_bias, conv_state,
                                ssm_state, core_attn_out))
     return e;
   Layer L{dims, mixed_qkv, a, b, conv_weight, conv_bias, A_log, dt_bias,
@@ -349,7 +352,7 @@ int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
     return fail(GDN_ERR_MISSING_OPTIONAL,
                 "a batch with both streams needs spec_token_indx and non_spec_token_indx");
   if (num_actual_tokens == 0) return GDN_OK;
-  if (int e = check_layer_ptrs(mixed_qkv, a, b, conv_weight, A_log, dt_bias, conv_state,
+  if (int e = check_layer_ptrs(dims, mixed_qkv, a, b, conv_weight, A_log, dt_bias, conv_state,
                                ssm_state, core_attn_out))
     return e;
   if (num_prefills > 0) {
@@ -494,7 +497,7 @@ int gdn_conv_only(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
   gdn::RowArgs r{};
   if (int e = stage_rows(dims, rows, num_actual_tokens, r)) return e;
   if (r.num_rows == 0) return GDN_OK;
-  if (!mixed_qkv || !conv_weight || !conv_state || !conv_out)
+  if (!mixed_qkv || !conv_weight || (!conv_state && dims->state_len > 0) || !conv_out)
     return fail(GDN_ERR_NULL, "mixed_qkv, conv_weight, conv_state and conv_out are required");
   r.qkv = mixed_qkv;
   r.conv_w = conv_weight;

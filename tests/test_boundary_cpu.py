@@ -376,3 +376,16 @@ def test_metadata_checker_fuzz(seed):
     needle = _corrupt(rng, d, nat, meta)
     assert _fuzz_check(cfg, d, nat, meta) == gdn.GDN_ERR_METADATA
     assert needle in gdn.gdn_last_error(), (needle, gdn.gdn_last_error())
+
+
+def test_conv_pool_may_be_null_only_without_history():
+    # a width-1 conv with state_len 0 keeps no ring: a NULL conv pool passes
+    # the pointer checks (this call then stops at its missing workspace);
+    # with a ring it is rejected
+    def call(d):
+        return L.gdn_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None,
+                               FAKE, 16, 2, 1, 6, FAKE, FAKE, None, FAKE, 2, 10, 5, FAKE,
+                               None, FAKE, FAKE, FAKE, FAKE, None, ctypes.c_size_t(0), None)
+    assert call(dims(conv_width=1, state_len=0)) == gdn.GDN_ERR_WORKSPACE
+    assert call(dims()) == gdn.GDN_ERR_NULL
+    assert "state pool" in gdn.gdn_last_error()

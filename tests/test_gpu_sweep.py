@@ -285,3 +285,24 @@ def test_conv_width_sweep(seed):
     slots = synth.referenced_slots(case)
     np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
     assert_states_close(g.host_ssm(slots), ssm_ref[slots])
+
+
+@pytest.mark.parametrize("kind", ["spec", "mixed"])
+def test_width_one_without_ring(kind):
+    # conv width 1 with state_len 0: the conv pool holds no bytes (its
+    # pointer is NULL) and the step still matches the oracle
+    d = dict(W=1, K=1, L=0, Hk=2, Hv=4, dk=32, dv=32, num_slots=32)
+    say(f"width-1 conv without a ring ({kind})")
+    if kind == "spec":
+        check_spec_case(synth.make_case("small", seed=25000, Ns=6, permute_tokens=True, **d))
+        return
+    case = synth.make_case("mixed", seed=25001, Ns=3, Nd=3, prefill_lens=(17, 65), **d)
+    o1, r1, s1, _ = helpers.run_nonspec(case)
+    c = helpers.clone(case)
+    c["conv_state"], c["ssm_state"] = r1, s1
+    out_ref, _, ssm_ref, _ = helpers.run_spec(c, out=o1)
+    g = Gpu(case)
+    g.attention()
+    assert_out_close(g.host_out(), out_ref)
+    slots = synth.referenced_slots(case)
+    assert_states_close(g.host_ssm(slots), ssm_ref[slots])
