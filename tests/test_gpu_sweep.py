@@ -24,15 +24,22 @@ W = 4
 
 def _heads(rng, dk):
     Hk = int(rng.choice([1, 2, 4]))
-    G = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 8]))   # up to 1024 state rows per k-head at dk 128
     return Hk, Hk * G
+
+
+def _fit_lds(K, dk, Hk, Hv, k_max_at_1024_rows):
+    # 1024 state rows per k-head (dk 128, 8 v-heads per k-head) stage 8 KiB
+    # of v and outputs per token in LDS: longer rows exceed it and are
+    # rejected (GDN_ERR_UNSUPPORTED), so the draw keeps them within it
+    return min(K, k_max_at_1024_rows) if dk * (Hv // Hk) == 1024 else K
 
 
 def spec_draw(seed):
     rng = np.random.default_rng(7000 + seed)
     dk = int(rng.choice([16, 32, 64, 128]))
     Hk, Hv = _heads(rng, dk)
-    K = int(rng.integers(1, 7))
+    K = _fit_lds(int(rng.integers(1, 7)), dk, Hk, Hv, 8)
     L = min(W - 1 + K - 1 + int(rng.choice([0, 1, 3])), 16)
     Ns = int(rng.integers(1, 11))
     ragged = bool(rng.integers(0, 2))
@@ -121,7 +128,7 @@ def wide_spec_draw(seed):
     rng = np.random.default_rng(11000 + seed)
     dk = int(rng.choice([16, 32, 64, 128]))
     Hk, Hv = _heads(rng, dk)
-    K = int(rng.choice([1, 2, 3, 4, 6, 8, 11, 14]))
+    K = _fit_lds(int(rng.choice([1, 2, 3, 4, 6, 8, 11, 14])), dk, Hk, Hv, 8)
     L = min(W - 1 + K - 1 + int(rng.choice([0, 0, 2])), 16)
     Ns = int(rng.integers(1, 9))
     lens = [int(x) for x in rng.integers(1, K + 1, size=Ns)] if rng.integers(0, 2) else None
@@ -177,7 +184,7 @@ def test_per_token_slots_sweep(seed):
     rng = np.random.default_rng(15000 + seed)
     dk = int(rng.choice([16, 32, 64, 128]))
     Hk, Hv = _heads(rng, dk)
-    K = int(rng.choice([1, 2, 3, 4, 6, 8]))
+    K = _fit_lds(int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16])), dk, Hk, Hv, 12)   # ring: W-1
     Ns = int(rng.integers(1, 9))
     null_p = float(rng.choice([0.0, 0.2]))
     say(f"per-token slots sweep {seed}: dk={dk} Hk={Hk} Hv={Hv} K={K} Ns={Ns} null_p={null_p}")
