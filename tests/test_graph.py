@@ -186,3 +186,21 @@ def test_graph_padded_prefills_replays():
     # captured step; the real prefill rows change length replay by replay
     _run_graph(True, [(330, 8, 6, [130, 64]), (331, 3, 4, [65]), (332, 5, 0, []),
                       (333, 0, 2, [1, 199]), (334, 8, 6, [200])])
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_graph_random_replays(seed):
+    # one captured step (decodes + prefills + spec rows at their padded
+    # sizes) replayed over six seeded batches: any number of real spec rows
+    # and decodes up to the pads (none included), up to two prefill rows
+    # whose lengths fit the token budget
+    rng = np.random.default_rng(340 + seed)
+    plan = []
+    for i in range(6):
+        n_pf = int(rng.integers(0, NP_PAD))
+        cuts = np.sort(rng.integers(0, PF_TOK + 1, size=n_pf))
+        pf = [int(x) for x in np.diff(np.concatenate([[0], cuts])) if x > 0]
+        plan.append((3400 + 10 * seed + i, int(rng.integers(0, NS_PAD + 1)),
+                     int(rng.integers(0, ND_PAD + 1)), pf))
+    say(f"random graph plan {seed}: {plan}")
+    _run_graph(True, plan)
