@@ -2,7 +2,7 @@
 bit): spec verify with all tokens accepted equals sequential decodes; K=1
 spec equals a decode on a minimal ring; rollback equals decodes over the
 accepted prefix; the stage entry points compose to the fused step; ten runs
-are byte-identical; token_indx permutations and the mixed layouts printed on
+are byte-identical; unit gates with orthonormal keys recall v exactly; token_indx permutations and the mixed layouts printed on
 the gate-fix page equal per-subset runs; a rejected call touches nothing."""
 from __future__ import annotations
 
@@ -146,6 +146,60 @@ def test_ten_runs_byte_identical(K):
         else:
             for x, y in zip(first, got):
                 assert x.tobytes() == y.tobytes()
+
+
+def test_exact_recall_unit_gates_one_hot_keys():
+    # With alpha = beta = 1 and orthonormal keys the delta rule writes token
+    # t's value into column k_t alone: reading with q_t = k_t returns v_t
+    # exactly (bf16 outputs bit-equal to v_t), and each stored state holds
+    # the rank-one writes so far, v_s in column k_s, zeros elsewhere.  Run
+    # through the delta-rule stage, which takes the conv output as given, on
+    # spec rows with a NULL load slot and permuted tokens.
+    import speculative_decoding_causal_amd as gdn
+    K, Ns = 4, 2
+    T = Ns * K
+    case = qcase(150, K, T, use_qk_l2norm=0, scale=1.0)
+    d = case["dims"]
+    Hk, Hv, dk, dv = d["Hk"], d["Hv"], d["dk"], d["dv"]
+    G, C = Hv // Hk, synth.conv_dim(Hk, Hv, dk, dv)
+    rng = np.random.default_rng(151)
+    # softplus(-100) is below fp32's smallest normal, so alpha = exp(-that)
+    # rounds to 1; sigmoid(100) rounds to 1
+    case["a"] = synth.to_bf16(np.full((T, Hv), -100.0, np.float32))
+    case["b"] = synth.to_bf16(np.full((T, Hv), 100.0, np.float32))
+    case["A_log"] = np.zeros(Hv, np.float32)
+    case["dt_bias"] = np.zeros(Hv, np.float32)
+    tix = rng.permutation(T).astype(np.int32)
+    ssi = np.array([[0, 3, 4, 5], [0, 7, 8, 9]], np.int32)
+    v = synth.from_bf16(synth.to_bf16(rng.standard_normal((T, Hv, dv)).astype(np.float32)))
+    cols = rng.permuted(np.tile(np.arange(dk), (Ns, Hk, 1)), axis=2)[:, :, :K]
+    y = np.zeros((T, C), np.float32)
+    for bb in range(Ns):
+        for t in range(K):
+            r = tix[bb * K + t]
+            for i in range(Hk):
+                y[r, i * dk + cols[bb, i, t]] = 1.0            # q
+                y[r, (Hk + i) * dk + cols[bb, i, t]] = 1.0     # k
+            y[r, 2 * Hk * dk:] = v[bb * K + t].reshape(-1)
+    g = Gpu(case)
+    say("exact recall, delta-rule stage")
+    gdn.gdn_delta_rule_only(g.cfg, torch.from_numpy(y).to(dev()), g.a, g.b, g.A_log, g.dt_bias,
+                            g.ssm, g.out, kind=gdn.GDN_ROWS_SPEC,
+                            query_start_loc=i32([0, K, 2 * K]), num_tokens=T,
+                            max_row_tokens=K, state_indices=i32(ssi),
+                            num_accepted_tokens=i32([1] * Ns), token_indx=i32(tix),
+                            state_len=d["L"])
+    out = g.host_out()  # raw bf16 bits
+    for j in range(T):
+        np.testing.assert_array_equal(out[tix[j]], synth.to_bf16(v[j]))
+    for bb in range(Ns):
+        got = g.host_ssm(ssi[bb, 1:])
+        for t in range(1, K):
+            want = np.zeros((Hv, dv, dk), np.float32)
+            for s in range(t + 1):
+                for h in range(Hv):
+                    want[h, :, cols[bb, h // G, s]] = v[bb * K + s, h]
+            np.testing.assert_array_equal(got[t - 1], want)
 
 
 def test_token_permutation_invariance():
