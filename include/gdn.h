@@ -77,7 +77,11 @@ enum {
                                     [P2 commit message] */
   GDN_ERR_WORKSPACE = -6,        /* workspace NULL or too small */
   GDN_ERR_HIP = -7,              /* a HIP launch failed */
-  GDN_ERR_UNSUPPORTED = -8,      /* shape outside what the kernels support */
+  GDN_ERR_UNSUPPORTED = -8,      /* shape outside what the kernels support,
+                                    launch sizes included: at most 2^22
+                                    (row, k-head) workgroups per row launch,
+                                    65535 64-token prefill units, 2^24
+                                    conv channels */
   GDN_ERR_METADATA = -9          /* gdn_check_metadata_host found a violation */
 };
 

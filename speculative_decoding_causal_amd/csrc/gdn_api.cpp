@@ -54,6 +54,14 @@ hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes) {
 
 namespace {
 
+// Launch limits: a row launch is one workgroup of up to 1024 threads per
+// (row, k-head) and a dispatch holds fewer than 2^32 work-items; the chunk
+// kernels put the 64-token units of the prefill rows on grid dimension y,
+// which holds at most 65535.
+constexpr int kMaxConvDim = 1 << 24;
+constexpr long long kMaxRowWorkgroups = 1LL << 22;
+constexpr long long kMaxPrefillUnits = 65535;
+
 int check_dims(const gdn_dims* d) {
   if (!d) return fail(GDN_ERR_NULL, "dims is NULL");
   if (d->num_k_heads <= 0 || d->num_v_heads <= 0)
@@ -91,6 +99,10 @@ int check_dims(const gdn_dims* d) {
   const int G = d->num_v_heads / d->num_k_heads;
   if (G * d->head_v_dim > 1024)
     return fail(GDN_ERR_UNSUPPORTED, "(Hv/Hk)*head_v_dim = %d exceeds 1024", G * d->head_v_dim);
+  // channel indices are 32-bit inside the kernels
+  const long long C = (long long)d->num_k_heads * (2 * d->head_k_dim + G * d->head_v_dim);
+  if (C > kMaxConvDim)
+    return fail(GDN_ERR_UNSUPPORTED, "conv dim %lld exceeds %d channels", C, kMaxConvDim);
   return GDN_OK;
 }
 
@@ -116,7 +128,12 @@ void fill_common(gdn::RowArgs& a, const gdn_dims* d, int num_actual_tokens) {
   a.num_actual_tokens = num_actual_tokens;
 }
 
-int lds_ok(const gdn::RowArgs& a, const gdn_dims* d) {
+int rows_launch_ok(const gdn::RowArgs& a, const gdn_dims* d) {
+  const long long wgs =
+      ((long long)a.num_rows + (a.more.num_rows > 0 ? a.more.num_rows : 0)) * a.Hk;
+  if (wgs > kMaxRowWorkgroups)
+    return fail(GDN_ERR_UNSUPPORTED, "row launch of %lld workgroups (rows x k-heads) exceeds %lld",
+                wgs, kMaxRowWorkgroups);
   size_t need = gdn::rows_lds_bytes(a, d->head_k_dim, d->head_v_dim);
   if (need > 160 * 1024)
     return fail(GDN_ERR_UNSUPPORTED, "row kernel needs %zu bytes of LDS (max 163840)", need);
@@ -238,7 +255,7 @@ gdn::RowArgs spec_rows(const Layer& L, const SpecBatch& s, const gdn::RowArgs* d
 int run_spec(const Layer& L, const SpecBatch& s, hipStream_t stream) {
   if (s.num_spec_decodes == 0) return GDN_OK;
   const gdn::RowArgs r = spec_rows(L, s);
-  if (int e = lds_ok(r, L.d)) return e;
+  if (int e = rows_launch_ok(r, L.d)) return e;
   return launch(gdn::launch_rows(r, L.d->head_k_dim, L.d->head_v_dim, stream),
                 "spec row kernel");
 }
@@ -360,6 +377,10 @@ int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
     if (!workspace || workspace_bytes < need)
       return fail(GDN_ERR_WORKSPACE, "prefill rows need %zu bytes of workspace (got %zu)",
                   need, workspace ? workspace_bytes : (size_t)0);
+    const long long units = ((long long)num_non_spec_tokens + 63) / 64 + num_prefills;
+    if (units > kMaxPrefillUnits)
+      return fail(GDN_ERR_UNSUPPORTED, "prefill rows span up to %lld 64-token units (max %lld)",
+                  units, kMaxPrefillUnits);
   }
   Layer L{dims, mixed_qkv, a, b, conv_weight, conv_bias, A_log, dt_bias,
           conv_state, ssm_state, core_attn_out, num_actual_tokens};
@@ -387,11 +408,11 @@ int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
   gdn::RowArgs rows_after{};
   if (s.num_spec_decodes > 0) {
     rows_after = spec_rows(L, s, merged ? &dec : nullptr);
-    if (int e = lds_ok(rows_after, dims)) return e;
+    if (int e = rows_launch_ok(rows_after, dims)) return e;
   }
   const bool decodes_alone = num_decodes > 0 && !merged;
   if (decodes_alone) {
-    if (int e = lds_ok(dec, dims)) return e;
+    if (int e = rows_launch_ok(dec, dims)) return e;
   }
   if (num_prefills > 0 && dims->head_k_dim >= 64) {
     if (int e = launch(gdn::prepare_chunked(dims->head_k_dim, dims->head_v_dim),
@@ -487,7 +508,7 @@ static int stage_rows(const gdn_dims* dims, const gdn_rows* rows, int num_actual
   r.nacc = rows->num_accepted_tokens;
   r.his = rows->has_initial_state;
   r.tix = rows->token_indx;
-  return lds_ok(r, dims);
+  return rows_launch_ok(r, dims);
 }
 
 int gdn_conv_only(const gdn_dims* dims, const gdn_bf16* mixed_qkv,

@@ -110,6 +110,24 @@ def test_bad_counts_rejected():
     assert spec_call(dims(), qkv=None) == gdn.GDN_ERR_NULL
 
 
+def test_launch_sizes_checked_before_any_launch():
+    # limits of the launch shapes are rejected on the host, not left to a
+    # launch that would fail part-way through a call
+    huge = dims(num_k_heads=1 << 20, num_v_heads=1 << 20)
+    assert spec_call(huge) == gdn.GDN_ERR_UNSUPPORTED
+    assert "conv dim" in gdn.gdn_last_error()
+    ns = (1 << 22) // 16 + 1        # rows x 16 k-heads just past 2^22 workgroups
+    assert spec_call(dims(), Ns=ns, T=ns, K=1, nat=ns) == gdn.GDN_ERR_UNSUPPORTED
+    assert "workgroups" in gdn.gdn_last_error()
+    d = dims()
+    nns = 1 << 22                   # 65536 units of 64 tokens, one prefill row
+    need = L.gdn_workspace_bytes(ctypes.byref(d), nns, 1)
+    rc = attn_call(d, nat=nns, nd=0, npf=1, nns=nns, Ns=0, Ts=0, K=0, sqsl=None, ssi=None,
+                   nacc=None, stix=None, ws=FAKE, ws_bytes=need)
+    assert rc == gdn.GDN_ERR_UNSUPPORTED, gdn.gdn_last_error()
+    assert "units" in gdn.gdn_last_error()
+
+
 def test_row_kernel_lds_checked_before_any_launch():
     # 8 v-heads on one k-head with 14-token spec rows need more LDS than a
     # CU has: the call is rejected before the prefill kernels are enqueued
