@@ -134,6 +134,33 @@ def profiled_traffic(workload):
     return rec.get("bytes_per_launch") if rec.get("source_sha256_16") == cur else None
 
 
+def same_box_ceilings(stream, achieved_gbs, mib=256, reps=20):
+    """Plain torch copy and fill rates on this GPU (context for the HBM peak:
+    what streaming kernels with no arithmetic reach here), timed with events
+    on the launch stream."""
+    import torch
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    rates = {}
+    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * n * 4),
+                            ("fill", lambda: dst.fill_(1.0), n * 4)):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        rates[name] = moved * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    return {"copy_GBs": rates["copy"], "fill_GBs": rates["fill"],
+            "frac_of_copy": achieved_gbs / rates["copy"],
+            "frac_of_fill": achieved_gbs / rates["fill"],
+            "what": f"torch copy_ of {mib} MiB (read + write counted) and fill_ of {mib} MiB, "
+                    f"{reps} each"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,6 +304,7 @@ def main():
                      "p10_launch_us": float(np.percentile(launch_ms, 10)) * 1e3,
                      "p90_launch_us": float(np.percentile(launch_ms, 90)) * 1e3},
     }
+    result["roofline"]["same_box"] = same_box_ceilings(stream, achieved)
     if ns is None and args.workload != DEFAULT_WORKLOAD:
         # the headline metric names its own batch; other spec batches say theirs
         result["metric"] = (f"GDN layer tokens/sec + us/layer + % HBM peak, spec verify "
