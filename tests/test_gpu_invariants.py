@@ -2,7 +2,8 @@
 bit): spec verify with all tokens accepted equals sequential decodes; K=1
 spec equals a decode on a minimal ring; rollback equals decodes over the
 accepted prefix; the stage entry points compose to the fused step; ten runs
-are byte-identical; unit gates with orthonormal keys recall v exactly; token_indx permutations and the mixed layouts printed on
+are byte-identical; unit gates with orthonormal keys recall v exactly;
+garbage metadata values stay inside the tensors; token_indx permutations and the mixed layouts printed on
 the gate-fix page equal per-subset runs; a rejected call touches nothing."""
 from __future__ import annotations
 
@@ -200,6 +201,71 @@ def test_exact_recall_unit_gates_one_hot_keys():
                 for h in range(Hv):
                     want[h, :, cols[bb, h // G, s]] = v[bb * K + s, h]
             np.testing.assert_array_equal(got[t - 1], want)
+
+
+def _guarded(t, fill, guard=8192):
+    # t's values inside a buffer with `guard` canary elements on each side
+    n = t.numel()
+    buf = torch.full((n + 2 * guard,), fill, dtype=t.dtype, device=t.device)
+    buf[guard:guard + n].copy_(t.reshape(-1))
+    return buf, buf[guard:guard + n].view(t.shape)
+
+
+def _guards_intact(buf, n, fill, guard=8192):
+    want = torch.full((guard,), fill, dtype=buf.dtype, device=buf.device)
+    return torch.equal(buf[:guard], want) and torch.equal(buf[guard + n:], want)
+
+
+def _junk(rng, n, lo, hi):
+    # per element one of: in range, any int32, -1, the first value past the
+    # range, small values around zero
+    pools = [rng.integers(lo, hi, n), rng.integers(-2 ** 31, 2 ** 31 - 1, n),
+             np.full(n, -1), np.full(n, hi), rng.integers(-5, 5, n)]
+    pick = rng.integers(0, len(pools), n)
+    return np.array([pools[k][i] for i, k in enumerate(pick)], np.int32)
+
+
+@pytest.mark.parametrize("seed,decodes", [(0, 0), (1, 0), (2, 0), (3, 5), (4, 5)])
+def test_garbage_metadata_stays_in_bounds(seed, decodes):
+    # Metadata values live in device memory and are not checked by the step
+    # (the host checker is separate): the kernels clamp query_start_loc,
+    # slots, num_accepted_tokens and token rows, so any values leave the
+    # results unspecified but every access inside the tensors.  Checked with
+    # canaries around the pools and the output.
+    import speculative_decoding_causal_amd as gdn
+    K, Ns = 3, 16
+    T = Ns * K
+    case = qcase(160 + seed, K, T + decodes, num_slots=24)
+    d = case["dims"]
+    rng = np.random.default_rng(170 + seed)
+    g = Gpu(case)
+    conv_buf, conv = _guarded(g.conv, 0.5)
+    ssm_buf, ssm = _guarded(g.ssm, 0.5)
+    out_buf, out = _guarded(g.out, 0.5)
+    spec = dict(spec_query_start_loc=i32(_junk(rng, Ns + 1, 0, T + 1)),
+                spec_state_indices=i32(_junk(rng, Ns * K, 0, d["num_slots"]).reshape(Ns, K)),
+                num_accepted_tokens=i32(_junk(rng, Ns, 1, K + 1)),
+                spec_cache_indices=i32(_junk(rng, Ns, 0, d["num_slots"])),
+                spec_token_indx=i32(_junk(rng, T, 0, T + decodes)))
+    say(f"garbage metadata seed={seed} decodes={decodes}")
+    if decodes == 0:
+        gdn.gdn_spec_attention(g.cfg, g.qkv, g.a, g.b, g.w, None, g.A_log, g.dt_bias, conv, ssm,
+                               spec["spec_query_start_loc"], spec["spec_state_indices"],
+                               spec["num_accepted_tokens"], out,
+                               spec_cache_indices=spec["spec_cache_indices"],
+                               spec_token_indx=spec["spec_token_indx"], num_spec_tokens=T)
+    else:
+        gdn.gdn_attention(g.cfg, g.qkv, g.a, g.b, g.w, None, g.A_log, g.dt_bias, conv, ssm, out,
+                          num_decodes=decodes, num_non_spec_tokens=decodes,
+                          query_start_loc=i32(_junk(rng, decodes + 1, 0, decodes + 1)),
+                          non_spec_state_indices=i32(_junk(rng, decodes, 0, d["num_slots"])),
+                          has_initial_state=u8(rng.integers(0, 2, decodes)),
+                          non_spec_token_indx=i32(_junk(rng, decodes, 0, T + decodes)),
+                          num_spec_tokens=T, **spec)
+    torch.cuda.synchronize()
+    assert _guards_intact(conv_buf, conv.numel(), 0.5)
+    assert _guards_intact(ssm_buf, ssm.numel(), 0.5)
+    assert _guards_intact(out_buf, out.numel(), 0.5)
 
 
 def test_token_permutation_invariance():
