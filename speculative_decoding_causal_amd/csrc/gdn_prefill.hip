@@ -133,7 +133,10 @@ prefill_map_kernel(PrefillArgs p, int* __restrict__ map, int cap) {
         map[2 * (s0 + u) + 1] = u;
       }
     }
-    carry = start[kMapThreads];
+    // Rows whose query_start_loc ranges overlap (values nothing has
+    // checked) can list more units than the map holds; those past `cap` are
+    // dropped, so the count saturates there instead of overflowing.
+    carry = min(start[kMapThreads], cap);
     __syncthreads();
   }
   for (int i = carry + tid; i < cap; i += kMapThreads) {

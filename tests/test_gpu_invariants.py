@@ -225,8 +225,11 @@ def _junk(rng, n, lo, hi):
     return np.array([pools[k][i] for i, k in enumerate(pick)], np.int32)
 
 
-@pytest.mark.parametrize("seed,decodes", [(0, 0), (1, 0), (2, 0), (3, 5), (4, 5)])
-def test_garbage_metadata_stays_in_bounds(seed, decodes):
+@pytest.mark.parametrize("seed,decodes,prefill,dk", [(0, 0, 0, 128), (1, 0, 0, 128),
+                                                     (2, 0, 0, 128), (3, 5, 0, 128),
+                                                     (4, 5, 0, 128), (5, 3, 150, 128),
+                                                     (6, 3, 150, 32), (7, 0, 300, 64)])
+def test_garbage_metadata_stays_in_bounds(seed, decodes, prefill, dk):
     # Metadata values live in device memory and are not checked by the step
     # (the host checker is separate): the kernels clamp query_start_loc,
     # slots, num_accepted_tokens and token rows, so any values leave the
@@ -235,34 +238,44 @@ def test_garbage_metadata_stays_in_bounds(seed, decodes):
     import speculative_decoding_causal_amd as gdn
     K, Ns = 3, 16
     T = Ns * K
-    case = qcase(160 + seed, K, T + decodes, num_slots=24)
+    nprefills = 3 if prefill else 0
+    nns = decodes + prefill           # the prefill rows share `prefill` tokens
+    case = helpers.small_case(seed=160 + seed, Hk=4, Hv=8, dk=dk, dv=dk, K=K, T=T + nns,
+                              num_slots=24)
     d = case["dims"]
     rng = np.random.default_rng(170 + seed)
     g = Gpu(case)
     conv_buf, conv = _guarded(g.conv, 0.5)
     ssm_buf, ssm = _guarded(g.ssm, 0.5)
     out_buf, out = _guarded(g.out, 0.5)
+    ws_buf = ws = None
+    if nprefills:
+        nbytes = gdn.gdn_workspace_bytes(g.cfg, d["L"], d["num_slots"], nns, nprefills)
+        ws_buf, ws = _guarded(torch.zeros(nbytes, dtype=torch.uint8, device=dev()), 0x5A)
     spec = dict(spec_query_start_loc=i32(_junk(rng, Ns + 1, 0, T + 1)),
                 spec_state_indices=i32(_junk(rng, Ns * K, 0, d["num_slots"]).reshape(Ns, K)),
                 num_accepted_tokens=i32(_junk(rng, Ns, 1, K + 1)),
                 spec_cache_indices=i32(_junk(rng, Ns, 0, d["num_slots"])),
-                spec_token_indx=i32(_junk(rng, T, 0, T + decodes)))
+                spec_token_indx=i32(_junk(rng, T, 0, T + nns)))
     say(f"garbage metadata seed={seed} decodes={decodes}")
-    if decodes == 0:
+    if decodes + nprefills == 0:
         gdn.gdn_spec_attention(g.cfg, g.qkv, g.a, g.b, g.w, None, g.A_log, g.dt_bias, conv, ssm,
                                spec["spec_query_start_loc"], spec["spec_state_indices"],
                                spec["num_accepted_tokens"], out,
                                spec_cache_indices=spec["spec_cache_indices"],
                                spec_token_indx=spec["spec_token_indx"], num_spec_tokens=T)
     else:
+        rows = decodes + nprefills
         gdn.gdn_attention(g.cfg, g.qkv, g.a, g.b, g.w, None, g.A_log, g.dt_bias, conv, ssm, out,
-                          num_decodes=decodes, num_non_spec_tokens=decodes,
-                          query_start_loc=i32(_junk(rng, decodes + 1, 0, decodes + 1)),
-                          non_spec_state_indices=i32(_junk(rng, decodes, 0, d["num_slots"])),
-                          has_initial_state=u8(rng.integers(0, 2, decodes)),
-                          non_spec_token_indx=i32(_junk(rng, decodes, 0, T + decodes)),
-                          num_spec_tokens=T, **spec)
+                          num_decodes=decodes, num_prefills=nprefills, num_non_spec_tokens=nns,
+                          query_start_loc=i32(_junk(rng, rows + 1, 0, nns + 1)),
+                          non_spec_state_indices=i32(_junk(rng, rows, 0, d["num_slots"])),
+                          has_initial_state=u8(rng.integers(0, 2, rows)),
+                          non_spec_token_indx=i32(_junk(rng, nns, 0, T + nns)),
+                          num_spec_tokens=T, workspace=ws, **spec)
     torch.cuda.synchronize()
+    if ws is not None:
+        assert _guards_intact(ws_buf, ws.numel(), 0x5A)
     assert _guards_intact(conv_buf, conv.numel(), 0.5)
     assert _guards_intact(ssm_buf, ssm.numel(), 0.5)
     assert _guards_intact(out_buf, out.numel(), 0.5)
