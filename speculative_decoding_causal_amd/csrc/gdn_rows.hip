@@ -322,8 +322,13 @@ gdn_rows_kernel(RowArgs pa) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int Hk = pa.Hk, G = pa.G, C = pa.C, L = pa.L;
-  int row = blockIdx.x / Hk;
-  const int ih = blockIdx.x - row * Hk;
+  // Workgroup i runs on XCD i % 8: the k-heads of a row share i % 8, so
+  // each XCD's L2 fetches a row's metadata and gate rows once.  The grid is
+  // padded to whole groups of 8 rows.
+  const int q8 = blockIdx.x >> 3;
+  const int ih = q8 % Hk;
+  int row = (q8 / Hk) * 8 + (blockIdx.x & 7);
+  if (row >= pa.num_rows + (pa.more.num_rows > 0 ? pa.more.num_rows : 0)) return;
   const int NCH = 2 * DK + G * DV;
   const int NR = G * DV;
   const int Tm = launch_row_tokens(pa);
@@ -636,7 +641,7 @@ hipError_t launch_typed(const RowArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int rows = a.num_rows + (a.more.num_rows > 0 ? a.more.num_rows : 0);
-  dim3 grid(static_cast<unsigned>(rows) * static_cast<unsigned>(a.Hk));
+  dim3 grid(static_cast<unsigned>((rows + 7) / 8 * 8) * static_cast<unsigned>(a.Hk));
   hipLaunchKernelGGL(kern, grid, dim3(NT), lay.total, s, a);
   return hipGetLastError();
 }
