@@ -225,11 +225,12 @@ def _junk(rng, n, lo, hi):
     return np.array([pools[k][i] for i, k in enumerate(pick)], np.int32)
 
 
-@pytest.mark.parametrize("seed,decodes,prefill,dk", [(0, 0, 0, 128), (1, 0, 0, 128),
-                                                     (2, 0, 0, 128), (3, 5, 0, 128),
-                                                     (4, 5, 0, 128), (5, 3, 150, 128),
-                                                     (6, 3, 150, 32), (7, 0, 300, 64)])
-def test_garbage_metadata_stays_in_bounds(seed, decodes, prefill, dk):
+@pytest.mark.parametrize("seed,decodes,prefill,dk,per_token",
+                         [(0, 0, 0, 128, 0), (1, 0, 0, 128, 0), (2, 0, 0, 128, 0),
+                          (3, 5, 0, 128, 0), (4, 5, 0, 128, 0), (5, 3, 150, 128, 0),
+                          (6, 3, 150, 32, 0), (7, 0, 300, 64, 0), (8, 0, 0, 128, 1),
+                          (9, 4, 0, 64, 1)])
+def test_garbage_metadata_stays_in_bounds(seed, decodes, prefill, dk, per_token):
     # Metadata values live in device memory and are not checked by the step
     # (the host checker is separate): the kernels clamp query_start_loc,
     # slots, num_accepted_tokens and token rows, so any values leave the
@@ -241,8 +242,9 @@ def test_garbage_metadata_stays_in_bounds(seed, decodes, prefill, dk):
     nprefills = 3 if prefill else 0
     nns = decodes + prefill           # the prefill rows share `prefill` tokens
     case = helpers.small_case(seed=160 + seed, Hk=4, Hv=8, dk=dk, dv=dk, K=K, T=T + nns,
-                              num_slots=24)
+                              num_slots=24, L=3 if per_token else None)
     d = case["dims"]
+    d["conv_layout"] = per_token       # per-token conv slots: one window per slot
     rng = np.random.default_rng(170 + seed)
     g = Gpu(case)
     conv_buf, conv = _guarded(g.conv, 0.5)
@@ -255,7 +257,8 @@ def test_garbage_metadata_stays_in_bounds(seed, decodes, prefill, dk):
     spec = dict(spec_query_start_loc=i32(_junk(rng, Ns + 1, 0, T + 1)),
                 spec_state_indices=i32(_junk(rng, Ns * K, 0, d["num_slots"]).reshape(Ns, K)),
                 num_accepted_tokens=i32(_junk(rng, Ns, 1, K + 1)),
-                spec_cache_indices=i32(_junk(rng, Ns, 0, d["num_slots"])),
+                spec_cache_indices=None if per_token else i32(_junk(rng, Ns, 0,
+                                                                    d["num_slots"])),
                 spec_token_indx=i32(_junk(rng, T, 0, T + nns)))
     say(f"garbage metadata seed={seed} decodes={decodes}")
     if decodes + nprefills == 0:
