@@ -2,16 +2,21 @@
  * gdn.h - C ABI of the MI355X (gfx950) Gated DeltaNet attention step with
  * speculative-decoding support.
  *
- * The step has two stages per token:
+ * The step has two stages per token, the two ops the pages name: the
+ * spec-aware causal_conv1d and the gated_delta_rule kernel fed by
+ * fused_sigmoid_gating ([P1] "Changes"; [P2] overview):
  *   1. a depthwise causal conv1d of width W over the packed projections
  *      mixed_qkv = [q (Hk*dk) | k (Hk*dk) | v (Hv*dv)], reading W-1 samples of
  *      history from a per-sequence conv-state ring and rolling that ring;
- *   2. the gated delta rule (Yang, Kautz, Hatamizadeh, "Gated Delta
- *      Networks", ICLR 2025) on an fp32 state S in R^{dv x dk} per v-head:
+ *   2. the gated delta rule on an fp32 state S in R^{dv x dk} per v-head:
  *        alpha = exp(-exp(A_log) * softplus(a + dt_bias)),  beta = sigmoid(b)
  *        S <- alpha S ;  u = beta (v - S k) ;  S <- S + u k^T ;  o = scale S q
- *      with q and k L2-normalised over dk (optional) and v-head h reading
- *      k-head h / (Hv/Hk).
+ *      i.e. S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *      o_t = S_t q_t, with q and k L2-normalised over dk (optional) and
+ *      v-head h reading k-head h / (Hv/Hk).  The pages name these ops but
+ *      print neither formula; this is the recurrence and gating the library
+ *      defines them as (the standard gated delta rule; background: Yang,
+ *      Kautz, Hatamizadeh, "Gated Delta Networks", ICLR 2025).
  *
  * Speculative-decoding semantics follow three web pages:
  *   [P1] "[GDN] Spec-decoding-aware attention kernel" (vllm-xpu-kernels
@@ -259,7 +264,10 @@ typedef struct gdn_rows {
   const int32_t* token_indx;
 } gdn_rows;
 
-/* Stage entry points (the conv and the delta rule as separate ops).
+/* Stage entry points: the conv and the delta rule as separate ops, the split
+ * requested in the issue [P1] "Related issues" cites (exposing
+ * causal_conv1d and gated_delta_rule as standalone ops, #189; the pull
+ * request itself keeps the single op, here gdn_attention).
  * gdn_conv_only runs the conv with the rows' window rule, rolls the rings and
  * writes the fp32 conv output of each token to conv_out[global row][C].
  * gdn_delta_rule_only reads conv_out at the same rows and runs gates, norms
@@ -276,28 +284,53 @@ int gdn_delta_rule_only(const gdn_dims* dims, const float* conv_out,
                         const gdn_rows* rows, gdn_bf16* core_attn_out,
                         gdn_stream_t stream);
 
+/* A host array for gdn_check_metadata_host: `len` int32 values readable at
+ * `data` (NULL with len 0 when the tensor is absent). */
+typedef struct gdn_host_i32 {
+  const int32_t* data;
+  int64_t len;
+} gdn_host_i32;
+
 /*
  * gdn_check_metadata_host - validate metadata VALUES on host copies of the
- * tensors (same meaning as in gdn_attention; any group may be absent by
- * passing 0 rows).  Checks: query_start_loc starts at 0 and is
- * non-decreasing (a prefill row may be empty); decode rows hold one token;
- * spec rows hold 1..max_spec_len
- * tokens; 1 <= n_acc <= T_b and (rolled history) n_acc + W - 2 <= state_len; slots
- * < num_slots; token rows in [0, num_actual_tokens) and distinct across both
- * streams; slots of different rows disjoint.  Returns GDN_OK or
- * GDN_ERR_METADATA (with gdn_last_error() naming the first violation).
+ * tensors, with the meaning they have in gdn_attention (spec rows: as in
+ * gdn_spec_attention).  Any group may be absent by passing 0 rows.
+ *
+ * Every array comes with its length, and each length is checked against
+ * what the counts require BEFORE any element is read: query_start_loc
+ * >= rows+1, non_spec_state_indices >= rows, non_spec_token_indx >=
+ * num_non_spec_tokens, spec_query_start_loc >= num_spec_decodes+1,
+ * spec_state_indices >= num_spec_decodes*max_spec_len, num_accepted_tokens
+ * and spec_cache_indices >= num_spec_decodes, spec_token_indx >=
+ * num_spec_tokens.  A short array is a GDN_ERR_DIMS; the function never
+ * reads past `len`.
+ *
+ * Value checks: query_start_loc starts at 0, is non-decreasing (a prefill
+ * row may be empty) and ends at num_non_spec_tokens; decode rows hold one
+ * token; spec_query_start_loc starts at 0 and ends at num_spec_tokens; spec
+ * rows hold 1..max_spec_len tokens; 1 <= n_acc <= T_b and (rolled history)
+ * n_acc + W - 2 <= state_len; slots < num_slots; token rows in
+ * [0, num_actual_tokens) and distinct across both streams (the identity
+ * mapping when a token_indx is absent); slots of different rows disjoint;
+ * num_non_spec_tokens + num_spec_tokens <= num_actual_tokens, with equality
+ * when there are non-spec rows (the conservation rule of gdn_attention
+ * ["[XE2] Support MTP of QWEN model", commit message]).  Returns GDN_OK,
+ * GDN_ERR_DIMS (a count or length) or GDN_ERR_METADATA (a value), with
+ * gdn_last_error() naming the first violation.  Host memory only; no HIP call.
  */
 int gdn_check_metadata_host(const gdn_dims* dims, int32_t num_actual_tokens,
                             int32_t num_decodes, int32_t num_prefills,
-                            const int32_t* query_start_loc,
-                            const int32_t* non_spec_state_indices,
-                            const int32_t* non_spec_token_indx,
-                            int32_t num_spec_decodes, int32_t max_spec_len,
-                            const int32_t* spec_query_start_loc,
-                            const int32_t* spec_cache_indices,
-                            const int32_t* spec_state_indices,
-                            const int32_t* num_accepted_tokens,
-                            const int32_t* spec_token_indx);
+                            int32_t num_non_spec_tokens,
+                            gdn_host_i32 query_start_loc,
+                            gdn_host_i32 non_spec_state_indices,
+                            gdn_host_i32 non_spec_token_indx,
+                            int32_t num_spec_decodes, int32_t num_spec_tokens,
+                            int32_t max_spec_len,
+                            gdn_host_i32 spec_query_start_loc,
+                            gdn_host_i32 spec_cache_indices,
+                            gdn_host_i32 spec_state_indices,
+                            gdn_host_i32 num_accepted_tokens,
+                            gdn_host_i32 spec_token_indx);
 
 /* Human-readable status; never NULL. */
 const char* gdn_status_string(int status);

@@ -25,12 +25,14 @@
  *   [P3] "[Bugfix] Align Qwen GDN gates with speculative tokens" (vLLM pull
  *        request 51812): "Purpose" (gates gathered with the same indices as
  *        mixed_qkv).
- *   [GDN] Yang, Kautz, Hatamizadeh, "Gated Delta Networks: Improving Mamba2
- *        with Delta Rule" (ICLR 2025): the gated delta rule
+ *   The recurrence and the gates.  [P1] "Changes" names the ops (the
+ *        gated_delta_rule kernel, fed by "fused_sigmoid_gating") but prints
+ *        no formula.  The oracle computes them as the gated delta rule
  *        S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T, o_t = S_t q_t,
- *        and the Mamba2-style decay a_t = exp(-exp(A_log) softplus(a+dt_bias)),
- *        b_t = sigmoid(b) computed by the "fused_sigmoid_gating" op that [P1]
- *        "Changes" names.
+ *        with decay a_t = exp(-exp(A_log) softplus(a+dt_bias)) and write
+ *        strength b_t = sigmoid(b): the definition this step is built to
+ *        (background: Yang, Kautz, Hatamizadeh, "Gated Delta Networks:
+ *        Improving Mamba2 with Delta Rule", ICLR 2025).
  *
  * Readings where the pages are silent (each one is listed in the design
  * notes with its reason):
@@ -111,7 +113,7 @@ static uint16_t bf16_round(double x) {
 
 static double softplus(double x) { return x > 20.0 ? x : log1p(exp(x)); }
 
-/* Decay and write strength of one (token, v-head) [GDN]; the gate rows are
+/* Decay and write strength of one (token, v-head) (the gates defined in the header); the gate rows are
  * read at the same global row as mixed_qkv [P3 "Purpose"]. */
 static void gates_one(uint16_t a_raw, uint16_t b_raw, double A_log,
                       double dt_bias, double* alpha, double* beta) {
@@ -240,7 +242,7 @@ static void conv_row_per_token(const oracle_dims* d, const uint16_t* mixed_qkv,
 }
 
 /*
- * Gated delta rule over the T tokens of one row, for every v-head [GDN]:
+ * Gated delta rule over the T tokens of one row, for every v-head (the recurrence defined in the header):
  *   S <- alpha S ;  p = S k ;  u = beta (v - p) ;  S <- S + u k^T
  *   (this equals alpha S (I - beta k k^T) + beta v k^T), the state is then
  *   rounded to fp32, and o = scale * S q is written as bf16 at row rows[j].

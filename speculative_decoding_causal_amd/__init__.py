@@ -24,7 +24,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgdn.so")
+# GDN_LIBRARY names another build of the library (e.g. one with the host
+# code under AddressSanitizer, from `build.py --asan`); default: in-tree.
+LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(_HERE, "libgdn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -95,8 +97,12 @@ _lib.gdn_conv_only.restype = ctypes.c_int
 _lib.gdn_delta_rule_only.argtypes = [ctypes.POINTER(GdnDims), _P, _P, _P, _P, _P, _P, _I,
                                      ctypes.POINTER(GdnRows), _P, _P]
 _lib.gdn_delta_rule_only.restype = ctypes.c_int
-_lib.gdn_check_metadata_host.argtypes = [ctypes.POINTER(GdnDims), _I, _I, _I, _P, _P, _P,
-                                         _I, _I, _P, _P, _P, _P, _P]
+class GdnHostI32(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("len", ctypes.c_int64)]
+
+
+_lib.gdn_check_metadata_host.argtypes = ([ctypes.POINTER(GdnDims), _I, _I, _I, _I] +
+                                         [GdnHostI32] * 3 + [_I, _I, _I] + [GdnHostI32] * 5)
 _lib.gdn_check_metadata_host.restype = ctypes.c_int
 _lib.gdn_status_string.argtypes = [ctypes.c_int]
 _lib.gdn_status_string.restype = ctypes.c_char_p
@@ -416,35 +422,46 @@ def gdn_delta_rule_only(cfg: GdnConfig, conv_out, a, b, A_log, dt_bias, ssm_stat
         raise GdnError(rc, "gdn_delta_rule_only")
 
 
-def _np_ptr(x):
-    if x is None:
-        return None
-    x = np.ascontiguousarray(x, dtype=np.int32)
-    return x, x.ctypes.data
-
-
 def gdn_check_metadata_host(cfg: GdnConfig, state_len: int, num_slots: int,
                             num_actual_tokens: int, *, num_decodes=0, num_prefills=0,
-                            query_start_loc=None, non_spec_state_indices=None,
-                            non_spec_token_indx=None, spec_query_start_loc=None,
-                            spec_cache_indices=None, spec_state_indices=None,
-                            num_accepted_tokens=None, spec_token_indx=None) -> int:
+                            num_non_spec_tokens=None, query_start_loc=None,
+                            non_spec_state_indices=None, non_spec_token_indx=None,
+                            num_spec_decodes=None, num_spec_tokens=None, max_spec_len=None,
+                            spec_query_start_loc=None, spec_cache_indices=None,
+                            spec_state_indices=None, num_accepted_tokens=None,
+                            spec_token_indx=None) -> int:
     """Check metadata values on host (numpy) copies; returns the status and
-    raises nothing (``gdn_last_error()`` explains a failure)."""
+    raises nothing (``gdn_last_error()`` explains a failure).  Each array is
+    passed with its length.  ``num_spec_decodes`` defaults to the length of
+    ``spec_query_start_loc`` less one, the token counts to the last entry of
+    the query_start_loc arrays, ``max_spec_len`` to the row length of
+    ``spec_state_indices`` (a flat array needs it given)."""
     dims = cfg.dims(state_len=state_len, num_slots=num_slots)
     keep = []
 
-    def p(x):
-        r = _np_ptr(x)
-        if r is None:
-            return None
-        keep.append(r[0])
-        return r[1]
+    def arr(x):
+        if x is None:
+            return GdnHostI32(None, 0)
+        a = np.ascontiguousarray(x, dtype=np.int32).ravel()
+        keep.append(a)
+        return GdnHostI32(a.ctypes.data if a.size else None, a.size)
 
-    Ns = 0 if spec_query_start_loc is None else len(spec_query_start_loc) - 1
-    K = 1 if spec_state_indices is None else np.asarray(spec_state_indices).shape[1]
+    ns_rows = int(num_decodes) + int(num_prefills)
+    if num_spec_decodes is not None:
+        Ns = int(num_spec_decodes)
+    else:
+        Ns = 0 if spec_query_start_loc is None else max(len(spec_query_start_loc) - 1, 0)
+    if num_non_spec_tokens is None:
+        num_non_spec_tokens = (int(query_start_loc[-1]) if ns_rows and query_start_loc is not None
+                               and len(query_start_loc) else 0)
+    if num_spec_tokens is None:
+        num_spec_tokens = int(spec_query_start_loc[-1]) if Ns else 0
+    if max_spec_len is None:
+        ssi = None if spec_state_indices is None else np.asarray(spec_state_indices)
+        max_spec_len = ssi.shape[1] if ssi is not None and ssi.ndim == 2 else 1
     return int(_lib.gdn_check_metadata_host(
         ctypes.byref(dims), int(num_actual_tokens), int(num_decodes), int(num_prefills),
-        p(query_start_loc), p(non_spec_state_indices), p(non_spec_token_indx), int(Ns), int(K),
-        p(spec_query_start_loc), p(spec_cache_indices), p(spec_state_indices),
-        p(num_accepted_tokens), p(spec_token_indx)))
+        int(num_non_spec_tokens), arr(query_start_loc), arr(non_spec_state_indices),
+        arr(non_spec_token_indx), int(Ns), int(num_spec_tokens), int(max_spec_len),
+        arr(spec_query_start_loc), arr(spec_cache_indices), arr(spec_state_indices),
+        arr(num_accepted_tokens), arr(spec_token_indx)))

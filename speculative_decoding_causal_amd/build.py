@@ -17,27 +17,44 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link ``libgdn.so``; returns its path."""
-    objs = []
+# Host code only under AddressSanitizer (device code is never instrumented):
+# load the result with GDN_LIBRARY=<path> and LD_PRELOAD=<clang asan runtime>.
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build(verbose: bool = False, out: str = LIB, asan: bool = False) -> str:
+    """Compile every source and link ``libgdn.so`` (or ``out``); returns its
+    path.  Sources compile in parallel."""
+    objs, procs = [], []
+    tag = ".asan" if asan else ""
     for src in SOURCES:
-        obj = os.path.join(CSRC, os.path.splitext(src)[0] + ".o")
-        lang = ["-x", "hip"]
-        cmd = ["hipcc", *HIPCC_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        obj = os.path.join(CSRC, os.path.splitext(src)[0] + tag + ".o")
+        cmd = ["hipcc", *HIPCC_FLAGS, *(ASAN_FLAGS if asan else []), "-x", "hip", "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.check_call(cmd)
+        procs.append((cmd, subprocess.Popen(cmd)))
         objs.append(obj)
-    tmp = LIB + ".tmp"
-    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    for cmd, p in procs:
+        if p.wait() != 0:
+            raise subprocess.CalledProcessError(p.returncode, cmd)
+    tmp = out + ".tmp"
+    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC",
+           *(["-Xarch_host", "-fsanitize=address", "-shared-libasan"] if asan else []),
+           "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     for obj in objs:
         os.remove(obj)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    args = sys.argv[1:]
+    if "--asan" in args:
+        i = args.index("--asan")
+        print(build(verbose="-v" in args, out=os.path.abspath(args[i + 1]), asan=True))
+    else:
+        print(build(verbose="-v" in args))

@@ -151,6 +151,23 @@ def _dev(x, device, bf16=False):
 
 def replay(path: str, device: str = "cuda:0") -> dict:
     """Rerun a captured call on compact pools and compare with the capture."""
+    rec, out, conv, ssm = rerun(path, device)
+    return compare(rec["arrays"], out, conv, ssm)
+
+
+def compact_metadata(rec: dict) -> dict:
+    """The capture's metadata arrays with slot ids remapped to the compact
+    pools (slot ``slots[i]`` becomes i+1; NULL, pad and out-of-range ids
+    become 0)."""
+    A = rec["arrays"]
+    return {k: (remap_slots(A[k], A["slots"]) if k in _SLOT_ARRAYS else A[k])
+            for k in _META if k in A}
+
+
+def rerun(path: str, device: str = "cuda:0"):
+    """Rerun a captured call on compact pools (slot 0 is NULL, slot i+1 holds
+    the capture's i-th slot).  Returns (record, core_attn_out, conv slots,
+    SSM slots) as host arrays, the pools without their NULL slot."""
     import speculative_decoding_causal_amd as gdn
     rec = load(path)
     A = rec["arrays"]
@@ -164,11 +181,7 @@ def replay(path: str, device: str = "cuda:0") -> dict:
         ssm[1:] = _dev(A["ssm_pre"], device)
     conv = conv.view(torch.bfloat16)
     out = _dev(A["core_attn_out_pre"], device, bf16=True)
-    kw = {}
-    for k in _META:
-        if k in A:
-            v = remap_slots(A[k], slots) if k in _SLOT_ARRAYS else A[k]
-            kw[k] = _dev(v, device)
+    kw = {k: _dev(v, device) for k, v in compact_metadata(rec).items()}
     inputs = {k: _dev(A.get(k), device, bf16=A.get(k) is not None and A[k].dtype == np.int16)
               for k in _INPUTS}
     sc = {k: v for k, v in rec["scalars"].items() if v is not None}
@@ -192,7 +205,7 @@ def replay(path: str, device: str = "cuda:0") -> dict:
     got_out = out.view(torch.int16).cpu().numpy()
     got_conv = conv.view(torch.int16)[1:].cpu().numpy()
     got_ssm = ssm[1:].cpu().numpy()
-    return compare(A, got_out, got_conv, got_ssm)
+    return rec, got_out, got_conv, got_ssm
 
 
 def _bf16_to_f64(x):

@@ -558,18 +558,66 @@ int gdn_delta_rule_only(const gdn_dims* dims, const float* conv_out,
 
 int gdn_check_metadata_host(const gdn_dims* dims, int32_t num_actual_tokens,
                             int32_t num_decodes, int32_t num_prefills,
-                            const int32_t* query_start_loc,
-                            const int32_t* non_spec_state_indices,
-                            const int32_t* non_spec_token_indx,
-                            int32_t num_spec_decodes, int32_t max_spec_len,
-                            const int32_t* spec_query_start_loc,
-                            const int32_t* spec_cache_indices,
-                            const int32_t* spec_state_indices,
-                            const int32_t* num_accepted_tokens,
-                            const int32_t* spec_token_indx) {
+                            int32_t num_non_spec_tokens,
+                            gdn_host_i32 query_start_loc,
+                            gdn_host_i32 non_spec_state_indices,
+                            gdn_host_i32 non_spec_token_indx,
+                            int32_t num_spec_decodes, int32_t num_spec_tokens,
+                            int32_t max_spec_len,
+                            gdn_host_i32 spec_query_start_loc,
+                            gdn_host_i32 spec_cache_indices,
+                            gdn_host_i32 spec_state_indices,
+                            gdn_host_i32 num_accepted_tokens,
+                            gdn_host_i32 spec_token_indx) {
   if (int e = check_dims(dims)) return e;
+  if (num_actual_tokens < 0 || num_decodes < 0 || num_prefills < 0 || num_non_spec_tokens < 0 ||
+      num_spec_decodes < 0 || num_spec_tokens < 0)
+    return fail(GDN_ERR_DIMS, "negative counts");
+  const int ns_rows = num_decodes + num_prefills;
+  if (ns_rows == 0 && num_non_spec_tokens != 0)
+    return fail(GDN_ERR_DIMS, "num_non_spec_tokens=%d with no non-spec rows", num_non_spec_tokens);
+  if (num_spec_decodes == 0 && num_spec_tokens != 0)
+    return fail(GDN_ERR_DIMS, "num_spec_tokens=%d with no spec rows", num_spec_tokens);
+  const long long streams = (long long)num_non_spec_tokens + num_spec_tokens;
+  if (streams > num_actual_tokens)
+    return fail(GDN_ERR_CONSERVATION, "non-spec tokens %d + spec tokens %d > num_actual_tokens %d",
+                num_non_spec_tokens, num_spec_tokens, num_actual_tokens);
+  if (ns_rows > 0 && streams != num_actual_tokens)
+    return fail(GDN_ERR_CONSERVATION, "non-spec tokens %d + spec tokens %d != %d",
+                num_non_spec_tokens, num_spec_tokens, num_actual_tokens);
+  // Lengths first: nothing below reads past what the caller said it holds.
+  auto need = [](const gdn_host_i32& a, long long n, bool required, const char* what) -> int {
+    if (!a.data) {
+      if (required && n > 0) return fail(GDN_ERR_NULL, "%s is required", what);
+      return GDN_OK;
+    }
+    if (a.len < n)
+      return fail(GDN_ERR_DIMS, "%s holds %lld values; the counts need %lld", what,
+                  (long long)a.len, n);
+    return GDN_OK;
+  };
+  if (ns_rows > 0) {
+    if (int e = need(query_start_loc, ns_rows + 1LL, true, "query_start_loc")) return e;
+    if (int e = need(non_spec_state_indices, ns_rows, true, "non_spec_state_indices")) return e;
+    if (int e = need(non_spec_token_indx, num_non_spec_tokens, false, "non_spec_token_indx"))
+      return e;
+  }
+  if (num_spec_decodes > 0) {
+    if (max_spec_len < 1 || max_spec_len > gdn::kMaxRowTokens)
+      return fail(GDN_ERR_UNSUPPORTED, "max_spec_len %d not in [1,%d]", max_spec_len,
+                  gdn::kMaxRowTokens);
+    if (int e = need(spec_query_start_loc, num_spec_decodes + 1LL, true, "spec_query_start_loc"))
+      return e;
+    if (int e = need(spec_state_indices, (long long)num_spec_decodes * max_spec_len, true,
+                     "spec_state_indices"))
+      return e;
+    if (int e = need(num_accepted_tokens, num_spec_decodes, true, "num_accepted_tokens"))
+      return e;
+    if (int e = need(spec_cache_indices, num_spec_decodes, false, "spec_cache_indices")) return e;
+    if (int e = need(spec_token_indx, num_spec_tokens, false, "spec_token_indx")) return e;
+  }
   const int L = dims->state_len, W = dims->conv_width, S = dims->num_slots;
-  std::vector<int> row_owner(num_actual_tokens > 0 ? num_actual_tokens : 0, -1);
+  std::vector<int> row_owner(num_actual_tokens, -1);
   std::vector<int> slot_owner(S, -1);
   int owner = 0;
   auto claim_slot = [&](int slot, int who, const char* what) -> int {
@@ -587,47 +635,58 @@ int gdn_check_metadata_host(const gdn_dims* dims, int32_t num_actual_tokens,
     row_owner[r] = who;
     return GDN_OK;
   };
-  const int ns_rows = num_decodes + num_prefills;
   if (ns_rows > 0) {
-    if (!query_start_loc || !non_spec_state_indices)
-      return fail(GDN_ERR_NULL, "non-spec metadata missing");
-    if (query_start_loc[0] != 0) return fail(GDN_ERR_METADATA, "query_start_loc[0] != 0");
+    const int32_t* qsl = query_start_loc.data;
+    if (qsl[0] != 0) return fail(GDN_ERR_METADATA, "query_start_loc[0] != 0");
+    for (int i = 0; i < ns_rows; ++i)
+      if (qsl[i + 1] < qsl[i])
+        return fail(GDN_ERR_METADATA, "query_start_loc decreases at row %d", i);
+    if (qsl[ns_rows] != num_non_spec_tokens)
+      return fail(GDN_ERR_METADATA, "query_start_loc[%d] = %d, but num_non_spec_tokens = %d",
+                  ns_rows, qsl[ns_rows], num_non_spec_tokens);
+    // qsl is non-decreasing from 0 to num_non_spec_tokens: every token index
+    // below lies inside non_spec_token_indx
     for (int i = 0; i < ns_rows; ++i, ++owner) {
-      int T = query_start_loc[i + 1] - query_start_loc[i];
-      if (T < 0) return fail(GDN_ERR_METADATA, "query_start_loc decreases at row %d", i);
+      const int T = qsl[i + 1] - qsl[i];
       if (i < num_decodes && T != 1)
         return fail(GDN_ERR_METADATA, "decode row %d has %d tokens", i, T);
-      if (int e = claim_slot(non_spec_state_indices[i], owner, "non-spec")) return e;
-      for (int j = query_start_loc[i]; j < query_start_loc[i + 1]; ++j)
-        if (int e = claim_row(non_spec_token_indx ? non_spec_token_indx[j] : j, owner)) return e;
+      if (int e = claim_slot(non_spec_state_indices.data[i], owner, "non-spec")) return e;
+      for (int j = qsl[i]; j < qsl[i + 1]; ++j)
+        if (int e = claim_row(non_spec_token_indx.data ? non_spec_token_indx.data[j] : j, owner))
+          return e;
     }
   }
   if (num_spec_decodes > 0) {
-    if (!spec_query_start_loc || !spec_state_indices || !num_accepted_tokens)
-      return fail(GDN_ERR_NULL, "spec metadata missing");
-    if (spec_query_start_loc[0] != 0)
-      return fail(GDN_ERR_METADATA, "spec_query_start_loc[0] != 0");
-    for (int bi = 0; bi < num_spec_decodes; ++bi, ++owner) {
-      int T = spec_query_start_loc[bi + 1] - spec_query_start_loc[bi];
+    const int32_t* sqsl = spec_query_start_loc.data;
+    if (sqsl[0] != 0) return fail(GDN_ERR_METADATA, "spec_query_start_loc[0] != 0");
+    for (int bi = 0; bi < num_spec_decodes; ++bi) {
+      const int T = sqsl[bi + 1] - sqsl[bi];
       if (T < 1 || T > max_spec_len)
         return fail(GDN_ERR_METADATA, "spec row %d has %d tokens (max %d)", bi, T, max_spec_len);
-      int n = num_accepted_tokens[bi];
+    }
+    if (sqsl[num_spec_decodes] != num_spec_tokens)
+      return fail(GDN_ERR_METADATA, "spec_query_start_loc[%d] = %d, but num_spec_tokens = %d",
+                  num_spec_decodes, sqsl[num_spec_decodes], num_spec_tokens);
+    const bool per_token = dims->conv_layout == GDN_CONV_PER_TOKEN_SLOTS;
+    for (int bi = 0; bi < num_spec_decodes; ++bi, ++owner) {
+      const int T = sqsl[bi + 1] - sqsl[bi];
+      const int n = num_accepted_tokens.data[bi];
       if (n < 1 || n > T)
         return fail(GDN_ERR_METADATA, "spec row %d: num_accepted_tokens %d not in [1,%d]", bi,
                     n, T);
-      const bool per_token = dims->conv_layout == GDN_CONV_PER_TOKEN_SLOTS;
       if (!per_token && n + W - 2 > L)
         return fail(GDN_ERR_METADATA, "spec row %d: window n_acc-1=%d needs state_len >= %d",
                     bi, n - 1, n + W - 2);
-      const int32_t* ssi = spec_state_indices + (size_t)bi * max_spec_len;
+      const int32_t* ssi = spec_state_indices.data + (size_t)bi * max_spec_len;
       if (!per_token) {
-        int cs = spec_cache_indices ? spec_cache_indices[bi] : ssi[0];
+        const int cs = spec_cache_indices.data ? spec_cache_indices.data[bi] : ssi[0];
         if (int e = claim_slot(cs, owner, "conv")) return e;
       }
       for (int t = 0; t < T; ++t)
         if (int e = claim_slot(ssi[t], owner, "spec state")) return e;
-      for (int j = spec_query_start_loc[bi]; j < spec_query_start_loc[bi + 1]; ++j)
-        if (int e = claim_row(spec_token_indx ? spec_token_indx[j] : j, owner)) return e;
+      for (int j = sqsl[bi]; j < sqsl[bi + 1]; ++j)
+        if (int e = claim_row(spec_token_indx.data ? spec_token_indx.data[j] : j, owner))
+          return e;
     }
   }
   return GDN_OK;

@@ -48,6 +48,20 @@ def run_nonspec(case, ns=None, with_conv=False, out=None):
     return o, c["conv_state"], c["ssm_state"], y
 
 
+def run_case(case, out=None):
+    """Oracle on a clone of the whole batch: the non-spec rows, then the spec
+    rows (rows of one call use disjoint slots, so the order does not matter).
+    Either stream may be absent.  Returns (out, conv_state, ssm_state)."""
+    c = clone(case)
+    d = c["dims"]
+    o = np.zeros(out_shape(c), np.uint16) if out is None else out.copy()
+    if c.get("nonspec") is not None:
+        oracle.nonspec_step(d, c, c["nonspec"], o)
+    if c.get("spec") is not None:
+        oracle.spec_step(d, c, c["spec"], o)
+    return o, c["conv_state"], c["ssm_state"]
+
+
 def spec_meta(sqsl, ssi, nacc, tix=None, cache=None):
     sqsl = np.asarray(sqsl, np.int32)
     ssi = np.asarray(ssi, np.int32)

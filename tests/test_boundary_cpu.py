@@ -185,13 +185,55 @@ def test_metadata_checker_rejects(change, needle):
     assert needle in gdn.gdn_last_error()
 
 
+def test_metadata_checker_reads_no_further_than_given():
+    # a 4-entry view of a 100-entry buffer named as the token rows of a
+    # 50-token prefill row: rejected on its length, before any entry is read
+    buf = np.arange(100, dtype=np.int32)
+    rc = check(num_actual_tokens=50, num_decodes=0, num_prefills=1, query_start_loc=[0, 50],
+               non_spec_state_indices=[9], non_spec_token_indx=buf[:4])
+    assert rc == gdn.GDN_ERR_DIMS
+    assert "non_spec_token_indx holds 4 values" in gdn.gdn_last_error()
+
+
+@pytest.mark.parametrize("name,short", [
+    ("query_start_loc", [0, 1]), ("non_spec_state_indices", [9]),
+    ("non_spec_token_indx", [0, 5, 6]), ("spec_query_start_loc", [0, 2]),
+    ("spec_state_indices", [1, 2, 3]), ("num_accepted_tokens", [1]),
+    ("spec_cache_indices", [1]), ("spec_token_indx", [1, 2, 3]),
+])
+def test_metadata_checker_rejects_short_arrays(name, short):
+    m = good_meta()
+    m.update({name: short, "num_spec_decodes": 2, "num_spec_tokens": 4, "num_non_spec_tokens": 4,
+              "max_spec_len": 2})
+    assert check(**m) == gdn.GDN_ERR_DIMS
+    assert gdn.gdn_last_error().startswith(name), gdn.gdn_last_error()
+
+
+def test_metadata_checker_counts_match_the_arrays():
+    m = good_meta()
+    # query_start_loc ends at 4 but the call says 3 non-spec tokens (and 5 spec)
+    m1 = dict(m, spec_token_indx=[1, 2, 3, 4, 0])
+    assert check(**m1, num_non_spec_tokens=3, num_spec_tokens=5) == gdn.GDN_ERR_METADATA
+    assert "num_non_spec_tokens" in gdn.gdn_last_error()
+    m2 = dict(m, query_start_loc=[0, 1, 5], non_spec_token_indx=[0, 5, 6, 7, 1])
+    assert check(**m2, num_non_spec_tokens=5, num_spec_tokens=3) == gdn.GDN_ERR_METADATA
+    assert "num_spec_tokens" in gdn.gdn_last_error()
+    # the two streams must add up to num_actual_tokens when non-spec rows exist
+    assert check(**m, num_actual_tokens=9) == gdn.GDN_ERR_CONSERVATION
+    assert check(**m, num_actual_tokens=7) == gdn.GDN_ERR_CONSERVATION
+    # spec rows alone may leave rows unmapped (as gdn_spec_attention does)
+    sp = {k: v for k, v in m.items() if k.startswith("spec") or k == "num_accepted_tokens"}
+    assert check(**sp, num_actual_tokens=9) == gdn.GDN_OK, gdn.gdn_last_error()
+    assert check(**sp, num_actual_tokens=4) == gdn.GDN_ERR_METADATA   # row 4 outside
+
+
 def test_metadata_checker_empty_prefill_row():
     # a prefill row may hold no tokens (a graph pad row); query_start_loc
     # must not decrease
     m = good_meta()
     m.update(num_prefills=2, query_start_loc=[0, 1, 1, 4], non_spec_state_indices=[9, 0, 10])
     assert check(**m) == gdn.GDN_OK
-    m.update(query_start_loc=[0, 1, 4, 3])
+    m.update(query_start_loc=[0, 1, 4, 3], num_non_spec_tokens=4)
     assert check(**m) == gdn.GDN_ERR_METADATA
     assert "decreases" in gdn.gdn_last_error()
 
@@ -326,6 +368,8 @@ def _fuzz_batch(seed):
     sp, ns, d = case["spec"], case["nonspec"], case["dims"]
     cfg = gdn.GdnConfig(d["Hk"], d["Hv"], d["dk"], d["dv"])
     meta = dict(num_decodes=ns["num_decodes"], num_prefills=ns["num_prefills"],
+                num_non_spec_tokens=ns["num_non_spec_tokens"],
+                num_spec_tokens=sp["num_spec_tokens"], max_spec_len=K,
                 query_start_loc=ns["query_start_loc"].copy(),
                 non_spec_state_indices=ns["cache_indices"].copy(),
                 non_spec_token_indx=ns["token_indx"].copy(),
@@ -353,7 +397,9 @@ def _corrupt(rng, d, nat, m):
     if len(tix) + len(ntix) >= 2:
         kinds.append("tix_twice")
     if m["num_decodes"] > 0:
-        kinds += ["decode_len", "qsl_decreases"]
+        kinds.append("qsl_decreases")
+        if m["num_decodes"] + m["num_prefills"] >= 2:
+            kinds.append("decode_len")
     kind = kinds[int(rng.integers(0, len(kinds)))]
     b = int(rng.integers(0, Ns))
     if kind == "nacc_low":
@@ -380,8 +426,7 @@ def _corrupt(rng, d, nat, m):
         return "outside"
     q = m["query_start_loc"]
     if kind == "decode_len":
-        q[1:] += 1                          # the first decode row holds two tokens
-        m["non_spec_token_indx"] = np.append(ntix, nat - 1)
+        q[1] += 1                           # the first decode row takes the next row's token
         return "decode row"
     q[1] = -1                               # kind == "qsl_decreases"
     return "decreases"

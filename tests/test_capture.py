@@ -1,12 +1,18 @@
 """Capture/replay format ("[GDN] Spec-decoding-aware attention kernel", "Test
-Plan": regression on captured (metadata, inputs, outputs) tuples)."""
+Plan": regression on captured (metadata, inputs, outputs) tuples, each replay
+diffed against an oracle at atol = rtol = 2e-2).  A replay is compared with
+the bytes it recorded and, independently, with the CPU oracle run on the
+capture's own inputs and compact pools."""
 from __future__ import annotations
 
 import numpy as np
 import pytest
 
 from speculative_decoding_causal_amd import capture
-from tests.gpu_util import Gpu, gpu_available, i32, say, u8
+import synth
+from tests import helpers
+from tests.gpu_util import (Gpu, assert_out_close, assert_states_close, gpu_available, i32,
+                            say, u8)
 
 
 def test_slot_remap():
@@ -34,8 +40,43 @@ def test_file_round_trip(tmp_path):
     np.testing.assert_array_equal(back["arrays"]["mixed_qkv"], rec["arrays"]["mixed_qkv"])
 
 
+def oracle_of_capture(rec):
+    """The oracle on a capture's inputs and compact pools (slot i+1 holds the
+    capture's i-th slot, slot 0 is NULL): returns (out, conv, ssm), the pools
+    without their NULL slot.  Only grouped mixed_qkv captures."""
+    A, cfg, sc = rec["arrays"], rec["cfg"], rec["scalars"]
+    assert cfg["reorder_input"], "the oracle reads the grouped channel order"
+    n = len(A["slots"]) + 1
+    d = synth.dims_of(cfg["num_k_heads"], cfg["num_v_heads"], cfg["head_k_dim"],
+                      cfg["head_v_dim"], cfg["conv_width"], rec["state_len"], n,
+                      cfg["activation"], cfg["use_qk_l2norm"], cfg["l2norm_eps"],
+                      cfg["scale"] if cfg["scale"] is not None else cfg["head_k_dim"] ** -0.5)
+    d["conv_layout"] = cfg["conv_layout"]
+    u16 = lambda x: None if x is None else np.ascontiguousarray(x).view(np.uint16)
+    conv = np.zeros((n,) + A["conv_pre"].shape[1:], np.uint16)
+    ssm = np.zeros((n,) + A["ssm_pre"].shape[1:], np.float32)
+    conv[1:], ssm[1:] = u16(A["conv_pre"]), A["ssm_pre"]
+    case = dict(dims=d, mixed_qkv=u16(A["mixed_qkv"]), a=u16(A["a"]), b=u16(A["b"]),
+                conv_weight=u16(A["conv_weight"]), conv_bias=u16(A.get("conv_bias")),
+                A_log=A["A_log"], dt_bias=A["dt_bias"], conv_state=conv, ssm_state=ssm,
+                num_actual_tokens=int(A["mixed_qkv"].shape[0]), spec=None, nonspec=None)
+    m = capture.compact_metadata(rec)
+    if "spec_state_indices" in m:
+        case["spec"] = helpers.spec_meta(m["spec_query_start_loc"], m["spec_state_indices"],
+                                         m["num_accepted_tokens"], m.get("spec_token_indx"),
+                                         m.get("spec_cache_indices"))
+    if "non_spec_state_indices" in m:
+        case["nonspec"] = dict(num_decodes=sc["num_decodes"], num_prefills=sc["num_prefills"],
+                               num_non_spec_tokens=sc["num_non_spec_tokens"],
+                               query_start_loc=m["query_start_loc"],
+                               cache_indices=m["non_spec_state_indices"],
+                               has_initial_state=m.get("has_initial_state"),
+                               token_indx=m.get("non_spec_token_indx"))
+    out, conv, ssm = helpers.run_case(case, out=u16(A["core_attn_out_pre"]))
+    return out, conv[1:], ssm[1:]
+
+
 def _record(g, tmp_path, name):
-    import synth  # noqa: F401
     sp, ns = g.case.get("spec"), g.case.get("nonspec")
     kw = dict(mixed_qkv=g.qkv, a=g.a, b=g.b, conv_weight=g.w, conv_bias=g.bias, A_log=g.A_log,
               dt_bias=g.dt_bias)
@@ -76,9 +117,16 @@ def test_record_then_replay_is_bit_exact(name, tmp_path):
     g = Gpu(synth.make_case(name, seed=31, permute_tokens=(name == "small")))
     say(f"capture + replay {name}")
     path = _record(g, tmp_path, name)
-    res = capture.replay(path)
+    rec, out, conv, ssm = capture.rerun(path)
+    res = capture.compare(rec["arrays"], out, conv, ssm)
     assert res["out_bit_equal"] and res["conv_bit_equal"] and res["ssm_bit_equal"], res
     assert res["within_tolerance"]
+    # the replay against the oracle on the capture's own inputs and pools
+    ref_out, ref_conv, ref_ssm = oracle_of_capture(rec)
+    assert_out_close(out.view(np.uint16), ref_out)
+    np.testing.assert_array_equal(conv.view(np.uint16), ref_conv)
+    assert_states_close(ssm, ref_ssm)
+    assert capture.replay(path)["within_tolerance"]
 
 
 @pytest.mark.gpu
@@ -96,3 +144,48 @@ def test_replay_reports_a_wrong_capture(tmp_path):
     res = capture.replay(path)
     assert not res["out_bit_equal"] and not res["ssm_bit_equal"]
     assert not res["within_tolerance"]
+
+
+@pytest.mark.parametrize("name", ["small", "mixed"])
+def test_compact_pools_keep_the_oracle_result(name):
+    # A capture record built on the host (as record_call lays it out) from a
+    # batch and its oracle result: rerunning the oracle on the compact pools
+    # and remapped metadata gives the same outputs and the same bytes for the
+    # named slots.  Checks the slot remap that replays rely on, no GPU.
+    case = synth.make_case(name, seed=33, permute_tokens=(name == "small"))
+    if name == "mixed":   # keep the prefill rows short: host-side oracle time
+        case = synth.make_case(name, seed=33, prefill_lens=(70, 5))
+    out0 = np.full(helpers.out_shape(case), 0x5A5A, np.uint16)
+    out1, conv1, ssm1 = helpers.run_case(case, out=out0)
+    sp, ns = case["spec"], case["nonspec"]
+    meta = dict(spec_query_start_loc=sp["spec_query_start_loc"],
+                spec_state_indices=sp["spec_state_indices"],
+                num_accepted_tokens=sp["num_accepted_tokens"],
+                spec_token_indx=sp["spec_token_indx"])
+    scalars = dict(num_spec_tokens=sp["num_spec_tokens"])
+    if ns is not None:
+        meta.update(query_start_loc=ns["query_start_loc"],
+                    non_spec_state_indices=ns["cache_indices"],
+                    has_initial_state=ns["has_initial_state"],
+                    non_spec_token_indx=ns["token_indx"])
+        scalars.update(num_decodes=ns["num_decodes"], num_prefills=ns["num_prefills"],
+                       num_non_spec_tokens=ns["num_non_spec_tokens"])
+    meta = {k: v for k, v in meta.items() if v is not None}
+    d = case["dims"]
+    slots = capture.referenced_slots(meta, d["num_slots"])
+    i16 = lambda x: np.ascontiguousarray(x).view(np.int16)
+    arrays = dict(mixed_qkv=i16(case["mixed_qkv"]), a=i16(case["a"]), b=i16(case["b"]),
+                  conv_weight=i16(case["conv_weight"]), A_log=case["A_log"],
+                  dt_bias=case["dt_bias"], slots=slots,
+                  conv_pre=i16(case["conv_state"][slots]), ssm_pre=case["ssm_state"][slots],
+                  core_attn_out_pre=i16(out0), **meta)
+    cfg = dict(num_k_heads=d["Hk"], num_v_heads=d["Hv"], head_k_dim=d["dk"],
+               head_v_dim=d["dv"], conv_width=d["W"], activation=d["activation"],
+               use_qk_l2norm=d["use_qk_l2norm"], l2norm_eps=d["eps"], scale=d["scale"],
+               reorder_input=True, conv_layout=0)
+    rec = dict(format=capture.FORMAT, call="gdn_attention", cfg=cfg, state_len=d["L"],
+               num_slots=d["num_slots"], scalars=scalars, arrays=arrays)
+    out, conv, ssm = oracle_of_capture(rec)
+    np.testing.assert_array_equal(out, out1)
+    np.testing.assert_array_equal(conv, conv1[slots])
+    np.testing.assert_array_equal(ssm, ssm1[slots])

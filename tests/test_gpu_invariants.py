@@ -378,6 +378,8 @@ def test_generated_metadata_passes_host_checker(name):
     rc = gdn.gdn_check_metadata_host(
         cfg, d["L"], d["num_slots"], case["num_actual_tokens"],
         num_decodes=ns.get("num_decodes", 0), num_prefills=ns.get("num_prefills", 0),
+        num_non_spec_tokens=ns.get("num_non_spec_tokens", 0),
+        num_spec_tokens=sp["num_spec_tokens"],
         query_start_loc=ns.get("query_start_loc"),
         non_spec_state_indices=ns.get("cache_indices"),
         non_spec_token_indx=ns.get("token_indx"),

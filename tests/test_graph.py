@@ -17,7 +17,9 @@ import pytest
 import torch
 
 from tests import helpers
-from tests.gpu_util import Gpu, bf, cfg_of, f32, gpu_available, i32, say, u8
+import synth
+from tests.gpu_util import (Gpu, assert_out_close, assert_states_close, bf, cfg_of, f32,
+                            gpu_available, i32, say, u8)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU and libgdn.so")]
@@ -167,9 +169,20 @@ def _run_graph(with_decodes, plan):
             eager.spec()
         torch.cuda.synchronize()
         t_real = real["num_actual_tokens"]
-        np.testing.assert_array_equal(st.g.host_out()[:t_real], eager.host_out())
-        np.testing.assert_array_equal(st.g.host_conv(), eager.host_conv())
-        np.testing.assert_array_equal(st.g.host_ssm(), eager.host_ssm())
+        out, conv, ssm = st.g.host_out(), st.g.host_conv(), st.g.host_ssm()
+        # the oracle on the unpadded batch
+        ref_out, ref_conv, ref_ssm = helpers.run_case(real)
+        assert_out_close(out[:t_real], ref_out)
+        np.testing.assert_array_equal(conv, ref_conv)
+        named = synth.referenced_slots(real)
+        if len(named):
+            assert_states_close(ssm[named], ref_ssm[named])
+        rest = np.setdiff1d(np.arange(ssm.shape[0]), named)
+        np.testing.assert_array_equal(ssm[rest], real["ssm_state"][rest])
+        # and the eager call on the unpadded batch, bit for bit
+        np.testing.assert_array_equal(out[:t_real], eager.host_out())
+        np.testing.assert_array_equal(conv, eager.host_conv())
+        np.testing.assert_array_equal(ssm, eager.host_ssm())
 
 
 def test_graph_padded_spec_replays():

@@ -249,6 +249,27 @@ def test_exact_recall_orthonormal_keys():
         np.testing.assert_array_equal(out[t, 0], synth.to_bf16(vals[qsel[t]]))
 
 
+def test_l2norm_eps_inside_the_square_root():
+    # q = k = 2 e_1 (sum of squares 4) with eps = 12: the norm is
+    # sqrt(4 + 12) = 4, so q_hat = k_hat = e_1 / 2 exactly.  With beta = 1,
+    # decay 1, scale 1 and a zero prior state, S = v k_hat^T and
+    # o = (k_hat . q_hat) v = v / 4, both exact in binary.  eps added outside
+    # the root (2 / (2 + 12)) or dropped (e_1) gives v / 49 or v.
+    dk, dv = 8, 4
+    case = small_case(seed=12, Hk=1, Hv=1, dk=dk, dv=dv, K=1, T=1, eps=12.0, scale=1.0)
+    _identity_conv(case)
+    case["A_log"][:] = -np.inf
+    case["b"][:] = synth.to_bf16(np.full(case["b"].shape, np.inf, np.float32))
+    v = np.array([1.0, -2.0, 0.5, 3.0], np.float32)
+    _set_blocks(case, 0, q=2 * np.eye(dk)[1], k=2 * np.eye(dk)[1], v=v)
+    case["ssm_state"][3] = 0.0
+    out, _, ssm, _ = run_spec(case, spec_meta([0, 1], [[3]], [1]))
+    np.testing.assert_array_equal(out[0, 0], synth.to_bf16(v / 4))
+    want = np.zeros((dv, dk), np.float32)
+    want[:, 1] = v / 2
+    np.testing.assert_array_equal(ssm[3, 0], want)
+
+
 def test_last_write_recall_any_state():
     # beta = 1 and a unit key give S_t k_t = v_t whatever S_{t-1} and alpha;
     # the query equal to the key returns scale * v_t.
