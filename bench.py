@@ -9,7 +9,13 @@ have), so no step finds the previous step's states in the last-level cache.
 
 Prints one JSON line: tokens/s, us per layer, achieved HBM bandwidth of the
 kernel against the 8 TB/s MI355X peak, and the CPU oracle timed on a bounded
-sample of the same workload.
+sample of the same workload (one thread, then all the host's threads).
+Beside the headline mean over the timed region: the median, p10 and p90 of
+one series of the same steps (an event between consecutive calls), a
+labelled "hot" series (one layer back to back), and a measured same-GPU
+ceiling for the step's state traffic (a kernel that only reads each row's
+state blocks and writes them to the store slots, on the same layers and
+metadata).
 """
 from __future__ import annotations
 
@@ -97,25 +103,87 @@ def chunked_flops(case) -> int:
     return int(total)
 
 
-def cpu_baseline(case, min_seconds=10.0):
-    """The oracle (single-threaded C, fp64) on the whole batch, repeated until
-    at least ``min_seconds`` of CPU time has been spent."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _host_threads():
+    """Threads this process may use: its CPU affinity (else the CPU count),
+    capped by OMP_NUM_THREADS when that is set (the host's share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS")
+    return max(1, min(n, int(cap))) if cap and cap.isdigit() else n
+
+
+def oracle_row_blocks(case, nthreads):
+    """The spec metadata split into ``nthreads`` contiguous blocks of rows
+    (each keeping its tokens' global rows)."""
+    from tests.gpu_util import sub_spec
+    sp = case["spec"]
+    bounds = np.linspace(0, sp["num_spec_decodes"], nthreads + 1).astype(int)
+    return [sub_spec(sp, list(range(bounds[i], bounds[i + 1]))) for i in range(nthreads)]
+
+
+def oracle_threaded(dims, c, parts, out):
+    """One oracle step with one thread per block of rows, in place on the
+    pools of ``c`` and on ``out`` (the blocks touch disjoint slots and rows)."""
+    import threading
+
+    import oracle  # test infrastructure: the baseline leg only
+    ts = [threading.Thread(target=oracle.spec_step, args=(dims, c, p, out)) for p in parts]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+
+
+def cpu_baseline(case, seconds=(8.0, 8.0)):
+    """The oracle (C, fp64) on the whole batch, repeated for a bounded time:
+    first on one thread, then on N threads, each taking a contiguous block of
+    rows (rows use disjoint slots and token rows; ctypes releases the GIL
+    during each call).  Results are the same bits at any thread count."""
     import oracle  # test infrastructure: the baseline leg only
     from tests.helpers import clone
     c = clone(case)
     sp = case["spec"]
     out = np.zeros((case["num_actual_tokens"], case["dims"]["Hv"], case["dims"]["dv"]), np.uint16)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.spec_step(case["dims"], c, sp, out)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    return {"value": reps * sp["num_spec_tokens"] / dt, "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"the whole batch ({sp['num_spec_decodes']} rows, {sp['num_spec_tokens']} "
-                      f"tokens) {reps} times in a row on one thread, {dt:.1f} s"}
+    nrows = sp["num_spec_decodes"]
+    nthreads = max(1, min(_host_threads(), nrows))
+    parts = oracle_row_blocks(case, nthreads)
+
+    def run(limit, n):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            if n == 1:
+                oracle.spec_step(case["dims"], c, sp, out)
+            else:
+                oracle_threaded(case["dims"], c, parts, out)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= limit:
+                return reps, dt
+
+    r1, t1 = run(seconds[0], 1)
+    rn, tn = run(seconds[1], nthreads)
+    tok = sp["num_spec_tokens"]
+    return {"value": rn * tok / tn, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"the whole batch ({nrows} rows, {tok} tokens) {rn} times in {tn:.1f} s on "
+                      f"{nthreads} threads (a block of rows each)",
+            "one_thread": {"value": r1 * tok / t1, "unit": "tokens/s", "cores": 1,
+                           "sample": f"the whole batch {r1} times in {t1:.1f} s on one thread"},
+            "us_per_layer": tn / rn * 1e6, "us_per_layer_one_thread": t1 / r1 * 1e6,
+            "host_cpu": _cpu_model(), "host_threads": _host_threads()}
 
 
 def profiled_traffic(workload):
@@ -134,36 +202,68 @@ def profiled_traffic(workload):
     return rec.get("bytes_per_launch") if rec.get("source_sha256_16") == cur else None
 
 
-def same_box_ceilings(stream, achieved_gbs, mib=256, reps=20):
-    """Plain torch copy and fill rates on this GPU (context for the HBM peak:
-    what streaming kernels with no arithmetic reach here), timed with events
-    on the launch stream."""
+def state_bytes(case) -> int:
+    """The state part of the algorithmic bytes: load and per-token stores."""
+    d, sp = case["dims"], case["spec"]
+    tile = d["Hv"] * d["dv"] * d["dk"] * 4
+    sq, ssi, nacc = sp["spec_query_start_loc"], sp["spec_state_indices"], sp["num_accepted_tokens"]
+    total = 0
+    for b in range(sp["num_spec_decodes"]):
+        Tb = int(sq[b + 1] - sq[b])
+        total += tile * (int(ssi[b][int(nacc[b]) - 1] > 0) + int((ssi[b][:Tb] > 0).sum()))
+    return int(total)
+
+
+def _bench_lib():
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "speculative_decoding_causal_amd", "libgdn_bench.so"))
+    lib.gdn_bench_state_fanout.argtypes = [ctypes.c_void_p] + [ctypes.c_int32] * 7 + \
+        [ctypes.c_void_p] * 4
+    lib.gdn_bench_state_fanout.restype = ctypes.c_int
+    return lib
+
+
+def state_fanout_ceiling(case, layers, meta, stream, steps, achieved_gbs):
+    """The step's state traffic alone (gdn_bench_state_fanout: each row's
+    state blocks read from the load slot and written to every store slot, no
+    arithmetic) on the same layers and metadata, timed the same way: a
+    measured ceiling for the access pattern on this GPU."""
+    lib = _bench_lib()
+    d, sp = case["dims"], case["spec"]
+
+    def call(i):
+        L = layers[i % len(layers)]
+        rc = lib.gdn_bench_state_fanout(L["ssm"].data_ptr(), d["num_slots"], d["Hk"], d["Hv"],
+                                        d["dk"], d["dv"], sp["num_spec_decodes"], sp["K"],
+                                        meta["sqsl"].data_ptr(), meta["ssi"].data_ptr(),
+                                        meta["nacc"].data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"gdn_bench_state_fanout failed ({rc})")
+
+    for i in range(5):
+        call(i)
+    series = time_series(call, steps, stream, start=5)
+    sb = state_bytes(case)
+    gbs = sb / (series["mean_us"] * 1e-6) / 1e9
+    return {"kernel": "gdn_bench_state_fanout (state load + per-token stores, no arithmetic)",
+            "state_bytes_per_launch": sb, "series_us": series, "achieved_GBs": gbs,
+            "frac_of_peak": gbs / HBM_PEAK_GBS, "frac_of_ceiling": achieved_gbs / gbs}
+
+
+def time_series(fn, n, stream, start=0):
+    """n calls back to back with one event between consecutive calls: the
+    intervals sum to the whole region, so their median, p10 and p90 describe
+    the same series as the mean."""
     import torch
-    n = (mib << 20) // 4
-    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
-    dst = torch.empty_like(src)
-    rates = {}
-    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * n * 4),
-                            ("fill", lambda: dst.fill_(1.0), n * 4)):
-        fn()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        rates[name] = moved * reps / (a.elapsed_time(b) * 1e-3) / 1e9
-    del src, dst
-    # one read per three writes, as the spec step moves its state: a copy of
-    # a quarter of the bytes (read + write) and a fill of the other half, run
-    # one after the other
-    mix = 1.0 / (0.5 / rates["copy"] + 0.5 / rates["fill"])
-    return {"copy_GBs": rates["copy"], "fill_GBs": rates["fill"], "mix_1r3w_GBs": mix,
-            "frac_of_copy": achieved_gbs / rates["copy"],
-            "frac_of_fill": achieved_gbs / rates["fill"],
-            "frac_of_mix_1r3w": achieved_gbs / mix,
-            "what": f"torch copy_ of {mib} MiB (read + write counted) and fill_ of {mib} MiB, "
-                    f"{reps} each"}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record(stream)
+    for i in range(n):
+        fn(start + i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)])
+    return {"mean_us": float(us.mean()), "median_us": float(np.median(us)),
+            "p10_us": float(np.percentile(us, 10)), "p90_us": float(np.percentile(us, 90))}
 
 
 def main():
@@ -264,17 +364,14 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_begin.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    # Per-launch kernel durations: events on the launch stream around each call.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    # The same steps again with an event between consecutive calls (layers
+    # cycled: cold states): median, p10 and p90 of one series.
+    cold = time_series(step, args.steps, stream, start=args.warmup)
+    # Hot: one layer called back to back, so its states may sit in the
+    # last-level cache between calls (labelled; not the headline).
+    hot = time_series(lambda i: step(0), max(args.steps // 2, 10), stream)
     # Kernel time per launch over the timed region (one launch per step for
-    # the spec workload); the per-launch event pairs give the spread.
+    # the spec workload).
     avg_launch_s = ms_per_step * 1e-3
     nbytes = algorithmic_bytes(case) + (nonspec_bytes(case) if ns is not None else 0)
     achieved = nbytes / avg_launch_s / 1e9
@@ -306,10 +403,11 @@ def main():
                      "kernel": "gdn_rows_kernel (dk=dv=128)",
                      "algorithmic_bytes_per_launch": nbytes,
                      "avg_launch_us": avg_launch_s * 1e6,
-                     "p10_launch_us": float(np.percentile(launch_ms, 10)) * 1e3,
-                     "p90_launch_us": float(np.percentile(launch_ms, 90)) * 1e3},
+                     "series_us": cold, "hot_series_us": hot},
     }
-    result["roofline"]["same_box"] = same_box_ceilings(stream, achieved)
+    if ns is None:
+        result["roofline"]["same_box"] = state_fanout_ceiling(case, layers, meta, stream,
+                                                              args.steps, achieved)
     if ns is None and args.workload != DEFAULT_WORKLOAD:
         # the headline metric names its own batch; other spec batches say theirs
         result["metric"] = (f"GDN layer tokens/sec + us/layer + % HBM peak, spec verify "

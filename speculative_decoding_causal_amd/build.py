@@ -9,6 +9,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
 SOURCES = ["gdn_api.cpp", "gdn_rows.hip", "gdn_prefill.hip", "gdn_chunk.hip"]
+# measurement kernels for the benchmark (include/gdn_bench.h), a library of
+# their own so that the step's library holds only the step
+BENCH_LIB = os.path.join(HERE, "libgdn_bench.so")
+BENCH_SOURCES = ["bench_ceiling.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -22,12 +26,13 @@ HIPCC_FLAGS = [
 ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
 
 
-def build(verbose: bool = False, out: str = LIB, asan: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, asan: bool = False,
+          sources=SOURCES) -> str:
     """Compile every source and link ``libgdn.so`` (or ``out``); returns its
     path.  Sources compile in parallel."""
     objs, procs = [], []
     tag = ".asan" if asan else ""
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(CSRC, os.path.splitext(src)[0] + tag + ".o")
         cmd = ["hipcc", *HIPCC_FLAGS, *(ASAN_FLAGS if asan else []), "-x", "hip", "-c",
                os.path.join(CSRC, src), "-o", obj]
@@ -58,3 +63,4 @@ if __name__ == "__main__":
         print(build(verbose="-v" in args, out=os.path.abspath(args[i + 1]), asan=True))
     else:
         print(build(verbose="-v" in args))
+        print(build(verbose="-v" in args, out=BENCH_LIB, sources=BENCH_SOURCES))

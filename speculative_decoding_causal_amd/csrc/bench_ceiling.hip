@@ -1,0 +1,73 @@
+// Measured ceiling for the spec-verify step's state traffic: the load and
+// per-token stores of every (row, k-head) state block, with no arithmetic.
+// Declared in include/gdn_bench.h; built into libgdn_bench.so, which the
+// benchmark loads beside libgdn.so.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gdn_bench.h"
+
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+constexpr int kThreads = 512;
+constexpr int kPer = 16;                           // float4 per thread
+constexpr int kBlockFloats = kThreads * kPer * 4;  // 128 KiB
+
+__device__ __forceinline__ int clamp_i(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+__global__ void __launch_bounds__(kThreads)
+state_fanout(float* pool, int num_slots, int Hk, int Hv, int num_rows, int K, const int* qsl,
+             const int* ssi, const int* nacc, size_t slot_floats) {
+  // workgroup i runs on XCD i % 8: the k-heads of a row share i % 8
+  const int q8 = blockIdx.x >> 3;
+  const int ih = q8 % Hk;
+  const int row = (q8 / Hk) * 8 + (blockIdx.x & 7);
+  if (row >= num_rows) return;
+  const int tid = threadIdx.x;
+  const int j0 = qsl[row];
+  const int T = clamp_i(qsl[row + 1] - j0, 0, K);
+  if (T <= 0) return;
+  const int* s = ssi + (size_t)row * K;
+  const int ls = s[clamp_i(nacc[row], 1, T) - 1];
+  const bool load = ls > 0 && ls < num_slots;
+  const size_t off = (size_t)ih * kBlockFloats;
+  const v4f* src = reinterpret_cast<const v4f*>(pool + (size_t)(load ? ls : 0) * slot_floats + off);
+  v4f S[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) S[e] = __builtin_nontemporal_load(src + e * kThreads + tid);
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) S[e] = load ? S[e] : v4f{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < T; ++t) {
+    const int st = s[t];
+    if (st <= 0 || st >= num_slots) continue;
+    v4f* dst = reinterpret_cast<v4f*>(pool + (size_t)st * slot_floats + off);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      v4f v = S[e];
+      if (e == 0 && tid == 0) v.x += (float)t;
+      __builtin_nontemporal_store(v, dst + e * kThreads + tid);
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" int gdn_bench_state_fanout(float* ssm_state, int32_t num_slots, int32_t num_k_heads,
+                                      int32_t num_v_heads, int32_t head_k_dim,
+                                      int32_t head_v_dim, int32_t num_rows,
+                                      int32_t max_spec_len, const int32_t* qsl,
+                                      const int32_t* ssi, const int32_t* nacc, void* stream) {
+  if (!ssm_state || !qsl || !ssi || !nacc || num_k_heads <= 0 || num_v_heads % num_k_heads ||
+      num_rows < 0 || max_spec_len < 1 || num_slots <= 0)
+    return -1;
+  const long long block = (long long)(num_v_heads / num_k_heads) * head_v_dim * head_k_dim;
+  if (block != kBlockFloats) return -1;
+  if (num_rows == 0) return 0;
+  const size_t slot_floats = (size_t)num_v_heads * head_v_dim * head_k_dim;
+  const unsigned grid = (unsigned)((num_rows + 7) / 8 * 8) * (unsigned)num_k_heads;
+  hipLaunchKernelGGL(state_fanout, dim3(grid), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), ssm_state, num_slots, num_k_heads,
+                     num_v_heads, num_rows, max_spec_len, qsl, ssi, nacc, slot_floats);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}

@@ -19,8 +19,8 @@ L = gdn._lib
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(gdn_[a-z_]+)\s*\(",
                                  text, flags=re.M)))
@@ -31,6 +31,21 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == set(gdn.EXPORTED_SYMBOLS), names
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_bench_library_exports_its_header():
+    # the measurement kernels of include/gdn_bench.h live in libgdn_bench.so
+    names = declared_functions(os.path.join(ROOT, "include", "gdn_bench.h"))
+    assert names == ["gdn_bench_state_fanout"], names
+    lib = ctypes.CDLL(os.path.join(ROOT, "speculative_decoding_causal_amd", "libgdn_bench.so"))
+    for n in names:
+        assert hasattr(lib, n), n
+    # shapes it does not support and NULL pointers are refused before a launch
+    f = lib.gdn_bench_state_fanout
+    f.argtypes = [ctypes.c_void_p] + [ctypes.c_int32] * 7 + [ctypes.c_void_p] * 4
+    assert f(FAKE, 512, 16, 32, 64, 64, 64, 3, FAKE, FAKE, FAKE, None) == -1
+    assert f(None, 512, 16, 32, 128, 128, 64, 3, FAKE, FAKE, FAKE, None) == -1
+    assert f(FAKE, 512, 16, 32, 128, 128, 0, 3, FAKE, FAKE, FAKE, None) == 0
 
 
 def dims(**kw):
