@@ -242,7 +242,7 @@ def state_fanout_ceiling(case, layers, meta, stream, steps, achieved_gbs):
 
     for i in range(5):
         call(i)
-    series = time_series(call, steps, stream, start=5)
+    series = time_series(call, steps, stream, start=5, block=len(layers))
     sb = state_bytes(case)
     gbs = sb / (series["mean_us"] * 1e-6) / 1e9
     return {"kernel": "gdn_bench_state_fanout (state load + per-token stores, no arithmetic)",
@@ -250,20 +250,25 @@ def state_fanout_ceiling(case, layers, meta, stream, steps, achieved_gbs):
             "frac_of_peak": gbs / HBM_PEAK_GBS, "frac_of_ceiling": achieved_gbs / gbs}
 
 
-def time_series(fn, n, stream, start=0):
-    """n calls back to back with one event between consecutive calls: the
-    intervals sum to the whole region, so their median, p10 and p90 describe
-    the same series as the mean."""
+def time_series(fn, n, stream, start=0, block=8):
+    """n calls back to back in blocks of ``block`` calls with one event
+    between consecutive blocks: each sample is a block's time per call (the
+    events' own cost spread over the block), the samples sum to the whole
+    region, and their median, p10 and p90 describe the same series as the
+    mean."""
     import torch
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    nb = max(n // block, 1)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
     ev[0].record(stream)
-    for i in range(n):
-        fn(start + i)
+    for i in range(nb):
+        for j in range(block):
+            fn(start + i * block + j)
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    us = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)])
+    us = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 / block for i in range(nb)])
     return {"mean_us": float(us.mean()), "median_us": float(np.median(us)),
-            "p10_us": float(np.percentile(us, 10)), "p90_us": float(np.percentile(us, 90))}
+            "p10_us": float(np.percentile(us, 10)), "p90_us": float(np.percentile(us, 90)),
+            "samples": int(nb), "calls_per_sample": int(block)}
 
 
 def main():
@@ -364,12 +369,12 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_begin.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    # The same steps again with an event between consecutive calls (layers
-    # cycled: cold states): median, p10 and p90 of one series.
-    cold = time_series(step, args.steps, stream, start=args.warmup)
+    # The same steps again with an event after every block of `layers` calls
+    # (layers cycled: cold states): median, p10 and p90 of one series.
+    cold = time_series(step, args.steps, stream, start=args.warmup, block=args.layers)
     # Hot: one layer called back to back, so its states may sit in the
     # last-level cache between calls (labelled; not the headline).
-    hot = time_series(lambda i: step(0), max(args.steps // 2, 10), stream)
+    hot = time_series(lambda i: step(0), args.steps, stream, block=args.layers)
     # Kernel time per launch over the timed region (one launch per step for
     # the spec workload).
     avg_launch_s = ms_per_step * 1e-3

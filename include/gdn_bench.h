@@ -29,8 +29,8 @@ extern "C" {
  *   stream: hipStream_t (NULL = default stream)
  *
  * One 512-thread workgroup per (row, k-head), the k-heads of a row on one
- * XCD; each wave instruction moves 1 KiB of consecutive bytes with
- * non-temporal loads and stores.  Supports G*dv*dk == 32768 (a 128 KiB
+ * XCD, one workgroup per CU; each wave instruction moves 1 KiB of
+ * consecutive bytes with non-temporal loads and stores.  Supports G*dv*dk == 32768 (a 128 KiB
  * block, e.g. Hv/Hk = 2 with dk = dv = 128).  Slots, n_acc and T_b are
  * clamped to stay inside the pool.  Returns 0, -1 for an unsupported shape
  * or NULL pointer, -7 when the launch fails.

@@ -17,7 +17,9 @@
 //   3. the recurrence, streaming the G*dv state rows of the k-head's v-heads
 //      through VGPRs: each state row of dk floats is spread over dk/16 lanes
 //      (16 floats, four float4 each), so row dot products need dk/16-lane DPP
-//      sums and every global access moves full 128-byte lines.  The state of
+//      sums and every global access moves full 128-byte lines (at dk = 128
+//      the waves' rows interleave, so one instruction of the workgroup
+//      covers 64 consecutive rows).  The state of
 //      each token is stored to its slot (spec) or only the final one
 //      (non-spec).  The initial-state load precedes every store of the row.
 //   4. outputs remapped through token_indx, as bf16.
@@ -124,8 +126,12 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 // For dk = 128: state rows per lane (R), threads per workgroup (T), the
 // waves per SIMD the registers are fitted to (WPE), rows taken through all
-// tokens at a time (RB), and whether snapshots use non-temporal stores; all
-// chosen by measurement on MI355X.
+// tokens at a time (RB), whether snapshots use non-temporal stores, the row
+// order (ORDER: 1 interleaves the waves, so each instruction of the
+// workgroup covers 64 consecutive state rows) and a floor on the dynamic LDS
+// (LDS_MIN: above half of the CU's 160 KiB, so one workgroup runs per CU);
+// all chosen by measurement on MI355X: one interleaved workgroup per CU
+// moves the state about 2% faster than two banded ones.
 #ifndef GDN_ROWS_R128
 #define GDN_ROWS_R128 4
 #endif
@@ -140,6 +146,12 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 #endif
 #ifndef GDN_NT_STORE
 #define GDN_NT_STORE 1
+#endif
+#ifndef GDN_ROWS_ORDER128
+#define GDN_ROWS_ORDER128 1
+#endif
+#ifndef GDN_ROWS_LDS_MIN128
+#define GDN_ROWS_LDS_MIN128 (80 * 1024 + 16)
 #endif
 
 __device__ __forceinline__ void store_row4(float* p, v4f v) {
@@ -156,12 +168,12 @@ __device__ __forceinline__ void store_row4(float* p, v4f v) {
 // NULL slot (slot 0 stands in) and rows past NR re-read row NR-1;
 // zero_rows drops those values where the rows are first used, so the loads
 // stay in flight until then.
-template <int DK, int R, int LPR, int RPW>
+template <int DK, int R, int LPR, int SS>
 __device__ __forceinline__ void load_rows(v4f (&S)[R][4], const float* base, int rho0, int jl,
                                           int NR) {
 #pragma unroll
   for (int s = 0; s < R; ++s) {
-    const int rho = rho0 + s * RPW;
+    const int rho = rho0 + s * SS;
     const int rc = rho < NR ? rho : NR - 1;
 #pragma unroll
     for (int n = 0; n < 4; ++n)
@@ -170,11 +182,11 @@ __device__ __forceinline__ void load_rows(v4f (&S)[R][4], const float* base, int
   }
 }
 
-template <int R, int RPW>
+template <int R, int SS>
 __device__ __forceinline__ void zero_rows(v4f (&S)[R][4], bool valid, int rho0, int NR) {
 #pragma unroll
   for (int s = 0; s < R; ++s) {
-    const bool keep = valid && rho0 + s * RPW < NR;
+    const bool keep = valid && rho0 + s * SS < NR;
 #pragma unroll
     for (int n = 0; n < 4; ++n) S[s][n] = keep ? S[s][n] : v4f{0.f, 0.f, 0.f, 0.f};
   }
@@ -310,7 +322,7 @@ __device__ __forceinline__ void conv_chan(const float (&w)[kMaxWidth], float bia
 // NT threads per workgroup, R state rows per lane; WPE waves per SIMD is the
 // occupancy the register budget is fitted to.  LM / KT bound state_len and
 // the tokens per row for the register gathers of the conv phase.
-template <int DK, int DV, int R, int NT, int WPE, int LM, int KT, int RB, bool FUSED>
+template <int DK, int DV, int R, int NT, int WPE, int LM, int KT, int RB, bool FUSED, int ORDER>
 __global__ void __launch_bounds__(NT, WPE)
 gdn_rows_kernel(RowArgs pa) {
   static_assert(R % RB == 0, "row batch");
@@ -409,6 +421,12 @@ gdn_rows_kernel(RowArgs pa) {
                            head_off;
   constexpr int kRowsPerWavePass = RPW * R;
   constexpr int kRowsPerPass = (NT / 64) * kRowsPerWavePass;
+  // Rows of a lane: ORDER 0 gives each wave a band of RPW*R consecutive
+  // rows (sub-row stride RPW); ORDER 1 interleaves the waves, so that the
+  // workgroup's instruction s covers NT/64*RPW consecutive rows (sub-row
+  // stride NT/64*RPW).
+  constexpr int SS = ORDER ? (NT / 64) * RPW : RPW;
+  const int wave_row0 = ORDER ? wv * RPW : wv * kRowsPerWavePass;
   constexpr bool kEarlyRows = LM + KT <= 10;
   v4f S[R][4];
   {
@@ -444,7 +462,7 @@ gdn_rows_kernel(RowArgs pa) {
     // (Only with the smallest register gathers: the others leave no room.)
     if constexpr (kEarlyRows) {
       if (stage != kConvOnly)
-        load_rows<DK, R, LPR, RPW>(S, load_base, wv * kRowsPerWavePass + gl, jl, NR);
+        load_rows<DK, R, LPR, SS>(S, load_base, wave_row0 + gl, jl, NR);
       // keep the state loads ahead of the staging, which waits for the conv inputs
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -484,7 +502,7 @@ gdn_rows_kernel(RowArgs pa) {
   }
   if (stage == kConvOnly) return;
   if constexpr (!kEarlyRows)
-    load_rows<DK, R, LPR, RPW>(S, load_base, wv * kRowsPerWavePass + gl, jl, NR);
+    load_rows<DK, R, LPR, SS>(S, load_base, wave_row0 + gl, jl, NR);
 
 
 
@@ -529,11 +547,11 @@ gdn_rows_kernel(RowArgs pa) {
   // ---- phase 3: recurrence over the state rows -----------------------------
   // Rows are taken RB at a time through all the row's tokens, so the first
   // snapshots are stored as soon as those rows' loads have arrived.
-  for (int r0 = wv * kRowsPerWavePass; r0 < NR; r0 += kRowsPerPass) {
-    const bool full = r0 + kRowsPerWavePass <= NR;
+  for (int r0 = wave_row0; r0 < NR; r0 += kRowsPerPass) {
+    const bool full = r0 + (R - 1) * SS + RPW <= NR;
     const int rho0 = r0 + gl;
-    if (r0 != wv * kRowsPerWavePass) load_rows<DK, R, LPR, RPW>(S, load_base, rho0, jl, NR);
-    zero_rows<R, RPW>(S, load_valid, rho0, NR);
+    if (r0 != wave_row0) load_rows<DK, R, LPR, SS>(S, load_base, rho0, jl, NR);
+    zero_rows<R, SS>(S, load_valid, rho0, NR);
 #pragma unroll
     for (int sb = 0; sb < R; sb += RB) {
       for (int j = 0; j < T; ++j) {
@@ -560,7 +578,7 @@ gdn_rows_kernel(RowArgs pa) {
         }
         const float kqj = kq[j];
         float al[RB], u[RB];
-        if constexpr (DV % kRowsPerWavePass == 0) {
+        if constexpr (ORDER == 0 && DV % kRowsPerWavePass == 0) {
           // The wave's rows lie in one v-head: its gates are wave-uniform.
           const int g = r0 / DV;
           const float alw = __builtin_bit_cast(
@@ -569,7 +587,7 @@ gdn_rows_kernel(RowArgs pa) {
               float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gb[j * G + g])));
 #pragma unroll
           for (int q = 0; q < RB; ++q) {
-            const int rho = rho0 + (sb + q) * RPW;
+            const int rho = rho0 + (sb + q) * SS;
             const float vr = vs[j * NR + (rho < NR ? rho : NR - 1)];
             al[q] = alw;
             // S_new = al S + u k^T with u = be (v - al S k); o = S_new q.
@@ -580,7 +598,7 @@ gdn_rows_kernel(RowArgs pa) {
         } else {
 #pragma unroll
           for (int q = 0; q < RB; ++q) {
-            const int rho = rho0 + (sb + q) * RPW;
+            const int rho = rho0 + (sb + q) * SS;
             const int rr = rho < NR ? rho : NR - 1;
             const int g = rr / DV;
             al[q] = ga[j * G + g];
@@ -608,7 +626,7 @@ gdn_rows_kernel(RowArgs pa) {
           float* base = p.ssm_pool + (size_t)st * slot_stride + head_off;
 #pragma unroll
           for (int q = 0; q < RB; ++q) {
-            const int rho = rho0 + (sb + q) * RPW;
+            const int rho = rho0 + (sb + q) * SS;
             if (full || rho < NR) {
 #pragma unroll
               for (int n = 0; n < 4; ++n)
@@ -634,15 +652,17 @@ template <int DK, int DV, int R, int NT, int WPE, int LM, int KT>
 hipError_t launch_typed(const RowArgs& a, hipStream_t s) {
   const Lds lay = lds_layout(DK, DV, a.G, a.L, launch_row_tokens(a));
   constexpr int RB = DK == 128 ? GDN_ROWS_RB128 : R;
-  auto kern = a.stage == kFused ? gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT, RB, true>
-                                : gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT, RB, false>;
-  if (lay.total > 64 * 1024) {
-    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lay.total);
+  constexpr int ORDER = DK == 128 ? GDN_ROWS_ORDER128 : 0;
+  const int lds = DK == 128 && lay.total < GDN_ROWS_LDS_MIN128 ? GDN_ROWS_LDS_MIN128 : lay.total;
+  auto kern = a.stage == kFused ? gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT, RB, true, ORDER>
+                                : gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT, RB, false, ORDER>;
+  if (lds > 64 * 1024) {
+    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lds);
     if (e != hipSuccess) return e;
   }
   const int rows = a.num_rows + (a.more.num_rows > 0 ? a.more.num_rows : 0);
   dim3 grid(static_cast<unsigned>((rows + 7) / 8 * 8) * static_cast<unsigned>(a.Hk));
-  hipLaunchKernelGGL(kern, grid, dim3(NT), lay.total, s, a);
+  hipLaunchKernelGGL(kern, grid, dim3(NT), lds, s, a);
   return hipGetLastError();
 }
 
