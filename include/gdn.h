@@ -237,6 +237,40 @@ int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
                   gdn_bf16* core_attn_out, void* workspace,
                   size_t workspace_bytes, gdn_stream_t stream);
 
+/*
+ * gdn_attention_static - gdn_attention for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without the workspace.  Prefill
+ * rows take their scratch from a library-owned static device array of
+ * GDN_STATIC_SCRATCH_BYTES per GPU (held by each GPU the library runs on
+ * until the process ends); a batch whose prefill rows need more
+ * (gdn_workspace_bytes) is rejected with GDN_ERR_WORKSPACE before anything
+ * is enqueued.  Nothing is allocated and nothing needs clearing.  Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other threads) race and must be ordered by the caller.
+ */
+#define GDN_STATIC_SCRATCH_BYTES (64ull << 20)
+int gdn_attention_static(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
+                         const gdn_bf16* a, const gdn_bf16* b,
+                         const gdn_bf16* conv_weight, const gdn_bf16* conv_bias,
+                         const float* A_log, const float* dt_bias,
+                         gdn_bf16* conv_state, float* ssm_state,
+                         int32_t num_actual_tokens,
+                         int32_t num_decodes, int32_t num_prefills,
+                         int32_t num_non_spec_tokens,
+                         const int32_t* query_start_loc,
+                         const int32_t* non_spec_state_indices,
+                         const uint8_t* has_initial_state,
+                         const int32_t* non_spec_token_indx,
+                         int32_t num_spec_decodes, int32_t num_spec_tokens,
+                         int32_t max_spec_len,
+                         const int32_t* spec_query_start_loc,
+                         const int32_t* spec_cache_indices,
+                         const int32_t* spec_state_indices,
+                         const int32_t* num_accepted_tokens,
+                         const int32_t* spec_token_indx,
+                         gdn_bf16* core_attn_out, gdn_stream_t stream);
+
 /* Bytes of workspace gdn_attention needs for a batch whose non-spec stream
  * has at most max_non_spec_tokens tokens, of which max_prefill_rows rows are
  * prefills.  0 when no prefill row is present. */

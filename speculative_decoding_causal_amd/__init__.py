@@ -9,7 +9,7 @@ kernels; there is no CPU fallback, and importing fails loudly when the
 library has not been built.
 
 Entry points (same names as the C ABI):
-  gdn_spec_attention, gdn_attention, gdn_workspace_bytes, gdn_conv_only,
+  gdn_spec_attention, gdn_attention, gdn_attention_static, gdn_workspace_bytes, gdn_conv_only,
   gdn_delta_rule_only, gdn_check_metadata_host, gdn_status_string,
   gdn_last_error.
 Capture and replay of step calls: ``speculative_decoding_causal_amd.capture``.
@@ -54,7 +54,7 @@ GDN_ROWS_SPEC = 1
 MAX_ROW_TOKENS = 16
 
 EXPORTED_SYMBOLS = (
-    "gdn_spec_attention", "gdn_attention", "gdn_workspace_bytes",
+    "gdn_spec_attention", "gdn_attention", "gdn_attention_static", "gdn_workspace_bytes",
     "gdn_conv_only", "gdn_delta_rule_only", "gdn_check_metadata_host",
     "gdn_status_string", "gdn_last_error",
 )
@@ -89,6 +89,10 @@ _lib.gdn_spec_attention.restype = ctypes.c_int
 _lib.gdn_attention.argtypes = ([ctypes.POINTER(GdnDims)] + [_P] * 9 + [_I] * 4 + [_P] * 4 +
                                [_I] * 3 + [_P] * 5 + [_P, _P, ctypes.c_size_t, _P])
 _lib.gdn_attention.restype = ctypes.c_int
+_lib.gdn_attention_static.argtypes = ([ctypes.POINTER(GdnDims)] + [_P] * 9 + [_I] * 4 + [_P] * 4 +
+                                      [_I] * 3 + [_P] * 5 + [_P, _P])
+_lib.gdn_attention_static.restype = ctypes.c_int
+STATIC_SCRATCH_BYTES = 64 << 20   # GDN_STATIC_SCRATCH_BYTES
 _lib.gdn_workspace_bytes.argtypes = [ctypes.POINTER(GdnDims), _I, _I]
 _lib.gdn_workspace_bytes.restype = ctypes.c_size_t
 _lib.gdn_conv_only.argtypes = [ctypes.POINTER(GdnDims), _P, _P, _P, _P, _I,
@@ -306,6 +310,37 @@ def gdn_attention(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias, A_log
     """A layer step over a batch of non-spec rows (decodes, then prefills)
     and spec rows.  ``workspace`` (uint8 device tensor) is needed when
     ``num_prefills > 0``; size it with ``gdn_workspace_bytes``."""
+    _attention(False, cfg, mixed_qkv, a, b, conv_weight, conv_bias, A_log, dt_bias, conv_state,
+               ssm_state, core_attn_out, num_decodes, num_prefills, num_non_spec_tokens,
+               query_start_loc, non_spec_state_indices, has_initial_state, non_spec_token_indx,
+               spec_query_start_loc, spec_state_indices, num_accepted_tokens, spec_cache_indices,
+               spec_token_indx, num_spec_tokens, workspace, num_actual_tokens, stream)
+
+
+def gdn_attention_static(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias, A_log,
+                         dt_bias, conv_state, ssm_state, core_attn_out, *,
+                         num_decodes=0, num_prefills=0, num_non_spec_tokens=0,
+                         query_start_loc=None, non_spec_state_indices=None,
+                         has_initial_state=None, non_spec_token_indx=None,
+                         spec_query_start_loc=None, spec_state_indices=None,
+                         num_accepted_tokens=None, spec_cache_indices=None,
+                         spec_token_indx=None, num_spec_tokens=None,
+                         num_actual_tokens=None, stream=None) -> None:
+    """``gdn_attention`` without a workspace: prefill rows use the library's
+    static per-GPU scratch (STATIC_SCRATCH_BYTES); nothing is allocated.
+    Calls that overlap on one GPU share that scratch and race."""
+    _attention(True, cfg, mixed_qkv, a, b, conv_weight, conv_bias, A_log, dt_bias, conv_state,
+               ssm_state, core_attn_out, num_decodes, num_prefills, num_non_spec_tokens,
+               query_start_loc, non_spec_state_indices, has_initial_state, non_spec_token_indx,
+               spec_query_start_loc, spec_state_indices, num_accepted_tokens, spec_cache_indices,
+               spec_token_indx, num_spec_tokens, None, num_actual_tokens, stream)
+
+
+def _attention(static, cfg, mixed_qkv, a, b, conv_weight, conv_bias, A_log, dt_bias, conv_state,
+               ssm_state, core_attn_out, num_decodes, num_prefills, num_non_spec_tokens,
+               query_start_loc, non_spec_state_indices, has_initial_state, non_spec_token_indx,
+               spec_query_start_loc, spec_state_indices, num_accepted_tokens, spec_cache_indices,
+               spec_token_indx, num_spec_tokens, workspace, num_actual_tokens, stream):
     dev = mixed_qkv.device
     _check_pools(cfg, conv_state, ssm_state)
     dims = cfg.dims(conv_state)
@@ -320,9 +355,7 @@ def gdn_attention(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias, A_log
     _check_nonspec_meta(int(num_decodes) + int(num_prefills), int(num_non_spec_tokens),
                         query_start_loc, non_spec_state_indices, has_initial_state,
                         non_spec_token_indx)
-    ws_ptr = _ptr(workspace, None, "workspace", dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = _lib.gdn_attention(
+    args = [
         ctypes.byref(dims), _ptr(mixed_qkv, _BF16, "mixed_qkv", dev), _ptr(a, _BF16, "a", dev),
         _ptr(b, _BF16, "b", dev), _ptr(conv_weight, _BF16, "conv_weight", dev),
         _ptr(conv_bias, _BF16, "conv_bias", dev), _ptr(A_log, torch.float32, "A_log", dev),
@@ -339,10 +372,15 @@ def gdn_attention(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias, A_log
         _ptr(spec_state_indices, _I32, "spec_state_indices", dev),
         _ptr(num_accepted_tokens, _I32, "num_accepted_tokens", dev),
         _ptr(spec_token_indx, _I32, "spec_token_indx", dev),
-        _ptr(core_attn_out, _BF16, "core_attn_out", dev), ws_ptr, ctypes.c_size_t(ws_bytes),
-        _stream(stream))
+        _ptr(core_attn_out, _BF16, "core_attn_out", dev)]
+    if static:
+        rc = _lib.gdn_attention_static(*args, _stream(stream))
+    else:
+        ws_ptr = _ptr(workspace, None, "workspace", dev)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        rc = _lib.gdn_attention(*args, ws_ptr, ctypes.c_size_t(ws_bytes), _stream(stream))
     if rc != GDN_OK:
-        raise GdnError(rc, "gdn_attention")
+        raise GdnError(rc, "gdn_attention_static" if static else "gdn_attention")
 
 
 def _rows(kind, query_start_loc, num_tokens, max_row_tokens, cache_indices=None,

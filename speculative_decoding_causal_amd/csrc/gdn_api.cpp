@@ -692,4 +692,84 @@ int gdn_check_metadata_host(const gdn_dims* dims, int32_t num_actual_tokens,
   return GDN_OK;
 }
 
+// ---- allocation-free variant of gdn_attention ------------------------------
+// For callers that cannot allocate device memory: the prefill rows' scratch
+// comes from this file-scope array instead of a caller workspace.  Each GPU
+// the library runs on holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, so its device address is taken
+// once per device with hipGetSymbolAddress and only that address is used.
+static __device__ __align__(256) unsigned char scratch[GDN_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (taken on the first call
+// on each device).
+int static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GDN_ERR_UNSUPPORTED, "device %d beyond the %d the static scratch tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(GDN_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+
+}  // namespace
+
+int gdn_attention_static(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
+                         const gdn_bf16* a, const gdn_bf16* b,
+                         const gdn_bf16* conv_weight, const gdn_bf16* conv_bias,
+                         const float* A_log, const float* dt_bias,
+                         gdn_bf16* conv_state, float* ssm_state,
+                         int32_t num_actual_tokens,
+                         int32_t num_decodes, int32_t num_prefills,
+                         int32_t num_non_spec_tokens,
+                         const int32_t* query_start_loc,
+                         const int32_t* non_spec_state_indices,
+                         const uint8_t* has_initial_state,
+                         const int32_t* non_spec_token_indx,
+                         int32_t num_spec_decodes, int32_t num_spec_tokens,
+                         int32_t max_spec_len,
+                         const int32_t* spec_query_start_loc,
+                         const int32_t* spec_cache_indices,
+                         const int32_t* spec_state_indices,
+                         const int32_t* num_accepted_tokens,
+                         const int32_t* spec_token_indx,
+                         gdn_bf16* core_attn_out, gdn_stream_t stream) {
+  if (int e = check_dims(dims)) return e;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (num_prefills > 0 && num_non_spec_tokens > 0) {
+    const size_t need = gdn_workspace_bytes(dims, num_non_spec_tokens, num_prefills);
+    if (need > (size_t)GDN_STATIC_SCRATCH_BYTES)
+      return fail(GDN_ERR_WORKSPACE,
+                  "prefill rows need %zu bytes of scratch; the static scratch holds %zu "
+                  "(use gdn_attention with a workspace)",
+                  need, (size_t)GDN_STATIC_SCRATCH_BYTES);
+    if (int e = static_scratch(&ws)) return e;
+    ws_bytes = GDN_STATIC_SCRATCH_BYTES;
+  }
+  return gdn_attention(dims, mixed_qkv, a, b, conv_weight, conv_bias, A_log, dt_bias, conv_state,
+                       ssm_state, num_actual_tokens, num_decodes, num_prefills,
+                       num_non_spec_tokens, query_start_loc, non_spec_state_indices,
+                       has_initial_state, non_spec_token_indx, num_spec_decodes,
+                       num_spec_tokens, max_spec_len, spec_query_start_loc, spec_cache_indices,
+                       spec_state_indices, num_accepted_tokens, spec_token_indx, core_attn_out,
+                       ws, ws_bytes, stream);
+}
+
 }  // extern "C"

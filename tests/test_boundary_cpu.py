@@ -155,6 +155,25 @@ def test_row_kernel_lds_checked_before_any_launch():
     assert "LDS" in gdn.gdn_last_error()
 
 
+def test_static_entry_point_rejects_batches_beyond_its_scratch():
+    # gdn_attention_static: prefill rows whose scratch exceeds the static
+    # array are refused (GDN_ERR_WORKSPACE) before any HIP call
+    d = dims()
+    nns = 4096
+    need = L.gdn_workspace_bytes(ctypes.byref(d), nns, 1)
+    assert need > gdn.STATIC_SCRATCH_BYTES
+    rc = L.gdn_attention_static(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                FAKE, nns, 0, 1, nns, FAKE, FAKE, None, None, 0, 0, 1, None,
+                                None, None, None, None, FAKE, None)
+    assert rc == gdn.GDN_ERR_WORKSPACE, gdn.gdn_last_error()
+    assert "static scratch holds 67108864" in gdn.gdn_last_error()
+    # dimension errors come first, as in gdn_attention
+    assert L.gdn_attention_static(ctypes.byref(dims(head_k_dim=96, head_v_dim=96)), FAKE, FAKE,
+                                  FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, nns, 0, 1, nns, FAKE,
+                                  FAKE, None, None, 0, 0, 1, None, None, None, None, None, FAKE,
+                                  None) == gdn.GDN_ERR_UNSUPPORTED
+
+
 def test_status_strings():
     for code in range(0, -10, -1):
         assert gdn.gdn_status_string(code) != "unknown status"
