@@ -50,6 +50,23 @@ hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes) {
   if (e == hipSuccess) done.push_back({kernel, dev, bytes});
   return e;
 }
+hipError_t device_cu_count(int* cus) {
+  static std::mutex mu;
+  static std::vector<int> count;  // by device, 0 until queried
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= (int)count.size()) count.resize(dev + 1, 0);
+  if (count[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    count[dev] = n > 0 ? n : 1;
+  }
+  *cus = count[dev];
+  return hipSuccess;
+}
 }  // namespace gdn
 
 namespace {

@@ -20,6 +20,9 @@ enum Stage : int { kFused = 0, kConvOnly = 1, kDeltaOnly = 2 };
 // captured into a graph; the attribute is set outside any stream work).
 hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes);
 
+// Compute units of the current device (queried once per device).
+hipError_t device_cu_count(int* cus);
+
 // Everything one launch of the row kernel needs, passed by value.
 struct RowArgs {
   // shape

@@ -130,8 +130,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // order (ORDER: 1 interleaves the waves, so each instruction of the
 // workgroup covers 64 consecutive state rows) and a floor on the dynamic LDS
 // (LDS_MIN: above half of the CU's 160 KiB, so one workgroup runs per CU);
-// all chosen by measurement on MI355X: one interleaved workgroup per CU
-// moves the state about 2% faster than two banded ones.
+// all chosen by measurement on MI355X: with more than three (row, k-head)
+// units per CU, one interleaved workgroup per CU moves the state about 2%
+// faster than two banded ones; with fewer, two per CU finish in fewer rounds
+// (5% faster at two units per CU), so the floor applies only above three.
 #ifndef GDN_ROWS_R128
 #define GDN_ROWS_R128 4
 #endif
@@ -653,15 +655,23 @@ hipError_t launch_typed(const RowArgs& a, hipStream_t s) {
   const Lds lay = lds_layout(DK, DV, a.G, a.L, launch_row_tokens(a));
   constexpr int RB = DK == 128 ? GDN_ROWS_RB128 : R;
   constexpr int ORDER = DK == 128 ? GDN_ROWS_ORDER128 : 0;
-  const int lds = DK == 128 && lay.total < GDN_ROWS_LDS_MIN128 ? GDN_ROWS_LDS_MIN128 : lay.total;
+  const int rows = a.num_rows + (a.more.num_rows > 0 ? a.more.num_rows : 0);
+  // units: (row, k-head), rows padded to whole groups of 8
+  const unsigned units = static_cast<unsigned>((rows + 7) / 8 * 8) * static_cast<unsigned>(a.Hk);
+  int cus = 0;
+  if (DK == 128) {
+    hipError_t e = device_cu_count(&cus);
+    if (e != hipSuccess) return e;
+  }
+  const bool one_per_cu = DK == 128 && units > 3u * static_cast<unsigned>(cus);
+  const int lds = one_per_cu && lay.total < GDN_ROWS_LDS_MIN128 ? GDN_ROWS_LDS_MIN128 : lay.total;
   auto kern = a.stage == kFused ? gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT, RB, true, ORDER>
                                 : gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT, RB, false, ORDER>;
   if (lds > 64 * 1024) {
     hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lds);
     if (e != hipSuccess) return e;
   }
-  const int rows = a.num_rows + (a.more.num_rows > 0 ? a.more.num_rows : 0);
-  dim3 grid(static_cast<unsigned>((rows + 7) / 8 * 8) * static_cast<unsigned>(a.Hk));
+  dim3 grid(units);
   hipLaunchKernelGGL(kern, grid, dim3(NT), lds, s, a);
   return hipGetLastError();
 }

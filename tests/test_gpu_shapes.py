@@ -129,3 +129,23 @@ def test_mixed_partial_channel_wave(dk, Hk, Hv):
     slots = synth.referenced_slots(case)
     np.testing.assert_array_equal(g.host_conv(slots), conv_ref[slots])
     assert_states_close(g.host_ssm(slots), ssm_ref[slots])
+
+
+@pytest.mark.parametrize("shape", ["K16_ring16", "K16_per_token", "G8_dv1024"])
+def test_spec_maximum_sizes(shape):
+    # The largest shapes the header allows: 16 tokens per row (a width-2 conv
+    # whose 16-column ring keeps the window at n_acc - 1 in range for every
+    # n_acc), 16 tokens per row under the per-token conv contract, and eight
+    # v-heads per k-head at dk = 128 ((Hv/Hk) * dv = 1024 state rows).
+    if shape == "K16_ring16":
+        case = synth.make_case("small", seed=90, K=16, W=2, Ns=5, Hk=2, Hv=4, num_slots=96,
+                               null_p=0.1, permute_tokens=True)
+        assert case["dims"]["L"] == 16
+    elif shape == "K16_per_token":
+        from tests.test_gpu_per_token import per_token_case
+        case = per_token_case(91, Ns=6, K=16, Hk=2, Hv=4)
+    else:
+        case = synth.make_case("small", seed=92, K=4, Ns=6, Hk=1, Hv=8, num_slots=64,
+                               null_p=0.1, permute_tokens=True)
+    say(f"maximum size {shape}")
+    check_spec_case(case)
