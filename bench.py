@@ -54,7 +54,12 @@ def algorithmic_bytes(case) -> int:
         n = int(nacc[b])
         cs = int(sp["spec_cache_indices"][b]) if sp.get("spec_cache_indices") is not None \
             else int(ssi[b][0])
-        if cs > 0:
+        if d.get("conv_layout", 0) == 1:
+            # per-token slots: the window of slot ssi[n-1], a window per stored token
+            if ssi[b][n - 1] > 0:
+                total += (W - 1) * C * 2
+            total += sum((W - 1) * C * 2 for t in range(Tb) if ssi[b][t] > 0)
+        elif cs > 0:
             read_cols = set(range(n - 1, n - 1 + W - 1)) | set(range(n, n + max(L - Tb, 0)))
             total += (len(read_cols) + L) * C * 2               # ring read + rewrite
         if ssi[b][n - 1] > 0:
@@ -280,6 +285,14 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--qkv-layout", choices=("grouped", "per_k_head"), default="grouped",
+                    help="channel order of mixed_qkv (per_k_head: reorder_input=False; the "
+                         "same values repacked)")
+    ap.add_argument("--conv-layout", choices=("rolled", "per_token"), default="rolled",
+                    help="conv contract of spec rows (per_token: a window per token slot, "
+                         "state_len = conv_width - 1)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture each layer's step in a HIP graph and time graph replays")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB ten times "
                          "(the reference kernel for scaling the HBM byte counters)")
@@ -305,10 +318,22 @@ def main():
     import synth
     from tests.gpu_util import bf, f32, i32, u8
 
-    case = synth.make_case(args.workload, seed=args.seed)
+    over = {}
+    if args.conv_layout == "per_token":
+        over["L"] = synth.CONFIGS[args.workload]["W"] - 1
+    case = synth.make_case(args.workload, seed=args.seed, **over)
     d, sp, ns = case["dims"], case["spec"], case.get("nonspec")
+    if args.conv_layout == "per_token":
+        if ns is not None:
+            raise SystemExit("--conv-layout per_token applies to spec-only workloads")
+        d["conv_layout"] = 1
+    if args.qkv_layout == "per_k_head":
+        from tests.test_layout import per_k_head
+        case["mixed_qkv"] = per_k_head(case["mixed_qkv"], d["Hk"], d["Hv"], d["dk"], d["dv"])
     cfg = gdn.GdnConfig(d["Hk"], d["Hv"], d["dk"], d["dv"], d["W"], d["activation"],
-                        d["use_qk_l2norm"], d["eps"], d["scale"])
+                        d["use_qk_l2norm"], d["eps"], d["scale"],
+                        reorder_input=args.qkv_layout == "grouped",
+                        conv_layout=int(d.get("conv_layout", 0)))
     dev = torch.device("cuda:0")
     T_spec = sp["num_spec_tokens"]
     T_all = case["num_actual_tokens"]
@@ -359,6 +384,26 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    if args.graph:
+        # one graph per layer, captured on a side stream after the warm-up;
+        # a step is then one replay on the launch stream
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        for li in range(len(layers)):
+            g_ = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_, stream=side):
+                call_stream = torch.cuda.current_stream()
+                eager, stream = stream, call_stream
+                step(li)
+                stream = eager
+            graphs.append(g_)
+        torch.cuda.synchronize()
+        eager_step = step
+
+        def step(i):  # noqa: F811 (the timed step replays the layer's graph)
+            graphs[i % len(graphs)].replay()
+        del eager_step
     # Timed region: exactly `steps` layer steps, synchronised on both sides.
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -380,7 +425,8 @@ def main():
     avg_launch_s = ms_per_step * 1e-3
     nbytes = algorithmic_bytes(case) + (nonspec_bytes(case) if ns is not None else 0)
     achieved = nbytes / avg_launch_s / 1e9
-    traffic = profiled_traffic(args.workload) if ns is None else None
+    default_variant = (args.qkv_layout, args.conv_layout, args.graph) == ("grouped", "rolled", False)
+    traffic = profiled_traffic(args.workload) if ns is None and default_variant else None
     tokens = T_all if ns is not None else T_spec
 
     result = {
@@ -402,7 +448,9 @@ def main():
                    "tokens_per_step": tokens, "num_k_heads": d["Hk"], "num_v_heads": d["Hv"],
                    "head_k_dim": d["dk"], "head_v_dim": d["dv"], "conv_width": d["W"],
                    "state_len": d["L"], "num_slots": d["num_slots"],
-                   "layers_cycled": args.layers, "parallelism": "single GPU"},
+                   "layers_cycled": args.layers, "parallelism": "single GPU",
+                   "qkv_layout": args.qkv_layout, "conv_layout": args.conv_layout,
+                   "hip_graph": bool(args.graph)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "gdn_rows_kernel (dk=dv=128)",
