@@ -176,13 +176,17 @@ __device__ __forceinline__ void unpack4(u32x2 v, bool live, float (&x)[kCh]) {
 // slot 0's ring stands in without history, the taps for an empty ring or an
 // empty mixed_qkv (they hold C*W >= C values), row 0 for a token outside the
 // batch, the segment's last token for positions past it.
-template <int DK>
+// WT > 0 fixes the conv width and ACT >= 0 the activation at compile time
+// (the tap and window tests then fold away); WT = 0, ACT = -1 read them from
+// the arguments.
+template <int DK, int WT, int ACT>
 __global__ void __launch_bounds__(kThreads)
 conv_prefill_kernel(PrefillArgs p, float* __restrict__ y, float* __restrict__ ga,
                     float* __restrict__ gb) {
   constexpr int LPH = DK / kCh;  // lanes per head
   static_assert(LPH >= 4 && LPH <= 32, "head dim");
-  const int C = p.C, L = p.L, W = p.W;
+  const int C = p.C, L = p.L, W = WT > 0 ? WT : p.W;
+  const bool act = ACT >= 0 ? ACT != 0 : p.act != 0;
   const int c = (blockIdx.y * kThreads + threadIdx.x) * kCh;
   // Threads past the last channel stay for the lane-by-lane row gather
   // below (its values are read from lanes 0 .. 34 of every wave) and leave
@@ -335,7 +339,7 @@ conv_prefill_kernel(PrefillArgs p, float* __restrict__ y, float* __restrict__ ga
       for (int m = 0; m < kMaxWidth - 1; ++m)
         if (m < W - 1) acc = fmaf(w[m][e], win[m][e], acc);
       acc = fmaf(wl[e], xt[e], acc);
-      o[e] = p.act ? silu(acc) : acc;
+      o[e] = act ? silu(acc) : acc;
     }
     {
       float ss = o[0] * o[0];
@@ -352,7 +356,8 @@ conv_prefill_kernel(PrefillArgs p, float* __restrict__ y, float* __restrict__ ga
         const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ss), 48));
         ss = (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
       }
-      const float inv = p.l2norm ? 1.f / sqrtf(ss + p.eps) : 1.f;
+      // hardware reciprocal square root (within 1 ulp)
+      const float inv = p.l2norm ? __builtin_amdgcn_rsqf(ss + p.eps) : 1.f;
       const float f = c < p.Hk * DK ? inv * p.scale : (c < 2 * p.Hk * DK ? inv : 1.f);
 #pragma unroll
       for (int e = 0; e < kCh; ++e) o[e] *= f;
@@ -567,7 +572,9 @@ hipError_t launch_prefill_typed(const PrefillArgs& args, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g1(a.units, (a.C / kCh + kThreads - 1) / kThreads, kSeg / kTokThread);
-  hipLaunchKernelGGL(conv_prefill_kernel<DK>, g1, dim3(kThreads), 0, s, a, y, ga, gb);
+  // the usual layer (width 4, SiLU) takes the specialised kernel
+  auto conv = a.W == 4 && a.act ? conv_prefill_kernel<DK, 4, 1> : conv_prefill_kernel<DK, 0, -1>;
+  hipLaunchKernelGGL(conv, g1, dim3(kThreads), 0, s, a, y, ga, gb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (DK < 64) {
