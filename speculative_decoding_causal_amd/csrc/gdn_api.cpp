@@ -770,7 +770,9 @@ int gdn_attention_static(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
   if (int e = check_dims(dims)) return e;
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  if (num_prefills > 0 && num_non_spec_tokens > 0) {
+  // prefill rows always get the scratch (gdn_attention asks for a workspace
+  // whenever there are prefill rows, empty ones included)
+  if (num_prefills > 0) {
     const size_t need = gdn_workspace_bytes(dims, num_non_spec_tokens, num_prefills);
     if (need > (size_t)GDN_STATIC_SCRATCH_BYTES)
       return fail(GDN_ERR_WORKSPACE,

@@ -60,3 +60,25 @@ def test_static_scratch_matches_workspace_call_twice():
         np.testing.assert_array_equal(st.host_conv(), conv_ref)
         slots = synth.referenced_slots(case)
         assert_states_close(st.host_ssm(slots), ssm_ref[slots])
+
+
+def test_static_scratch_with_an_empty_prefill_row():
+    # a prefill row of no tokens (as a graph pad row is) beside a real one:
+    # the prefill kernels still get the static scratch
+    case = _mixed(64, (90, 0), 3, 2)
+    assert case["nonspec"]["num_prefills"] == 2
+    ref = Gpu(case)
+    ref.attention()
+    st = Gpu(case)
+    say("gdn_attention_static: prefills (90, 0), 3 decodes, 2 spec rows")
+    _call_static(st)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(st.host_out(), ref.host_out())
+    np.testing.assert_array_equal(st.host_conv(), ref.host_conv())
+    np.testing.assert_array_equal(st.host_ssm(), ref.host_ssm())
+    out_ref, conv_ref, ssm_ref = helpers.run_case(case, out=np.full(
+        helpers.out_shape(case), 0x5A5A, np.uint16))
+    assert_out_close(st.host_out(), out_ref)
+    np.testing.assert_array_equal(st.host_conv(), conv_ref)
+    slots = synth.referenced_slots(case)
+    assert_states_close(st.host_ssm(slots), ssm_ref[slots])
