@@ -188,6 +188,10 @@ conv_prefill_kernel(PrefillArgs p, float* __restrict__ y, float* __restrict__ ga
   const int C = p.C, L = p.L, W = WT > 0 ? WT : p.W;
   const bool act = ACT >= 0 ? ACT != 0 : p.act != 0;
   const int c = (blockIdx.y * kThreads + threadIdx.x) * kCh;
+  // the thread's four channels lie in one block: q (normalised, scaled), k
+  // (normalised) or v (as is)
+  const bool is_qk = c < 2 * p.Hk * DK;
+  const float qscale = c < p.Hk * DK ? p.scale : 1.f;
   // Threads past the last channel stay for the lane-by-lane row gather
   // below (its values are read from lanes 0 .. 34 of every wave) and leave
   // after it; until then they only form addresses, loading nothing.
@@ -349,16 +353,13 @@ conv_prefill_kernel(PrefillArgs p, float* __restrict__ y, float* __restrict__ ga
       ss = group_sum<(LPH < 16 ? LPH : 16)>(ss);
       if constexpr (LPH == 32) {
         // every lane of a 16-lane row now holds the row's sum; a head is two
-        // rows: combine them with scalar reads instead of an LDS permute
-        const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ss), 0));
-        const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ss), 16));
-        const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ss), 32));
-        const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ss), 48));
-        ss = (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
+        // rows: add the other row's sum (swizzle: lane xor 16 within each 32)
+        ss += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, ss),
+                                                                   0x401F));
       }
-      // hardware reciprocal square root (within 1 ulp)
-      const float inv = p.l2norm ? __builtin_amdgcn_rsqf(ss + p.eps) : 1.f;
-      const float f = c < p.Hk * DK ? inv * p.scale : (c < 2 * p.Hk * DK ? inv : 1.f);
+      // hardware reciprocal square root (within 1 ulp); q also takes the
+      // scale, with or without the norm
+      const float f = is_qk ? (p.l2norm ? __builtin_amdgcn_rsqf(ss + p.eps) : 1.f) * qscale : 1.f;
 #pragma unroll
       for (int e = 0; e < kCh; ++e) o[e] *= f;
     }
