@@ -657,7 +657,10 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
     // carry a NaN of padding rows into the state.
     tw.store_raw_split(Wl);
     tq.store_raw_split(Ql);
-    tk.store_raw_split(Kl, nt);
+    if (nt < kC)  // only a row's last chunk has rows past its tokens
+      tk.store_raw_split(Kl, nt);
+    else
+      tk.store_raw_split(Kl);
     tp.store_raw_split(Pl);
     tu.template store_pitched<UP>(Ul);
     if (tid < kC) Gc[tid] = tg * kLog2e;  // G in log2 units
@@ -668,22 +671,28 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
       const int gr = p.tix ? tx[r] : pr.j0 + c * kC + min(t, nt - 1);
       orow[r] = (t < nt && gr >= 0 && gr < p.num_actual_tokens) ? gr : -1;
     }
-    // S0 split: lanes 2m and 2m+1 hold adjacent columns of a row; the even
-    // lane writes their hi pair, the odd lane their lo pair
+    // S0 split: lanes 2m and 2m+1 hold columns c and c+1 of rows 4 lk + r.
+    // They swap two values, then the even lane splits the column pairs of
+    // rows 0 and 1 of the four, the odd lane those of rows 2 and 3, and each
+    // writes the pairs' hi and lo words.
+    {
+      const bool odd = (li & 1) != 0;
 #pragma unroll
-    for (int q = 0; q < TPW; ++q)
+      for (int q = 0; q < TPW; ++q) {
+        const v4f s = St[q];
+        const float x0 = dpp_mov<0xB1>(odd ? s[0] : s[2]);  // quad_perm 1,0,3,2
+        const float x1 = dpp_mov<0xB1>(odd ? s[1] : s[3]);
+        const int col = 16 * (TPW * tt + q) + (li & ~1);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        uint16_t hs, ls;
-        split1(St[q][r], hs, ls);
-        const unsigned hv = hs, lv = ls;
-        const unsigned hp = (unsigned)__builtin_amdgcn_mov_dpp((int)hv, 0xB1, 0xF, 0xF, false);
-        const unsigned lp = (unsigned)__builtin_amdgcn_mov_dpp((int)lv, 0xB1, 0xF, 0xF, false);
-        const int row = 16 * jt + 4 * lk + r, col = 16 * (TPW * tt + q) + li;
-        const bool odd = (li & 1) != 0;
-        *reinterpret_cast<unsigned*>(Ss + s0_off<DK>(row, odd ? DK + col - 1 : col)) =
-            odd ? (lp | (lv << 16)) : (hv | (hp << 16));
+        for (int k = 0; k < 2; ++k) {
+          const float xk = k ? x1 : x0;
+          const Split2 w = split2(odd ? xk : s[k], odd ? s[k + 2] : xk);
+          const int row = 16 * jt + 4 * lk + k + (odd ? 2 : 0);
+          *reinterpret_cast<unsigned*>(Ss + s0_off<DK>(row, col)) = w.hi;
+          *reinterpret_cast<unsigned*>(Ss + s0_off<DK>(row, DK + col)) = w.lo;
+        }
       }
+    }
     lds_barrier();
 
     const float gC = Gc[kC - 1];
@@ -700,11 +709,19 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) acc = mfma3(frag_rows<DK>(Wl, 16 * tt + li, ks, lk), sb[ks], acc);
       const int t0 = 16 * tt + 4 * lk;
+      // every row of the U~ block is readable (padding rows included), so
+      // the reads are issued together and the tokens tested afterwards
+      float ul[4], gt[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ul[r] = Ul[(t0 + r) * UP + 16 * jt + li];
+        gt[r] = Gc[t0 + r];
+      }
       v4f u, f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        u[r] = t0 + r < nt ? Ul[(t0 + r) * UP + 16 * jt + li] - acc[r] : 0.f;
-        f[r] = __builtin_amdgcn_exp2f(gC - Gc[t0 + r]);
+        u[r] = t0 + r < nt ? ul[r] - acc[r] : 0.f;
+        f[r] = __builtin_amdgcn_exp2f(gC - gt[r]);
       }
       store_split4<kC>(UTs, 16 * jt + li, t0, u);
       store_split4<kC>(UFs, 16 * jt + li, t0, u * f);
@@ -717,18 +734,22 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
     // (b) outputs on (tt, jt): e^{G_t} (Q S0^T)[t] + (P U)[t]; P is zero
     //     right of the diagonal block, so tokens 32..63 matter from tt = 2 on
     {
+      float eg[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) eg[r] = __builtin_amdgcn_exp2f(Gc[16 * tt + 4 * lk + r]);
       v4f aq = {0.f, 0.f, 0.f, 0.f}, ap = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) aq = mfma3(frag_rows<DK>(Ql, 16 * tt + li, ks, lk), sb[ks], aq);
       ap = mfma3(frag_rows<kC>(Pl, 16 * tt + li, 0, lk), frag_rows<kC>(UTs, 16 * jt + li, 0, lk), ap);
       if (tt >= 2)
         ap = mfma3(frag_rows<kC>(Pl, 16 * tt + li, 1, lk), frag_rows<kC>(UTs, 16 * jt + li, 1, lk), ap);
+      // bf16 round to nearest even (the hardware conversion)
+      uint16_t* ob = p.out + ((size_t)h * DV + RB * blk + 16 * jt + li);
+      const unsigned ostride = (unsigned)(Hv * DV);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tt + 4 * lk + r;
-        if (orow[r] >= 0)
-          p.out[((size_t)orow[r] * Hv + h) * DV + RB * blk + 16 * jt + li] =
-              f2bf(fmaf(__builtin_amdgcn_exp2f(Gc[t]), aq[r], ap[r]));
+        const uint16_t v = __builtin_bit_cast(uint16_t, (__bf16)fmaf(eg[r], aq[r], ap[r]));
+        if (orow[r] >= 0) ob[(size_t)(unsigned)orow[r] * ostride] = v;
       }
     }
 
