@@ -636,22 +636,33 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   // address: the value is dropped), so that no load sits behind a branch
   // and the waits for earlier loads stay exact.
   const int* tix = p.tix ? p.tix : reinterpret_cast<const int*>(ws.G);
-  auto gather = [&](int c) {
+  // The gather comes in four parts, spread over the phases of the previous
+  // chunk (W during (a), Q and K during (b), the rest during (c)): the
+  // workgroup's 120 KiB pass through the CU's vector memory path at a fixed
+  // rate, and a wave whose loads back up there stalls in issue, so loads
+  // issued all at once would hold every wave for that long.
+  auto gather_w = [&](int c) {
+    const int jb = pr.j0 + c * kC;
+    tw.load(ws.W + ((size_t)jb * Hv + h) * DK, Hv * DK);
+  };
+  auto gather_q = [&](int c) { tq.load(y + (size_t)(pr.j0 + c * kC) * C + ih * DK, C); };
+  auto gather_k = [&](int c) { tk.load(y + (size_t)(pr.j0 + c * kC) * C + Hk * DK + ih * DK, C); };
+  auto gather_rest = [&](int c) {
     const int jb = pr.j0 + c * kC;
     const int nt = min(kC, pr.T - c * kC);
-    const float* yb = y + (size_t)jb * C;
-    tw.load(ws.W + ((size_t)jb * Hv + h) * DK, Hv * DK);
-    tq.load(yb + ih * DK, C);
-    tk.load(yb + Hk * DK + ih * DK, C);
     tp.load(ws.P + ((size_t)jb * Hv + h) * kC, Hv * kC);
     tu.load(ws.U + ((size_t)jb * Hv + h) * DV + RB * blk, Hv * DV);
     tg = ws.G[(size_t)(jb + min(lane, nt - 1)) * Hv + h];
 #pragma unroll
     for (int r = 0; r < 4; ++r) tx[r] = tix[jb + min(16 * tt + 4 * lk + r, nt - 1)];
   };
-  gather(0);
+  gather_w(0);
+  gather_q(0);
+  gather_k(0);
+  gather_rest(0);
   for (int c = 0; c < nch; ++c) {
     const int nt = min(kC, pr.T - c * kC);
+    const int cn = c + 1 < nch ? c + 1 : c;  // the last chunk gathers itself again
     // Rows past the chunk's tokens reach only dropped results (U and the
     // outputs are tested per token), except through K: 0 * x there would
     // carry a NaN of padding rows into the state.
@@ -707,7 +718,14 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
     {
       v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma3(frag_rows<DK>(Wl, 16 * tt + li, ks, lk), sb[ks], acc);
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks == KS / 2) {
+          __builtin_amdgcn_sched_barrier(0);
+          gather_w(cn);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        acc = mfma3(frag_rows<DK>(Wl, 16 * tt + li, ks, lk), sb[ks], acc);
+      }
       const int t0 = 16 * tt + 4 * lk;
       // every row of the U~ block is readable (padding rows included), so
       // the reads are issued together and the tokens tested afterwards
@@ -727,9 +745,6 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
       store_split4<kC>(UFs, 16 * jt + li, t0, u * f);
     }
     lds_barrier();
-    // The next chunk's operands load during (b) and (c); the last chunk
-    // gathers itself again, so no load sits behind a branch.
-    gather(c + 1 < nch ? c + 1 : c);
 
     // (b) outputs on (tt, jt): e^{G_t} (Q S0^T)[t] + (P U)[t]; P is zero
     //     right of the diagonal block, so tokens 32..63 matter from tt = 2 on
@@ -738,8 +753,18 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) eg[r] = __builtin_amdgcn_exp2f(Gc[16 * tt + 4 * lk + r]);
       v4f aq = {0.f, 0.f, 0.f, 0.f}, ap = {0.f, 0.f, 0.f, 0.f};
+      __builtin_amdgcn_sched_barrier(0);
+      gather_q(cn);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) aq = mfma3(frag_rows<DK>(Ql, 16 * tt + li, ks, lk), sb[ks], aq);
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks == KS / 2) {
+          __builtin_amdgcn_sched_barrier(0);
+          gather_k(cn);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        aq = mfma3(frag_rows<DK>(Ql, 16 * tt + li, ks, lk), sb[ks], aq);
+      }
       ap = mfma3(frag_rows<kC>(Pl, 16 * tt + li, 0, lk), frag_rows<kC>(UTs, 16 * jt + li, 0, lk), ap);
       if (tt >= 2)
         ap = mfma3(frag_rows<kC>(Pl, 16 * tt + li, 1, lk), frag_rows<kC>(UTs, 16 * jt + li, 1, lk), ap);
@@ -754,6 +779,9 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
     }
 
     // (c) S = e^{G_C} S0 + U^T diag(e^{G_C - G_t}) K on this wave's tiles
+    __builtin_amdgcn_sched_barrier(0);
+    gather_rest(cn);
+    __builtin_amdgcn_sched_barrier(0);
     {
       const Frag ua[2] = {frag_rows<kC>(UFs, 16 * jt + li, 0, lk), frag_rows<kC>(UFs, 16 * jt + li, 1, lk)};
       const float eC = __builtin_amdgcn_exp2f(gC);
