@@ -322,7 +322,8 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
   const int nt = min(kC, pr.T - t0);
   const int jb = pr.j0 + t0;
   const int ih = h / p.G, Hk = p.Hk, Hv = p.Hv, C = p.C;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in a scalar register
   const int li = lane & 15, lk = lane >> 4;
   float* Mw = reinterpret_cast<float*>(smb + Lay::mw) + wv * 16 * MP;
 
@@ -399,18 +400,42 @@ chunk_prep_kernel(PrefillArgs p, const float* __restrict__ y, const float* __res
       for (int k = 0; k < DK / 32; ++k)
         acc = mfma3(frag_rows<DK>(Asrc, 16 * ti + li, k, lk), frag_rows<DK>(Ks, 16 * tj + li, k, lk),
                     acc);
+      // G and beta of the tile's rows and column read together (no read
+      // waits behind a test); decay e^{G_t - G_s} for s < t, 1 otherwise
+      const int s = 16 * tj + li, t0 = 16 * ti + 4 * lk;
+      const float gs = Gs[s];
+      float gt[4], bt[4], v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * ti + 4 * lk + r, s = 16 * tj + li;
-        const float dec = __builtin_amdgcn_exp2f((Gs[t] - Gs[s < t ? s : t]) * kLog2e);
-        if (!qk)
-          As[as_off(t, s)] = s < t ? Bs[t] * dec * acc[r] : 0.f;
-        else if (t < nt) {
-          uint16_t hi, lo;
-          split1(s <= t ? dec * acc[r] : 0.f, hi, lo);
-          uint16_t* prow = reinterpret_cast<uint16_t*>(ws.P + ((size_t)(jb + t) * Hv + h) * kC);
-          prow[s] = hi;
-          prow[kC + s] = lo;
+        gt[r] = Gs[t0 + r];
+        bt[r] = Bs[t0 + r];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + r;
+        const float dec = __builtin_amdgcn_exp2f((s < t ? gt[r] - gs : 0.f) * kLog2e);
+        v[r] = qk ? (s <= t ? dec * acc[r] : 0.f) : (s < t ? bt[r] * dec * acc[r] : 0.f);
+      }
+      if (!qk) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) As[as_off(t0 + r, s)] = v[r];
+      } else {
+        // P split, written as words of two columns: lanes 2m and 2m+1 swap
+        // two values, then the even lane writes rows 0 and 1 of its four,
+        // the odd lane rows 2 and 3
+        const bool odd = (li & 1) != 0;
+        const float x0 = dpp_mov<0xB1>(odd ? v[0] : v[2]);
+        const float x1 = dpp_mov<0xB1>(odd ? v[1] : v[3]);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float xk = k ? x1 : x0;
+          const Split2 w = split2(odd ? xk : v[k], odd ? v[k + 2] : xk);
+          const int t = t0 + k + (odd ? 2 : 0);
+          if (t < nt) {
+            unsigned* prow = reinterpret_cast<unsigned*>(ws.P + ((size_t)(jb + t) * Hv + h) * kC);
+            prow[(s & ~1) >> 1] = w.hi;
+            prow[(kC + (s & ~1)) >> 1] = w.lo;
+          }
         }
       }
     }
@@ -610,7 +635,8 @@ chunk_state_kernel(PrefillArgs p, const float* __restrict__ y, ChunkWs ws) {
   const PRow pr = prow(p, row);
   if (pr.T <= 0) return;
   const int ih = h / p.G;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in a scalar register
   const int li = lane & 15, lk = lane >> 4;
   const int tt = wv & 3, jt = wv >> 2;
 
