@@ -291,6 +291,9 @@ def main():
     ap.add_argument("--conv-layout", choices=("rolled", "per_token"), default="rolled",
                     help="conv contract of spec rows (per_token: a window per token slot, "
                          "state_len = conv_width - 1)")
+    ap.add_argument("--no-turns", action="store_true",
+                    help="call without turn counters: one row-kernel workgroup per "
+                         "(row, k-head) on every batch")
     ap.add_argument("--graph", action="store_true",
                     help="capture each layer's step in a HIP graph and time graph replays")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -356,7 +359,9 @@ def main():
         layers.append(dict(qkv=qkv, a=bf(case["a"]), b=bf(case["b"]),
                            conv=conv0.clone(), ssm=ssm0.clone(),
                            out=torch.empty(T_all, d["Hv"], d["dv"],
-                                           dtype=torch.bfloat16, device=dev)))
+                                           dtype=torch.bfloat16, device=dev),
+                           turns=None if args.no_turns
+                           else gdn.conv_turns(cfg, d["num_slots"], dev)))
     del conv0, ssm0
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -368,7 +373,7 @@ def main():
                                    L["conv"], L["ssm"], meta["sqsl"], meta["ssi"], meta["nacc"],
                                    L["out"], spec_cache_indices=meta["cache"],
                                    spec_token_indx=meta["tix"], num_spec_tokens=T_spec,
-                                   stream=stream)
+                                   conv_turns=L["turns"], stream=stream)
         else:
             gdn.gdn_attention(cfg, L["qkv"], L["a"], L["b"], w, None, A_log, dt_bias,
                               L["conv"], L["ssm"], L["out"], num_decodes=ns["num_decodes"],
@@ -379,7 +384,7 @@ def main():
                               spec_query_start_loc=meta["sqsl"], spec_state_indices=meta["ssi"],
                               num_accepted_tokens=meta["nacc"], spec_cache_indices=meta["cache"],
                               spec_token_indx=meta["tix"], num_spec_tokens=T_spec,
-                              workspace=workspace, stream=stream)
+                              workspace=workspace, conv_turns=L["turns"], stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -450,7 +455,8 @@ def main():
                    "state_len": d["L"], "num_slots": d["num_slots"],
                    "layers_cycled": args.layers, "parallelism": "single GPU",
                    "qkv_layout": args.qkv_layout, "conv_layout": args.conv_layout,
-                   "hip_graph": bool(args.graph)},
+                   "hip_graph": bool(args.graph),
+                   "conv_turns": not args.no_turns},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "gdn_rows_kernel (dk=dv=128)",

@@ -172,6 +172,17 @@ typedef struct gdn_dims {
  *   num_accepted_tokens [num_spec_decodes]
  *   num_spec_tokens = spec_query_start_loc[num_spec_decodes] (host copy)
  *
+ * conv_turns: NULL, or a device array of gdn_conv_turns_count(dims) uint32
+ * counters, four per (conv slot, k-head), that the caller zeroes once and
+ * keeps (any pools with the same dims may share one array; calls on one
+ * array are ordered by the caller).  With it the step runs one workgroup
+ * per (row, v-head) rather than per (row, k-head) on large batches
+ * (dk = dv = 128, Hv > Hk): the G = Hv/Hk workgroups of a k-head each read
+ * the shared q/k conv channels, and the last of them to have read its
+ * window (told by a wrapping count, 0 .. G-1, per 64 channels) rolls them.
+ * Every call leaves every counter at 0, metadata that violates the
+ * preconditions included.  The results are the same bits either way.
+ *
  * num_spec_decodes == 0 is a no-op that returns GDN_OK.
  */
 int gdn_spec_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
@@ -186,7 +197,12 @@ int gdn_spec_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
                        const int32_t* spec_state_indices,
                        const int32_t* num_accepted_tokens,
                        const int32_t* spec_token_indx,
-                       gdn_bf16* core_attn_out, gdn_stream_t stream);
+                       gdn_bf16* core_attn_out, uint32_t* conv_turns,
+                       gdn_stream_t stream);
+
+/* Number of uint32 turn counters gdn_spec_attention / gdn_attention take
+ * in conv_turns: 4 * num_slots * num_k_heads (0 for invalid dims). */
+size_t gdn_conv_turns_count(const gdn_dims* dims);
 
 /*
  * gdn_attention - a whole layer step over a batch that may mix non-spec rows
@@ -205,6 +221,8 @@ int gdn_spec_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
  *
  * Spec rows: exactly as gdn_spec_attention.  spec_state_indices and
  * num_accepted_tokens must be given together or not at all (GDN_ERR_SPEC_PAIR).
+ * conv_turns (NULL or as for gdn_spec_attention) serves the spec rows and
+ * the decodes.
  *
  * Checks: num_non_spec_tokens + num_spec_tokens == num_actual_tokens
  * (GDN_ERR_CONSERVATION); when both streams are non-empty both token_indx
@@ -234,13 +252,14 @@ int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
                   const int32_t* spec_state_indices,
                   const int32_t* num_accepted_tokens,
                   const int32_t* spec_token_indx,
-                  gdn_bf16* core_attn_out, void* workspace,
+                  gdn_bf16* core_attn_out, uint32_t* conv_turns, void* workspace,
                   size_t workspace_bytes, gdn_stream_t stream);
 
 /*
  * gdn_attention_static - gdn_attention for callers that cannot allocate
  * device memory (code under graph capture, tight serving loops, harnesses
- * that forbid hipMalloc): the same arguments without the workspace.  Prefill
+ * that forbid hipMalloc): the same arguments without the workspace (the
+ * caller's conv_turns array, or NULL, is used as it is).  Prefill
  * rows take their scratch from a library-owned static device array of
  * GDN_STATIC_SCRATCH_BYTES per GPU (held by each GPU the library runs on
  * until the process ends); a batch whose prefill rows need more
@@ -269,7 +288,8 @@ int gdn_attention_static(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
                          const int32_t* spec_state_indices,
                          const int32_t* num_accepted_tokens,
                          const int32_t* spec_token_indx,
-                         gdn_bf16* core_attn_out, gdn_stream_t stream);
+                         gdn_bf16* core_attn_out, uint32_t* conv_turns,
+                         gdn_stream_t stream);
 
 /* Bytes of workspace gdn_attention needs for a batch whose non-spec stream
  * has at most max_non_spec_tokens tokens, of which max_prefill_rows rows are

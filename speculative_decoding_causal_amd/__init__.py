@@ -55,6 +55,7 @@ MAX_ROW_TOKENS = 16
 
 EXPORTED_SYMBOLS = (
     "gdn_spec_attention", "gdn_attention", "gdn_attention_static", "gdn_workspace_bytes",
+    "gdn_conv_turns_count",
     "gdn_conv_only", "gdn_delta_rule_only", "gdn_check_metadata_host",
     "gdn_status_string", "gdn_last_error",
 )
@@ -84,17 +85,20 @@ class GdnRows(ctypes.Structure):
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
-_lib.gdn_spec_attention.argtypes = [ctypes.POINTER(GdnDims)] + [_P] * 9 + [_I] * 4 + [_P] * 6 + [_P]
+_lib.gdn_spec_attention.argtypes = ([ctypes.POINTER(GdnDims)] + [_P] * 9 + [_I] * 4 + [_P] * 6 +
+                                    [_P, _P])
 _lib.gdn_spec_attention.restype = ctypes.c_int
 _lib.gdn_attention.argtypes = ([ctypes.POINTER(GdnDims)] + [_P] * 9 + [_I] * 4 + [_P] * 4 +
-                               [_I] * 3 + [_P] * 5 + [_P, _P, ctypes.c_size_t, _P])
+                               [_I] * 3 + [_P] * 5 + [_P, _P, _P, ctypes.c_size_t, _P])
 _lib.gdn_attention.restype = ctypes.c_int
 _lib.gdn_attention_static.argtypes = ([ctypes.POINTER(GdnDims)] + [_P] * 9 + [_I] * 4 + [_P] * 4 +
-                                      [_I] * 3 + [_P] * 5 + [_P, _P])
+                                      [_I] * 3 + [_P] * 5 + [_P, _P, _P])
 _lib.gdn_attention_static.restype = ctypes.c_int
 STATIC_SCRATCH_BYTES = 64 << 20   # GDN_STATIC_SCRATCH_BYTES
 _lib.gdn_workspace_bytes.argtypes = [ctypes.POINTER(GdnDims), _I, _I]
 _lib.gdn_workspace_bytes.restype = ctypes.c_size_t
+_lib.gdn_conv_turns_count.argtypes = [ctypes.POINTER(GdnDims)]
+_lib.gdn_conv_turns_count.restype = ctypes.c_size_t
 _lib.gdn_conv_only.argtypes = [ctypes.POINTER(GdnDims), _P, _P, _P, _P, _I,
                                ctypes.POINTER(GdnRows), _P, _P]
 _lib.gdn_conv_only.restype = ctypes.c_int
@@ -258,12 +262,13 @@ def gdn_spec_attention(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias,
                        num_accepted_tokens, core_attn_out,
                        spec_cache_indices=None, spec_token_indx=None,
                        num_spec_tokens: int | None = None, num_actual_tokens: int | None = None,
-                       stream=None) -> None:
+                       conv_turns=None, stream=None) -> None:
     """One spec-verify step (see ``include/gdn.h``); pools are updated in
     place and ``core_attn_out`` [num_actual_tokens, Hv, dv] is written at the
     rows named by ``spec_token_indx``.  ``num_actual_tokens`` defaults to the
     rows of ``mixed_qkv``; pass ``num_spec_tokens`` too when capturing the
-    call in a graph (it is read back from the device otherwise)."""
+    call in a graph (it is read back from the device otherwise).
+    ``conv_turns``: None, or the pool's turn counters from ``conv_turns``."""
     dev = mixed_qkv.device
     _check_pools(cfg, conv_state, ssm_state)
     dims = cfg.dims(conv_state)
@@ -286,9 +291,29 @@ def gdn_spec_attention(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias,
         _ptr(spec_state_indices, _I32, "spec_state_indices", dev),
         _ptr(num_accepted_tokens, _I32, "num_accepted_tokens", dev),
         _ptr(spec_token_indx, _I32, "spec_token_indx", dev),
-        _ptr(core_attn_out, _BF16, "core_attn_out", dev), _stream(stream))
+        _ptr(core_attn_out, _BF16, "core_attn_out", dev),
+        _turns_ptr(cfg, conv_state, conv_turns, dev), _stream(stream))
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_spec_attention")
+
+
+def conv_turns(cfg: GdnConfig, num_slots: int, device=None):
+    """Zeroed turn counters for a conv pool of ``num_slots`` slots (four per
+    (slot, k-head)); keep them with the pool and pass them to every call on
+    it (see ``gdn_spec_attention`` in ``include/gdn.h``)."""
+    dims = cfg.dims(state_len=cfg.conv_width - 1, num_slots=num_slots)
+    n = int(_lib.gdn_conv_turns_count(ctypes.byref(dims)))
+    return torch.zeros(n, dtype=torch.int32, device=device)
+
+
+def _turns_ptr(cfg, conv_state, turns, dev):
+    if turns is None:
+        return None
+    n = 4 * int(conv_state.shape[0]) * cfg.num_k_heads
+    if turns.dtype != torch.int32 or turns.numel() != n:
+        raise ValueError(f"conv_turns must be int32 with {n} entries (4 * num_slots * "
+                         "num_k_heads)")
+    return _ptr(turns, torch.int32, "conv_turns", dev)
 
 
 def gdn_workspace_bytes(cfg: GdnConfig, state_len: int, num_slots: int,
@@ -306,15 +331,17 @@ def gdn_attention(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias, A_log
                   spec_query_start_loc=None, spec_state_indices=None,
                   num_accepted_tokens=None, spec_cache_indices=None,
                   spec_token_indx=None, num_spec_tokens=None, workspace=None,
-                  num_actual_tokens=None, stream=None) -> None:
+                  num_actual_tokens=None, conv_turns=None, stream=None) -> None:
     """A layer step over a batch of non-spec rows (decodes, then prefills)
     and spec rows.  ``workspace`` (uint8 device tensor) is needed when
-    ``num_prefills > 0``; size it with ``gdn_workspace_bytes``."""
+    ``num_prefills > 0``; size it with ``gdn_workspace_bytes``.
+    ``conv_turns``: None, or the pool's turn counters."""
     _attention(False, cfg, mixed_qkv, a, b, conv_weight, conv_bias, A_log, dt_bias, conv_state,
                ssm_state, core_attn_out, num_decodes, num_prefills, num_non_spec_tokens,
                query_start_loc, non_spec_state_indices, has_initial_state, non_spec_token_indx,
                spec_query_start_loc, spec_state_indices, num_accepted_tokens, spec_cache_indices,
-               spec_token_indx, num_spec_tokens, workspace, num_actual_tokens, stream)
+               spec_token_indx, num_spec_tokens, workspace, num_actual_tokens, conv_turns,
+               stream)
 
 
 def gdn_attention_static(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias, A_log,
@@ -325,7 +352,7 @@ def gdn_attention_static(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias
                          spec_query_start_loc=None, spec_state_indices=None,
                          num_accepted_tokens=None, spec_cache_indices=None,
                          spec_token_indx=None, num_spec_tokens=None,
-                         num_actual_tokens=None, stream=None) -> None:
+                         num_actual_tokens=None, conv_turns=None, stream=None) -> None:
     """``gdn_attention`` without a workspace: prefill rows use the library's
     static per-GPU scratch (STATIC_SCRATCH_BYTES); nothing is allocated.
     Calls that overlap on one GPU share that scratch and race."""
@@ -333,14 +360,14 @@ def gdn_attention_static(cfg: GdnConfig, mixed_qkv, a, b, conv_weight, conv_bias
                ssm_state, core_attn_out, num_decodes, num_prefills, num_non_spec_tokens,
                query_start_loc, non_spec_state_indices, has_initial_state, non_spec_token_indx,
                spec_query_start_loc, spec_state_indices, num_accepted_tokens, spec_cache_indices,
-               spec_token_indx, num_spec_tokens, None, num_actual_tokens, stream)
+               spec_token_indx, num_spec_tokens, None, num_actual_tokens, conv_turns, stream)
 
 
 def _attention(static, cfg, mixed_qkv, a, b, conv_weight, conv_bias, A_log, dt_bias, conv_state,
                ssm_state, core_attn_out, num_decodes, num_prefills, num_non_spec_tokens,
                query_start_loc, non_spec_state_indices, has_initial_state, non_spec_token_indx,
                spec_query_start_loc, spec_state_indices, num_accepted_tokens, spec_cache_indices,
-               spec_token_indx, num_spec_tokens, workspace, num_actual_tokens, stream):
+               spec_token_indx, num_spec_tokens, workspace, num_actual_tokens, turns, stream):
     dev = mixed_qkv.device
     _check_pools(cfg, conv_state, ssm_state)
     dims = cfg.dims(conv_state)
@@ -372,7 +399,8 @@ def _attention(static, cfg, mixed_qkv, a, b, conv_weight, conv_bias, A_log, dt_b
         _ptr(spec_state_indices, _I32, "spec_state_indices", dev),
         _ptr(num_accepted_tokens, _I32, "num_accepted_tokens", dev),
         _ptr(spec_token_indx, _I32, "spec_token_indx", dev),
-        _ptr(core_attn_out, _BF16, "core_attn_out", dev)]
+        _ptr(core_attn_out, _BF16, "core_attn_out", dev),
+        _turns_ptr(cfg, conv_state, turns, dev)]
     if static:
         rc = _lib.gdn_attention_static(*args, _stream(stream))
     else:

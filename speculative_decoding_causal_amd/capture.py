@@ -185,13 +185,17 @@ def rerun(path: str, device: str = "cuda:0"):
     inputs = {k: _dev(A.get(k), device, bf16=A.get(k) is not None and A[k].dtype == np.int16)
               for k in _INPUTS}
     sc = {k: v for k, v in rec["scalars"].items() if v is not None}
+    # fresh turn counters for the compact pools (the results are the same
+    # bits with or without them)
+    turns = gdn.conv_turns(cfg, n, device)
     if rec["call"] == "gdn_spec_attention":
         gdn.gdn_spec_attention(cfg, inputs["mixed_qkv"], inputs["a"], inputs["b"],
                                inputs["conv_weight"], inputs["conv_bias"], inputs["A_log"],
                                inputs["dt_bias"], conv, ssm, kw["spec_query_start_loc"],
                                kw["spec_state_indices"], kw["num_accepted_tokens"], out,
                                spec_cache_indices=kw.get("spec_cache_indices"),
-                               spec_token_indx=kw.get("spec_token_indx"), **sc)
+                               spec_token_indx=kw.get("spec_token_indx"), conv_turns=turns,
+                               **sc)
     else:
         ws = None
         if sc.get("num_prefills", 0) > 0:
@@ -200,7 +204,8 @@ def rerun(path: str, device: str = "cuda:0"):
             ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         gdn.gdn_attention(cfg, inputs["mixed_qkv"], inputs["a"], inputs["b"],
                           inputs["conv_weight"], inputs["conv_bias"], inputs["A_log"],
-                          inputs["dt_bias"], conv, ssm, out, workspace=ws, **kw, **sc)
+                          inputs["dt_bias"], conv, ssm, out, workspace=ws, conv_turns=turns,
+                          **kw, **sc)
     torch.cuda.synchronize()
     got_out = out.view(torch.int16).cpu().numpy()
     got_conv = conv.view(torch.int16)[1:].cpu().numpy()

@@ -217,6 +217,7 @@ struct Layer {
   float* ssm_state;
   gdn_bf16* out;
   int num_actual_tokens;
+  uint32_t* turns;
 };
 
 void fill_layer(gdn::RowArgs& r, const Layer& L) {
@@ -231,6 +232,7 @@ void fill_layer(gdn::RowArgs& r, const Layer& L) {
   r.conv_pool = L.conv_state;
   r.ssm_pool = L.ssm_state;
   r.out = L.out;
+  r.turns = reinterpret_cast<unsigned int*>(L.turns);
 }
 
 // Row-kernel arguments of the spec rows.  With `dec` (decode rows) the two
@@ -308,6 +310,12 @@ size_t gdn_workspace_bytes(const gdn_dims* dims, int32_t max_non_spec_tokens,
                                       max_non_spec_tokens, max_prefill_rows);
 }
 
+size_t gdn_conv_turns_count(const gdn_dims* dims) {
+  if (check_dims(dims) != GDN_OK) return 0;
+  // four per (conv slot, k-head): one per wave of the 2*dk q/k channels at dk = 128
+  return (size_t)dims->num_slots * (size_t)dims->num_k_heads * 4;
+}
+
 int gdn_spec_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
                        const gdn_bf16* a, const gdn_bf16* b,
                        const gdn_bf16* conv_weight, const gdn_bf16* conv_bias,
@@ -320,7 +328,7 @@ int gdn_spec_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
                        const int32_t* spec_state_indices,
                        const int32_t* num_accepted_tokens,
                        const int32_t* spec_token_indx,
-                       gdn_bf16* core_attn_out, gdn_stream_t stream) {
+                       gdn_bf16* core_attn_out, uint32_t* conv_turns, gdn_stream_t stream) {
   if (int e = check_dims(dims)) return e;
   if (num_actual_tokens < 0) return fail(GDN_ERR_DIMS, "num_actual_tokens < 0");
   SpecBatch s{num_spec_decodes, num_spec_tokens, max_spec_len, spec_query_start_loc,
@@ -333,7 +341,7 @@ int gdn_spec_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
                                ssm_state, core_attn_out))
     return e;
   Layer L{dims, mixed_qkv, a, b, conv_weight, conv_bias, A_log, dt_bias,
-          conv_state, ssm_state, core_attn_out, num_actual_tokens};
+          conv_state, ssm_state, core_attn_out, num_actual_tokens, conv_turns};
   return run_spec(L, s, static_cast<hipStream_t>(stream));
 }
 
@@ -356,7 +364,7 @@ int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
                   const int32_t* spec_state_indices,
                   const int32_t* num_accepted_tokens,
                   const int32_t* spec_token_indx,
-                  gdn_bf16* core_attn_out, void* workspace,
+                  gdn_bf16* core_attn_out, uint32_t* conv_turns, void* workspace,
                   size_t workspace_bytes, gdn_stream_t stream) {
   if (int e = check_dims(dims)) return e;
   if (num_actual_tokens < 0 || num_decodes < 0 || num_prefills < 0 || num_non_spec_tokens < 0)
@@ -400,7 +408,7 @@ int gdn_attention(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
                   units, kMaxPrefillUnits);
   }
   Layer L{dims, mixed_qkv, a, b, conv_weight, conv_bias, A_log, dt_bias,
-          conv_state, ssm_state, core_attn_out, num_actual_tokens};
+          conv_state, ssm_state, core_attn_out, num_actual_tokens, conv_turns};
   hipStream_t st = static_cast<hipStream_t>(stream);
   // Decode rows share the spec rows' launch when there are both (one grid,
   // decodes first).
@@ -766,7 +774,8 @@ int gdn_attention_static(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
                          const int32_t* spec_state_indices,
                          const int32_t* num_accepted_tokens,
                          const int32_t* spec_token_indx,
-                         gdn_bf16* core_attn_out, gdn_stream_t stream) {
+                         gdn_bf16* core_attn_out, uint32_t* conv_turns,
+                         gdn_stream_t stream) {
   if (int e = check_dims(dims)) return e;
   void* ws = nullptr;
   size_t ws_bytes = 0;
@@ -788,7 +797,7 @@ int gdn_attention_static(const gdn_dims* dims, const gdn_bf16* mixed_qkv,
                        has_initial_state, non_spec_token_indx, num_spec_decodes,
                        num_spec_tokens, max_spec_len, spec_query_start_loc, spec_cache_indices,
                        spec_state_indices, num_accepted_tokens, spec_token_indx, core_attn_out,
-                       ws, ws_bytes, stream);
+                       conv_turns, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -56,6 +56,11 @@ struct RowArgs {
   const uint8_t* his;
   const int* tix;
   int stage;
+  // Per (conv slot, k-head) turn counters (num_slots * Hk, 0 between
+  // calls), or null: with them the fused step runs one workgroup per
+  // (row, v-head) and the last of a k-head's G workgroups to read the
+  // shared q/k ring channels rolls them.
+  unsigned int* turns;
   // A second set of rows in the same launch (none when num_rows is 0): its
   // rows follow the first set's in the grid, with their own kind and metadata.
   struct RowSet {
@@ -76,7 +81,8 @@ __host__ __device__ inline int launch_row_tokens(const RowArgs& a) {
 }
 
 // Rows of at most kMaxRowTokens tokens (spec rows and decodes), one
-// workgroup per (row, k-head): conv + ring roll, gates, norms, recurrence.
+// workgroup per (row, k-head), or per (row, v-head) with turn counters:
+// conv + ring roll, gates, norms, recurrence.
 hipError_t launch_rows(const RowArgs& a, int dk, int dv, hipStream_t s);
 size_t rows_lds_bytes(const RowArgs& a, int dk, int dv);
 

@@ -7,6 +7,19 @@
 // "[GDN] Spec-decoding-aware attention kernel" ("Changes") holds inside one
 // workgroup, with the pre-state staged in LDS before the ring is rewritten.
 //
+// With turn counters (RowArgs::turns) the fused step runs one workgroup per
+// (row, v-head) instead: half the state per workgroup at G = 2, twice the
+// workgroups.  The G workgroups of a k-head each read and convolve the
+// shared q and k channels; each rolls its own v channels in place, and the
+// q/k channels are rolled by the last of the G to have consumed its window.
+// Each of the 2*dk/64 waves that hold q/k channels, once its loads of them
+// have returned, steps its counter of (conv slot, k-head, wave) with a
+// wrapping increment (0, 1, .., G-1, 0); the wave that finds G-1 is the
+// last reader of those 64 channels and rewrites them at its end.  Every
+// row steps a counter 0 or G times, so the counters are back at 0 after
+// every call (graph replays included), and no workgroup ever waits for
+// another.
+//
 // Phases:
 //   1. conv: stage the ring columns and the row's inputs (gathered through
 //      token_indx) in LDS, convolve, roll the ring (spec rows: window at
@@ -146,6 +159,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 #ifndef GDN_ROWS_RB128
 #define GDN_ROWS_RB128 4
 #endif
+// state rows per lane with (row, v-head) units: one pass over dv rows
+#ifndef GDN_ROWS_RV128
+#define GDN_ROWS_RV128 2
+#endif
 #ifndef GDN_NT_STORE
 #define GDN_NT_STORE 1
 #endif
@@ -214,17 +231,21 @@ __device__ __forceinline__ int pick(const int (&v)[KT], int j) {
   return r;
 }
 
-__device__ __forceinline__ int channel_of(int pc, int ih, int Hk, int DK, int NR) {
+// Channel of position pc of a unit: the q and k blocks of k-head ih, then
+// the v blocks of the unit's v-heads from hv0 on.
+__device__ __forceinline__ int channel_of(int pc, int ih, int hv0, int Hk, int DK, int DV) {
   if (pc < DK) return ih * DK + pc;
   if (pc < 2 * DK) return Hk * DK + ih * DK + (pc - DK);
-  return 2 * Hk * DK + ih * NR + (pc - 2 * DK);
+  return 2 * Hk * DK + hv0 * DV + (pc - 2 * DK);
 }
 
-// Column of mixed_qkv for channel position pc (grouped channel c) of k-head
-// ih: with the per-k-head layout the workgroup's channels are one block.
-__device__ __forceinline__ int input_column(const RowArgs& p, int pc, int c, int ih, int DK,
-                                            int NR) {
-  return p.qkv_layout ? ih * (2 * DK + NR) + pc : c;
+// Column of mixed_qkv for channel position pc (grouped channel c): with the
+// per-k-head layout k-head ih's channels are one block [q, k, v of its G
+// v-heads].
+__device__ __forceinline__ int input_column(const RowArgs& p, int pc, int c, int ih, int hv0,
+                                            int DK, int DV) {
+  const int bp = pc < 2 * DK ? pc : 2 * DK + (hv0 - ih * p.G) * DV + (pc - 2 * DK);
+  return p.qkv_layout ? ih * (2 * DK + p.G * DV) + bp : c;
 }
 
 template <int LM, int KT>
@@ -277,13 +298,35 @@ __device__ __forceinline__ void stage_chan(const ChanIn<LM, KT>& in, int L, int 
     if (j < T) zb[(L + j) * NCH + pc] = rj[j] >= 0 ? in.x[j] : (uint16_t)0;
 }
 
-// Convolve one staged channel and roll its ring; every ring write follows
-// every read of the pre-state (all of it is in LDS by now).
+// Roll one staged channel's ring (or write its per-token windows); every
+// ring write follows every read of the pre-state (all of it is in LDS).
+__device__ __forceinline__ void roll_chan(const RowArgs& p, const RowPlan& rp, int c, int pc,
+                                          int NCH, int T, const uint16_t* zb) {
+  const int L = p.L;
+  if (rp.save) {
+    // per-token slots: the window after token t is staged rows t+1 .. t+W-1
+    // (L == W-1 history rows, then the inputs), in token order
+    for (int t = 0; t < T; ++t) {
+      const int s = slot_or_null(rp.save[t], p.num_slots);
+      if (s <= 0) continue;
+      uint16_t* wslot = p.conv_pool + (size_t)s * L * p.C + c;
+      for (int l = 0; l < L; ++l) wslot[(size_t)l * p.C] = zb[(t + 1 + l) * NCH + pc];
+    }
+  } else if (rp.conv_slot > 0) {
+    uint16_t* wring = p.conv_pool + (size_t)rp.conv_slot * L * p.C + c;
+    for (int l = 0; l < L; ++l) {
+      const int src = l < L - T ? rp.shift + l : T + l;
+      wring[(size_t)l * p.C] = zb[src * NCH + pc];
+    }
+  }
+}
+
+// Convolve one staged channel and, with `roll`, roll its ring.
 template <int KT>
 __device__ __forceinline__ void conv_chan(const float (&w)[kMaxWidth], float bias,
                                           const RowArgs& p, const RowPlan& rp, int c, int pc,
                                           int NCH, int T, const uint16_t* zb, float* dst,
-                                          int dstride, const int (&rj)[KT]) {
+                                          int dstride, const int (&rj)[KT], bool roll) {
   const int L = p.L, W = p.W;
   for (int j = 0; j < T; ++j) {
     float acc = bias;
@@ -303,28 +346,14 @@ __device__ __forceinline__ void conv_chan(const float (&w)[kMaxWidth], float bia
       dst[j * dstride] = acc;
     }
   }
-  if (rp.save) {
-    // per-token slots: the window after token t is staged rows t+1 .. t+W-1
-    // (L == W-1 history rows, then the inputs), in token order
-    for (int t = 0; t < T; ++t) {
-      const int s = slot_or_null(rp.save[t], p.num_slots);
-      if (s <= 0) continue;
-      uint16_t* wslot = p.conv_pool + (size_t)s * L * p.C + c;
-      for (int l = 0; l < L; ++l) wslot[(size_t)l * p.C] = zb[(t + 1 + l) * NCH + pc];
-    }
-  } else if (rp.conv_slot > 0) {
-    uint16_t* wring = p.conv_pool + (size_t)rp.conv_slot * L * p.C + c;
-    for (int l = 0; l < L; ++l) {
-      const int src = l < L - T ? rp.shift + l : T + l;
-      wring[(size_t)l * p.C] = zb[src * NCH + pc];
-    }
-  }
+  if (roll) roll_chan(p, rp, c, pc, NCH, T, zb);
 }
 
 // NT threads per workgroup, R state rows per lane; WPE waves per SIMD is the
 // occupancy the register budget is fitted to.  LM / KT bound state_len and
 // the tokens per row for the register gathers of the conv phase.
-template <int DK, int DV, int R, int NT, int WPE, int LM, int KT, int RB, bool FUSED, int ORDER>
+template <int DK, int DV, int R, int NT, int WPE, int LM, int KT, int RB, bool FUSED, int ORDER,
+          bool VH>
 __global__ void __launch_bounds__(NT, WPE)
 gdn_rows_kernel(RowArgs pa) {
   static_assert(R % RB == 0, "row batch");
@@ -336,15 +365,21 @@ gdn_rows_kernel(RowArgs pa) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int Hk = pa.Hk, G = pa.G, C = pa.C, L = pa.L;
-  // Workgroup i runs on XCD i % 8: the k-heads of a row share i % 8, so
+  // The unit: k-head ih and its GU v-heads from hv0 on (all G of them, or
+  // one with turn counters).
+  const int GU = VH ? 1 : G;
+  const int NU = VH ? Hk * G : Hk;  // units per row
+  // Workgroup i runs on XCD i % 8: the units of a row share i % 8, so
   // each XCD's L2 fetches a row's metadata and gate rows once.  The grid is
   // padded to whole groups of 8 rows.
   const int q8 = blockIdx.x >> 3;
-  const int ih = q8 % Hk;
-  int row = (q8 / Hk) * 8 + (blockIdx.x & 7);
+  const int hu = q8 % NU;
+  const int ih = VH ? hu / G : hu;
+  const int hv0 = VH ? hu : hu * G;
+  int row = (q8 / NU) * 8 + (blockIdx.x & 7);
   if (row >= pa.num_rows + (pa.more.num_rows > 0 ? pa.more.num_rows : 0)) return;
-  const int NCH = 2 * DK + G * DV;
-  const int NR = G * DV;
+  const int NCH = 2 * DK + GU * DV;
+  const int NR = GU * DV;
   const int Tm = launch_row_tokens(pa);
   // rows of the second set take its kind and metadata (uniform selects)
   RowArgs p = pa;
@@ -367,7 +402,7 @@ gdn_rows_kernel(RowArgs pa) {
   const int T = rp.T;
   if (T <= 0) return;
 
-  const Lds lay = lds_layout(DK, DV, G, L, Tm);
+  const Lds lay = lds_layout(DK, DV, GU, L, Tm);
   int* rows_s = reinterpret_cast<int*>(smem + lay.rows);
   int* st_s = reinterpret_cast<int*>(smem + lay.stores);
   float* qs = reinterpret_cast<float*>(smem + lay.qs);
@@ -411,13 +446,13 @@ gdn_rows_kernel(RowArgs pa) {
   const int stage = FUSED ? kFused : p.stage;
   const bool conv_stage = stage != kDeltaOnly;
   const bool have_chan = conv_stage && tid < NCH;
-  const int c0 = channel_of(tid, ih, Hk, DK, NR);
+  const int c0 = channel_of(tid, ih, hv0, Hk, DK, DV);
   float w0[kMaxWidth], bias0 = 0.f;
   float a_log0, dt_bias0;
   // State rows of this lane (first pass), their slot and head block.
   const int jl = lane % LPR, gl = lane / LPR;
   const size_t slot_stride = (size_t)p.Hv * DV * DK;
-  const size_t head_off = (size_t)ih * NR * DK;
+  const size_t head_off = (size_t)hv0 * DV * DK;
   const bool load_valid = rp.load_slot > 0;
   const float* load_base = p.ssm_pool + (size_t)(load_valid ? rp.load_slot : 0) * slot_stride +
                            head_off;
@@ -431,17 +466,21 @@ gdn_rows_kernel(RowArgs pa) {
   const int wave_row0 = ORDER ? wv * RPW : wv * kRowsPerWavePass;
   constexpr bool kEarlyRows = LM + KT <= 10;
   v4f S[R][4];
+  // waves holding the q/k channels (one channel per thread, 64 per wave)
+  constexpr int kQKW = 2 * DK / 64;
+  static_assert(!VH || 2 * DK <= NT, "one q/k channel per thread");
+  unsigned int turn_old = 0;
   {
     // Gate inputs join the same batch (no branch around the loads): rows
     // outside the batch read row 0; with no token rows, or in the conv-only
     // stage (no gates), the loads go to A_log or the taps and are dropped.
-    const bool have_gate0 = stage != kConvOnly && tid < T * G;
+    const bool have_gate0 = stage != kConvOnly && tid < T * GU;
     const bool gate_rows = stage != kConvOnly && p.num_actual_tokens > 0;
     const uint16_t* gsrc_a = gate_rows ? p.a
         : (stage != kConvOnly ? reinterpret_cast<const uint16_t*>(p.A_log) : p.conv_w);
     const uint16_t* gsrc_b = gate_rows ? p.b : gsrc_a;
-    const int gr = have_gate0 ? pick<KT>(rj, tid / G) : -1;
-    const int gh = ih * G + tid % G;
+    const int gr = have_gate0 ? pick<KT>(rj, tid / GU) : -1;
+    const int gh = hv0 + tid % GU;
     const size_t gi = gate_rows ? (size_t)(gr >= 0 ? gr : 0) * p.Hv + gh : (size_t)gh;
     const uint16_t raw_a = gsrc_a[gi], raw_b = gsrc_b[gi];
     // the head's A_log and dt_bias too (the taps stand in for the conv-only
@@ -455,8 +494,8 @@ gdn_rows_kernel(RowArgs pa) {
     ChanIn<LM, KT> in0;
     if (conv_stage) {
       const int pcl = tid < NCH ? tid : NCH - 1;
-      const int cl = tid < NCH ? c0 : channel_of(pcl, ih, Hk, DK, NR);
-      load_chan<LM, KT>(in0, p, rp, cl, input_column(p, pcl, cl, ih, DK, NR), rj);
+      const int cl = tid < NCH ? c0 : channel_of(pcl, ih, hv0, Hk, DK, DV);
+      load_chan<LM, KT>(in0, p, rp, cl, input_column(p, pcl, cl, ih, hv0, DK, DV), rj);
     }
     // The first pass of state rows follows the conv and gate inputs in the
     // same stream of loads: it lands while the conv runs (vector loads
@@ -475,10 +514,34 @@ gdn_rows_kernel(RowArgs pa) {
       gb[tid] = gr >= 0 ? bf2f(raw_b) : 0.f;
     }
     if (have_chan) taps_of<LM, KT>(in0, p, w0, bias0);
+    // The turn of a q/k wave, once every conv load of the wave has
+    // returned: the counter's address carries an opaque zero computed from
+    // all of them (a wave's loads return together, lane by lane), so the
+    // step cannot be issued earlier.  Its result is first read at the end of
+    // phase 2, long after it arrives.  (A wrapping increment: an add of a
+    // uniform value would be rewritten into a wave-wide one that waits for
+    // its result at once.)
+    if constexpr (VH) {
+      if (wv < kQKW && rp.conv_slot > 0) {
+        int dep = in0.bias;
+#pragma unroll
+        for (int l = 0; l < LM; ++l) dep ^= in0.h[l];
+#pragma unroll
+        for (int j = 0; j < KT; ++j) dep ^= in0.x[j];
+#pragma unroll
+        for (int m = 0; m < kMaxWidth; ++m) dep ^= in0.w[m];
+        int zero;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(zero) : "v"(dep));
+        const size_t cell = ((size_t)rp.conv_slot * Hk + ih) * kQKW + wv;
+        if (lane == 0) turn_old = atomicInc(p.turns + cell + zero, (unsigned int)(G - 1));
+      }
+    }
   }
   // ---- phase 1: conv (or load of a precomputed conv output) -------------
   for (int pc = tid; pc < NCH; pc += NT) {
-    const int c = pc == tid ? c0 : channel_of(pc, ih, Hk, DK, NR);
+    const int c = pc == tid ? c0 : channel_of(pc, ih, hv0, Hk, DK, DV);
+    // with v-head units the shared q/k channels roll later, by one workgroup
+    const bool roll = !VH || pc >= 2 * DK;
     float* dst;
     int dstride;
     if (pc < DK) { dst = qs + pc; dstride = DK; }
@@ -492,14 +555,14 @@ gdn_rows_kernel(RowArgs pa) {
       continue;
     }
     if (pc == tid) {
-      conv_chan<KT>(w0, bias0, p, rp, c, pc, NCH, T, zb, dst, dstride, rj);
+      conv_chan<KT>(w0, bias0, p, rp, c, pc, NCH, T, zb, dst, dstride, rj, roll);
     } else {
       ChanIn<LM, KT> in;
-      load_chan<LM, KT>(in, p, rp, c, input_column(p, pc, c, ih, DK, NR), rj);
+      load_chan<LM, KT>(in, p, rp, c, input_column(p, pc, c, ih, hv0, DK, DV), rj);
       stage_chan<LM, KT>(in, L, T, pc, NCH, zb, rj);
       float w[kMaxWidth], bias;
       taps_of<LM, KT>(in, p, w, bias);
-      conv_chan<KT>(w, bias, p, rp, c, pc, NCH, T, zb, dst, dstride, rj);
+      conv_chan<KT>(w, bias, p, rp, c, pc, NCH, T, zb, dst, dstride, rj, roll);
     }
   }
   if (stage == kConvOnly) return;
@@ -509,9 +572,9 @@ gdn_rows_kernel(RowArgs pa) {
 
 
   // ---- phase 2: gates and q/k norms ---------------------------------------
-  if (tid < T * G) gate_pair(ga[tid], gb[tid], a_log0, dt_bias0, &ga[tid], &gb[tid]);
-  for (int idx = tid + NT; idx < T * G; idx += NT) {
-    const int j = idx / G, g = idx - j * G, h = ih * G + g;
+  if (tid < T * GU) gate_pair(ga[tid], gb[tid], a_log0, dt_bias0, &ga[tid], &gb[tid]);
+  for (int idx = tid + NT; idx < T * GU; idx += NT) {
+    const int j = idx / GU, g = idx - j * GU, h = hv0 + g;
     const int r = pick<KT>(rj, j);
     const float av = r >= 0 ? bf2f(p.a[(size_t)r * p.Hv + h]) : 0.f;
     const float bv = r >= 0 ? bf2f(p.b[(size_t)r * p.Hv + h]) : 0.f;
@@ -544,8 +607,17 @@ gdn_rows_kernel(RowArgs pa) {
     dot = wave_sum(dot);
     if (lane == 0) kq[j] = dot;
   }
+  // the last of the k-head's G waves to take its turn rolls the shared
+  // channels; without a ring slot nothing is read, and the wave of one
+  // fixed workgroup writes (per-token windows)
+  bool roll_qk = false;
+  if constexpr (VH) {
+    if (wv < kQKW)
+      roll_qk = rp.conv_slot > 0
+                    ? __builtin_amdgcn_readfirstlane(turn_old) == (unsigned int)(G - 1)
+                    : hv0 % G == G - 1;
+  }
   lds_barrier();
-
   // ---- phase 3: recurrence over the state rows -----------------------------
   // Rows are taken RB at a time through all the row's tokens, so the first
   // snapshots are stored as soon as those rows' loads have arrived.
@@ -584,9 +656,9 @@ gdn_rows_kernel(RowArgs pa) {
           // The wave's rows lie in one v-head: its gates are wave-uniform.
           const int g = r0 / DV;
           const float alw = __builtin_bit_cast(
-              float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ga[j * G + g])));
+              float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ga[j * GU + g])));
           const float bew = __builtin_bit_cast(
-              float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gb[j * G + g])));
+              float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gb[j * GU + g])));
 #pragma unroll
           for (int q = 0; q < RB; ++q) {
             const int rho = rho0 + (sb + q) * SS;
@@ -603,8 +675,8 @@ gdn_rows_kernel(RowArgs pa) {
             const int rho = rho0 + (sb + q) * SS;
             const int rr = rho < NR ? rho : NR - 1;
             const int g = rr / DV;
-            al[q] = ga[j * G + g];
-            const float be = gb[j * G + g];
+            al[q] = ga[j * GU + g];
+            const float be = gb[j * GU + g];
             const float vr = vs[j * NR + rr];
             u[q] = be * (vr - al[q] * pk[q]);
             const float o = fmaf(al[q], pq[q], u[q] * kqj);
@@ -641,32 +713,56 @@ gdn_rows_kernel(RowArgs pa) {
   }
   lds_barrier();
 
-  // ---- phase 4: outputs ----------------------------------------------------
+  // ---- phase 4: outputs (and the shared q/k roll of the last reader) ------
   uint16_t* out = p.out;
   for (int idx = tid; idx < T * NR; idx += NT) {
     int j = idx / NR, rr = idx - j * NR;
     int r = rows_s[j];
-    if (r >= 0) out[((size_t)r * p.Hv + ih * G) * DV + rr] = f2bf(ob[idx]);
+    if (r >= 0) out[((size_t)r * p.Hv + hv0) * DV + rr] = f2bf(ob[idx]);
+  }
+  if constexpr (VH) {
+    if (roll_qk) roll_chan(p, rp, channel_of(tid, ih, hv0, Hk, DK, DV), tid, NCH, T, zb);
   }
 }
 
 template <int DK, int DV, int R, int NT, int WPE, int LM, int KT>
 hipError_t launch_typed(const RowArgs& a, hipStream_t s) {
-  const Lds lay = lds_layout(DK, DV, a.G, a.L, launch_row_tokens(a));
   constexpr int RB = DK == 128 ? GDN_ROWS_RB128 : R;
   constexpr int ORDER = DK == 128 ? GDN_ROWS_ORDER128 : 0;
   const int rows = a.num_rows + (a.more.num_rows > 0 ? a.more.num_rows : 0);
-  // units: (row, k-head), rows padded to whole groups of 8
-  const unsigned units = static_cast<unsigned>((rows + 7) / 8 * 8) * static_cast<unsigned>(a.Hk);
+  const unsigned rows8 = static_cast<unsigned>((rows + 7) / 8 * 8);  // whole groups of 8
   int cus = 0;
   if (DK == 128) {
     hipError_t e = device_cu_count(&cus);
     if (e != hipSuccess) return e;
   }
+  // (row, v-head) units with turn counters, at one workgroup per CU, for
+  // rows of four tokens or more and more than three units per CU.
+  // Measured on MI355X (Qwen3-Next heads, one process, alternating): K=4,
+  // 256 rows 476 us against 509 us for (row, k-head) units; K=4, 96 rows
+  // 183 against 192 us; K=3 at 64, 128 and 256 rows 105/104, 200/201 and
+  // 400/398 us, where the (row, k-head) form stays.
+  if constexpr (DK == 128 && DV == 128) {
+    const unsigned vunits = rows8 * static_cast<unsigned>(a.Hv);
+    if (a.turns && a.G > 1 && a.stage == kFused && launch_row_tokens(a) >= 4 &&
+        vunits > 3u * static_cast<unsigned>(cus)) {
+      constexpr int RV = GDN_ROWS_RV128;
+      const Lds lay = lds_layout(DK, DV, 1, a.L, launch_row_tokens(a));
+      const int lds = lay.total < GDN_ROWS_LDS_MIN128 ? GDN_ROWS_LDS_MIN128 : lay.total;
+      auto kern = gdn_rows_kernel<DK, DV, RV, NT, WPE, LM, KT, RV, true, ORDER, true>;
+      hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3(vunits), dim3(NT), lds, s, a);
+      return hipGetLastError();
+    }
+  }
+  const Lds lay = lds_layout(DK, DV, a.G, a.L, launch_row_tokens(a));
+  // units: (row, k-head)
+  const unsigned units = rows8 * static_cast<unsigned>(a.Hk);
   const bool one_per_cu = DK == 128 && units > 3u * static_cast<unsigned>(cus);
   const int lds = one_per_cu && lay.total < GDN_ROWS_LDS_MIN128 ? GDN_ROWS_LDS_MIN128 : lay.total;
-  auto kern = a.stage == kFused ? gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT, RB, true, ORDER>
-                                : gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT, RB, false, ORDER>;
+  auto kern = a.stage == kFused ? gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT, RB, true, ORDER, false>
+                                : gdn_rows_kernel<DK, DV, R, NT, WPE, LM, KT, RB, false, ORDER, false>;
   if (lds > 64 * 1024) {
     hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lds);
     if (e != hipSuccess) return e;

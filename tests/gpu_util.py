@@ -69,9 +69,13 @@ def to_np_bf16(t):
 
 
 class Gpu:
-    """A case resident on the GPU."""
+    """A case resident on the GPU.  With ``turns`` (the default) the calls
+    pass the pool's turn counters, so batches large enough run the
+    (row, v-head) form of the row kernel; ``turns=False`` keeps the
+    (row, k-head) form everywhere."""
 
-    def __init__(self, case, out=None):
+    def __init__(self, case, out=None, turns=True):
+        import speculative_decoding_causal_amd as gdn
         self.case = case
         self.cfg = cfg_of(case)
         d = case["dims"]
@@ -88,6 +92,7 @@ class Gpu:
         if out is None:
             out = np.full((T, d["Hv"], d["dv"]), OUT_CANARY, np.uint16)
         self.out = bf(out)
+        self.turns = gdn.conv_turns(self.cfg, d["num_slots"], dev()) if turns else None
 
     def spec(self, spec=None, stream=None):
         import speculative_decoding_causal_amd as gdn
@@ -98,7 +103,7 @@ class Gpu:
             i32(sp["spec_state_indices"]), i32(sp["num_accepted_tokens"]), self.out,
             spec_cache_indices=i32(sp.get("spec_cache_indices")),
             spec_token_indx=i32(sp.get("spec_token_indx")),
-            num_spec_tokens=int(sp["num_spec_tokens"]), stream=stream)
+            num_spec_tokens=int(sp["num_spec_tokens"]), conv_turns=self.turns, stream=stream)
 
     def decode_row(self, r, slot, his=1):
         """One non-spec one-token decode of global row r on ``slot`` (tensors
@@ -109,7 +114,7 @@ class Gpu:
                           self.A_log, self.dt_bias, self.conv, self.ssm, self.out[sl],
                           num_decodes=1, num_non_spec_tokens=1,
                           query_start_loc=i32([0, 1]), non_spec_state_indices=i32([slot]),
-                          has_initial_state=u8([his]))
+                          has_initial_state=u8([his]), conv_turns=self.turns)
 
     def attention(self, ns="case", spec="case", workspace=None):
         import speculative_decoding_causal_amd as gdn
@@ -136,7 +141,8 @@ class Gpu:
                                              ns["num_non_spec_tokens"], ns["num_prefills"])
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev())
         gdn.gdn_attention(self.cfg, self.qkv, self.a, self.b, self.w, self.bias, self.A_log,
-                          self.dt_bias, self.conv, self.ssm, self.out, workspace=workspace, **kw)
+                          self.dt_bias, self.conv, self.ssm, self.out, workspace=workspace,
+                          conv_turns=self.turns, **kw)
 
     def host_out(self):
         return to_np_bf16(self.out)

@@ -60,14 +60,15 @@ def dims(**kw):
 def spec_call(d, Ns=4, T=12, K=3, sqsl=FAKE, ssi=FAKE, nacc=FAKE, qkv=FAKE, nat=12):
     return L.gdn_spec_attention(ctypes.byref(d), qkv, FAKE, FAKE, FAKE, None, FAKE, FAKE,
                                 FAKE, FAKE, nat, Ns, T, K, sqsl, None, ssi, nacc, None,
-                                FAKE, None)
+                                FAKE, None, None)
 
 
 def attn_call(d, nat=16, nd=2, npf=1, nns=6, qsl=FAKE, nsi=FAKE, ntix=FAKE, Ns=2, Ts=10,
               K=5, sqsl=FAKE, ssi=FAKE, nacc=FAKE, stix=FAKE, ws=None, ws_bytes=0):
     return L.gdn_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
                            FAKE, nat, nd, npf, nns, qsl, nsi, None, ntix, Ns, Ts, K, sqsl,
-                           None, ssi, nacc, stix, FAKE, ws, ctypes.c_size_t(ws_bytes), None)
+                           None, ssi, nacc, stix, FAKE, None, ws, ctypes.c_size_t(ws_bytes),
+                           None)
 
 
 def test_spec_pair_rejected():
@@ -164,14 +165,14 @@ def test_static_entry_point_rejects_batches_beyond_its_scratch():
     assert need > gdn.STATIC_SCRATCH_BYTES
     rc = L.gdn_attention_static(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
                                 FAKE, nns, 0, 1, nns, FAKE, FAKE, None, None, 0, 0, 1, None,
-                                None, None, None, None, FAKE, None)
+                                None, None, None, None, FAKE, None, None)
     assert rc == gdn.GDN_ERR_WORKSPACE, gdn.gdn_last_error()
     assert "static scratch holds 67108864" in gdn.gdn_last_error()
     # dimension errors come first, as in gdn_attention
     assert L.gdn_attention_static(ctypes.byref(dims(head_k_dim=96, head_v_dim=96)), FAKE, FAKE,
                                   FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, nns, 0, 1, nns, FAKE,
                                   FAKE, None, None, 0, 0, 1, None, None, None, None, None, FAKE,
-                                  None) == gdn.GDN_ERR_UNSUPPORTED
+                                  None, None) == gdn.GDN_ERR_UNSUPPORTED
 
 
 def test_status_strings():
@@ -482,7 +483,8 @@ def test_conv_pool_may_be_null_only_without_history():
     def call(d):
         return L.gdn_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None,
                                FAKE, 16, 2, 1, 6, FAKE, FAKE, None, FAKE, 2, 10, 5, FAKE,
-                               None, FAKE, FAKE, FAKE, FAKE, None, ctypes.c_size_t(0), None)
+                               None, FAKE, FAKE, FAKE, FAKE, None, None, ctypes.c_size_t(0),
+                               None)
     assert call(dims(conv_width=1, state_len=0)) == gdn.GDN_ERR_WORKSPACE
     assert call(dims()) == gdn.GDN_ERR_NULL
     assert "state pool" in gdn.gdn_last_error()

@@ -225,19 +225,23 @@ def _junk(rng, n, lo, hi):
     return np.array([pools[k][i] for i, k in enumerate(pick)], np.int32)
 
 
-@pytest.mark.parametrize("seed,decodes,prefill,dk,per_token",
-                         [(0, 0, 0, 128, 0), (1, 0, 0, 128, 0), (2, 0, 0, 128, 0),
-                          (3, 5, 0, 128, 0), (4, 5, 0, 128, 0), (5, 3, 150, 128, 0),
-                          (6, 3, 150, 32, 0), (7, 0, 300, 64, 0), (8, 0, 0, 128, 1),
-                          (9, 4, 0, 64, 1)])
-def test_garbage_metadata_stays_in_bounds(seed, decodes, prefill, dk, per_token):
+@pytest.mark.parametrize("seed,decodes,prefill,dk,per_token,Ns,K",
+                         [(0, 0, 0, 128, 0, 16, 3), (1, 0, 0, 128, 0, 16, 3),
+                          (2, 0, 0, 128, 0, 16, 3), (3, 5, 0, 128, 0, 16, 3),
+                          (4, 5, 0, 128, 0, 16, 3), (5, 3, 150, 128, 0, 16, 3),
+                          (6, 3, 150, 32, 0, 16, 3), (7, 0, 300, 64, 0, 16, 3),
+                          (8, 0, 0, 128, 1, 16, 3), (9, 4, 0, 64, 1, 16, 3),
+                          (10, 0, 0, 128, 0, 128, 4), (11, 6, 0, 128, 0, 128, 4),
+                          (12, 0, 0, 128, 1, 128, 4)])
+def test_garbage_metadata_stays_in_bounds(seed, decodes, prefill, dk, per_token, Ns, K):
     # Metadata values live in device memory and are not checked by the step
     # (the host checker is separate): the kernels clamp query_start_loc,
     # slots, num_accepted_tokens and token rows, so any values leave the
     # results unspecified but every access inside the tensors.  Checked with
-    # canaries around the pools and the output.
+    # canaries around the pools, the output and the turn counters; 128 rows
+    # of four tokens take the (row, v-head) form, where garbage slots put
+    # many rows on one counter, and every counter must still be back at 0.
     import speculative_decoding_causal_amd as gdn
-    K, Ns = 3, 16
     T = Ns * K
     nprefills = 3 if prefill else 0
     nns = decodes + prefill           # the prefill rows share `prefill` tokens
@@ -250,6 +254,7 @@ def test_garbage_metadata_stays_in_bounds(seed, decodes, prefill, dk, per_token)
     conv_buf, conv = _guarded(g.conv, 0.5)
     ssm_buf, ssm = _guarded(g.ssm, 0.5)
     out_buf, out = _guarded(g.out, 0.5)
+    turns_buf, turns = _guarded(g.turns, 0x5A5A5A5A)
     ws_buf = ws = None
     if nprefills:
         nbytes = gdn.gdn_workspace_bytes(g.cfg, d["L"], d["num_slots"], nns, nprefills)
@@ -266,7 +271,8 @@ def test_garbage_metadata_stays_in_bounds(seed, decodes, prefill, dk, per_token)
                                spec["spec_query_start_loc"], spec["spec_state_indices"],
                                spec["num_accepted_tokens"], out,
                                spec_cache_indices=spec["spec_cache_indices"],
-                               spec_token_indx=spec["spec_token_indx"], num_spec_tokens=T)
+                               spec_token_indx=spec["spec_token_indx"], num_spec_tokens=T,
+                               conv_turns=turns)
     else:
         rows = decodes + nprefills
         gdn.gdn_attention(g.cfg, g.qkv, g.a, g.b, g.w, None, g.A_log, g.dt_bias, conv, ssm, out,
@@ -275,10 +281,12 @@ def test_garbage_metadata_stays_in_bounds(seed, decodes, prefill, dk, per_token)
                           non_spec_state_indices=i32(_junk(rng, rows, 0, d["num_slots"])),
                           has_initial_state=u8(rng.integers(0, 2, rows)),
                           non_spec_token_indx=i32(_junk(rng, nns, 0, T + nns)),
-                          num_spec_tokens=T, workspace=ws, **spec)
+                          num_spec_tokens=T, workspace=ws, conv_turns=turns, **spec)
     torch.cuda.synchronize()
     if ws is not None:
         assert _guards_intact(ws_buf, ws.numel(), 0x5A)
+    assert _guards_intact(turns_buf, turns.numel(), 0x5A5A5A5A)
+    assert bool((turns == 0).all())
     assert _guards_intact(conv_buf, conv.numel(), 0.5)
     assert _guards_intact(ssm_buf, ssm.numel(), 0.5)
     assert _guards_intact(out_buf, out.numel(), 0.5)

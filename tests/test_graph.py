@@ -29,10 +29,11 @@ NS_PAD, ND_PAD = 8, 6
 NP_PAD, PF_TOK = 3, 200  # prefill rows (the last one pads) and their token budget
 
 
-def scenario(seed, ns, nd, pf=None):
-    """Padded metadata for ns real spec rows, nd real decodes and (with pf,
-    a list of at most NP_PAD - 1 lengths) real prefill rows, and the
-    unpadded case with the same real rows."""
+def scenario(seed, ns, nd, pf=None, ns_pad=NS_PAD, num_slots=SLOTS, k=K):
+    """Padded metadata for ns real spec rows of k tokens (of ns_pad), nd real
+    decodes and (with pf, a list of at most NP_PAD - 1 lengths) real prefill
+    rows, and the unpadded case with the same real rows."""
+    NS_PAD, SLOTS, K = ns_pad, num_slots, k  # noqa: N806 (the pads of this scenario)
     rng = np.random.default_rng(seed)
     pf = None if pf is None else list(pf)
     npf, pf_real = (0, 0) if pf is None else (NP_PAD, sum(pf))
@@ -72,7 +73,7 @@ def scenario(seed, ns, nd, pf=None):
     dqsl = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     dtix = np.concatenate([dec_rows, dec_pad, pf_rows, pf_pad]).astype(np.int32)
     padded = dict(sqsl=sqsl, ssi=ssi, nacc=nacc, stix=stix, dqsl=dqsl, cache=cache, his=his,
-                  dtix=dtix, t=t_pad, npf=npf, pf_tok=pf_tok)
+                  dtix=dtix, t=t_pad, npf=npf, pf_tok=pf_tok, ns_pad=NS_PAD, k=K)
     real = dict(case)
     for k in ("mixed_qkv", "a", "b"):
         real[k] = case[k][:t_real]
@@ -97,6 +98,7 @@ class Static:
         self.meta = {k: (i32(v) if v.dtype == np.int32 else u8(v))
                      for k, v in padded.items() if isinstance(v, np.ndarray)}
         self.t, self.npf, self.pf_tok = padded["t"], padded["npf"], padded["pf_tok"]
+        self.ns_pad, self.k = padded["ns_pad"], padded["k"]
         self.with_decodes = with_decodes
         self.ws = None
         if self.npf:
@@ -122,15 +124,15 @@ class Static:
     def call(self):
         import speculative_decoding_causal_amd as gdn
         g, m = self.g, self.meta
+        ts = self.ns_pad * self.k
         spec = dict(spec_query_start_loc=m["sqsl"], spec_state_indices=m["ssi"],
                     num_accepted_tokens=m["nacc"], spec_token_indx=m["stix"],
-                    num_spec_tokens=NS_PAD * K)
+                    num_spec_tokens=ts)
         if not self.with_decodes:
-            gdn.gdn_spec_attention(self.cfg, g.qkv[:NS_PAD * K], g.a[:NS_PAD * K],
-                                   g.b[:NS_PAD * K], g.w, None, g.A_log, g.dt_bias, g.conv,
-                                   g.ssm, m["sqsl"], m["ssi"], m["nacc"], g.out,
-                                   spec_token_indx=m["stix"], num_spec_tokens=NS_PAD * K,
-                                   num_actual_tokens=NS_PAD * K)
+            gdn.gdn_spec_attention(self.cfg, g.qkv[:ts], g.a[:ts], g.b[:ts], g.w, None, g.A_log,
+                                   g.dt_bias, g.conv, g.ssm, m["sqsl"], m["ssi"], m["nacc"],
+                                   g.out, spec_token_indx=m["stix"], num_spec_tokens=ts,
+                                   num_actual_tokens=ts, conv_turns=g.turns)
         else:
             gdn.gdn_attention(self.cfg, g.qkv, g.a, g.b, g.w, None, g.A_log, g.dt_bias, g.conv,
                               g.ssm, g.out, num_decodes=ND_PAD, num_prefills=self.npf,
@@ -138,11 +140,11 @@ class Static:
                               query_start_loc=m["dqsl"],
                               non_spec_state_indices=m["cache"], has_initial_state=m["his"],
                               non_spec_token_indx=m["dtix"], num_actual_tokens=self.t,
-                              workspace=self.ws, **spec)
+                              workspace=self.ws, conv_turns=g.turns, **spec)
 
 
-def _run_graph(with_decodes, plan):
-    case0, pad0, _ = scenario(*plan[0])
+def _run_graph(with_decodes, plan, **pads):
+    case0, pad0, _ = scenario(*plan[0], **pads)
     st = Static(case0, pad0, with_decodes)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -155,11 +157,12 @@ def _run_graph(with_decodes, plan):
         st.call()
     for step in plan:
         seed, ns, nd = step[:3]
-        case, padded, real = scenario(*step)
+        case, padded, real = scenario(*step, **pads)
         st.load(case, padded)
         torch.cuda.synchronize()
         pf = f", prefills {step[3]}" if len(step) > 3 else ""
-        say(f"graph replay: {ns} spec rows, {nd} decodes{pf} (padded to {NS_PAD}, {ND_PAD})")
+        say(f"graph replay: {ns} spec rows, {nd} decodes{pf} "
+            f"(padded to {padded['ns_pad']}, {ND_PAD})")
         graph.replay()
         torch.cuda.synchronize()
         eager = Gpu(real)
@@ -188,6 +191,16 @@ def _run_graph(with_decodes, plan):
 def test_graph_padded_spec_replays():
     # spec-only graph: the padded step uses the first NS_PAD * K input rows
     _run_graph(False, [(300, 8, 0), (301, 5, 0), (302, 2, 0), (303, 8, 0), (304, 1, 0)])
+
+
+def test_graph_vhead_units_replays():
+    # padded to 104 spec rows of four tokens (plus the decodes) the captured
+    # step runs one workgroup per (row, v-head) with turn counters, replay
+    # after replay; the eager calls on the smaller real batches run the
+    # (row, k-head) form, so the two forms are compared bit for bit as well
+    # as with the oracle
+    _run_graph(True, [(350, 104, 6), (351, 40, 3), (352, 104, 0), (353, 0, 6), (354, 77, 5)],
+               ns_pad=104, num_slots=500, k=4)
 
 
 def test_graph_padded_decodes_and_spec_replays():

@@ -36,7 +36,8 @@ def _call_static(g):
         spec_query_start_loc=i32(sp["spec_query_start_loc"]),
         spec_state_indices=i32(sp["spec_state_indices"]),
         num_accepted_tokens=i32(sp["num_accepted_tokens"]),
-        spec_token_indx=i32(sp.get("spec_token_indx")), num_spec_tokens=sp["num_spec_tokens"])
+        spec_token_indx=i32(sp.get("spec_token_indx")), num_spec_tokens=sp["num_spec_tokens"],
+        conv_turns=g.turns)
 
 
 def test_static_scratch_matches_workspace_call_twice():
