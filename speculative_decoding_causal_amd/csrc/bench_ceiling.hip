@@ -11,18 +11,18 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 512;
-constexpr int kPer = 16;                           // float4 per thread
-constexpr int kBlockFloats = kThreads * kPer * 4;  // 128 KiB
+constexpr int kPer = 8;                            // float4 per thread
+constexpr int kBlockFloats = kThreads * kPer * 4;  // 64 KiB: one v-head
 
 __device__ __forceinline__ int clamp_i(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 __global__ void __launch_bounds__(kThreads)
-state_fanout(float* pool, int num_slots, int Hk, int Hv, int num_rows, int K, const int* qsl,
+state_fanout(float* pool, int num_slots, int Hv, int num_rows, int K, const int* qsl,
              const int* ssi, const int* nacc, size_t slot_floats) {
-  // workgroup i runs on XCD i % 8: the k-heads of a row share i % 8
+  // workgroup i runs on XCD i % 8: the v-heads of a row share i % 8
   const int q8 = blockIdx.x >> 3;
-  const int ih = q8 % Hk;
-  const int row = (q8 / Hk) * 8 + (blockIdx.x & 7);
+  const int ih = q8 % Hv;
+  const int row = (q8 / Hv) * 8 + (blockIdx.x & 7);
   if (row >= num_rows) return;
   const int tid = threadIdx.x;
   const int j0 = qsl[row];
@@ -61,11 +61,11 @@ extern "C" int gdn_bench_state_fanout(float* ssm_state, int32_t num_slots, int32
   if (!ssm_state || !qsl || !ssi || !nacc || num_k_heads <= 0 || num_v_heads % num_k_heads ||
       num_rows < 0 || max_spec_len < 1 || num_slots <= 0)
     return -1;
-  const long long block = (long long)(num_v_heads / num_k_heads) * head_v_dim * head_k_dim;
+  const long long block = (long long)head_v_dim * head_k_dim;
   if (block != kBlockFloats) return -1;
   if (num_rows == 0) return 0;
   const size_t slot_floats = (size_t)num_v_heads * head_v_dim * head_k_dim;
-  const unsigned grid = (unsigned)((num_rows + 7) / 8 * 8) * (unsigned)num_k_heads;
+  const unsigned grid = (unsigned)((num_rows + 7) / 8 * 8) * (unsigned)num_v_heads;
   // one workgroup per CU (LDS above half of the CU's 160 KiB): the fastest
   // occupancy for this pattern in measurements on MI355X
   constexpr int kLds = 80 * 1024 + 16;
@@ -73,7 +73,7 @@ extern "C" int gdn_bench_state_fanout(float* ssm_state, int32_t num_slots, int32
                           hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess)
     return -7;
   hipLaunchKernelGGL(state_fanout, dim3(grid), dim3(kThreads), kLds,
-                     static_cast<hipStream_t>(stream), ssm_state, num_slots, num_k_heads,
-                     num_v_heads, num_rows, max_spec_len, qsl, ssi, nacc, slot_floats);
+                     static_cast<hipStream_t>(stream), ssm_state, num_slots, num_v_heads,
+                     num_rows, max_spec_len, qsl, ssi, nacc, slot_floats);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }

@@ -737,15 +737,16 @@ hipError_t launch_typed(const RowArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   // (row, v-head) units with turn counters, at one workgroup per CU, for
-  // rows of four tokens or more and more than three units per CU.
+  // rows of four tokens or more and at least twelve units per CU.
   // Measured on MI355X (Qwen3-Next heads, one process, alternating): K=4,
   // 256 rows 476 us against 509 us for (row, k-head) units; K=4, 96 rows
-  // 183 against 192 us; K=3 at 64, 128 and 256 rows 105/104, 200/201 and
-  // 400/398 us, where the (row, k-head) form stays.
+  // 183 against 192 us; 32 spec rows of K=4 with 32 decodes (64 rows)
+  // 100.8 against 98.4 us; K=3 at 64, 128 and 256 rows 105/104, 200/201
+  // and 400/398 us: there the (row, k-head) form stays.
   if constexpr (DK == 128 && DV == 128) {
     const unsigned vunits = rows8 * static_cast<unsigned>(a.Hv);
     if (a.turns && a.G > 1 && a.stage == kFused && launch_row_tokens(a) >= 4 &&
-        vunits > 3u * static_cast<unsigned>(cus)) {
+        vunits >= 12u * static_cast<unsigned>(cus)) {
       constexpr int RV = GDN_ROWS_RV128;
       const Lds lay = lds_layout(DK, DV, 1, a.L, launch_row_tokens(a));
       const int lds = lay.total < GDN_ROWS_LDS_MIN128 ? GDN_ROWS_LDS_MIN128 : lay.total;

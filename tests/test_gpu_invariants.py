@@ -231,21 +231,23 @@ def _junk(rng, n, lo, hi):
                           (4, 5, 0, 128, 0, 16, 3), (5, 3, 150, 128, 0, 16, 3),
                           (6, 3, 150, 32, 0, 16, 3), (7, 0, 300, 64, 0, 16, 3),
                           (8, 0, 0, 128, 1, 16, 3), (9, 4, 0, 64, 1, 16, 3),
-                          (10, 0, 0, 128, 0, 128, 4), (11, 6, 0, 128, 0, 128, 4),
-                          (12, 0, 0, 128, 1, 128, 4)])
+                          (10, 0, 0, 128, 0, 96, 4), (11, 6, 0, 128, 0, 96, 4),
+                          (12, 0, 0, 128, 1, 96, 4)])
 def test_garbage_metadata_stays_in_bounds(seed, decodes, prefill, dk, per_token, Ns, K):
     # Metadata values live in device memory and are not checked by the step
     # (the host checker is separate): the kernels clamp query_start_loc,
     # slots, num_accepted_tokens and token rows, so any values leave the
     # results unspecified but every access inside the tensors.  Checked with
-    # canaries around the pools, the output and the turn counters; 128 rows
-    # of four tokens take the (row, v-head) form, where garbage slots put
-    # many rows on one counter, and every counter must still be back at 0.
+    # canaries around the pools, the output and the turn counters; 96 rows
+    # of four tokens and 32 v-heads take the (row, v-head) form, where
+    # garbage slots put many rows on one counter, and every counter must
+    # still be back at 0.
     import speculative_decoding_causal_amd as gdn
     T = Ns * K
     nprefills = 3 if prefill else 0
     nns = decodes + prefill           # the prefill rows share `prefill` tokens
-    case = helpers.small_case(seed=160 + seed, Hk=4, Hv=8, dk=dk, dv=dk, K=K, T=T + nns,
+    Hk, Hv = (16, 32) if Ns > 16 else (4, 8)
+    case = helpers.small_case(seed=160 + seed, Hk=Hk, Hv=Hv, dk=dk, dv=dk, K=K, T=T + nns,
                               num_slots=24, L=3 if per_token else None)
     d = case["dims"]
     d["conv_layout"] = per_token       # per-token conv slots: one window per slot

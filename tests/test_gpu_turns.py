@@ -1,7 +1,9 @@
 """The row kernel with turn counters: one workgroup per (row, v-head) for
-rows of four or more tokens, the last of a k-head's workgroups to read the
-shared q/k conv channels rolling them ("[GDN] Spec-decoding-aware attention
-kernel", "Changes": stage the pre-state, then roll).  Compared bit for bit
+rows of four or more tokens on batches of at least twelve such units per CU
+(96 rows of 32 v-heads on MI355X's 256 CUs), the last of a k-head's
+workgroups to read the shared q/k conv channels rolling them ("[GDN]
+Spec-decoding-aware attention kernel", "Changes": stage the pre-state, then
+roll).  Compared bit for bit
 with the (row, k-head) form (no counters), which holds one k-head's channels
 in one workgroup, and with the oracle; every counter is back at 0 after
 every call."""
@@ -35,7 +37,7 @@ def _zero_turns(g):
 
 
 def _k4(seed, Ns=96, G=2, **kw):
-    # Qwen3-Next-like heads, rows of up to four tokens: more than three
+    # Qwen3-Next-like heads, rows of up to four tokens, 96 rows: twelve
     # (row, v-head) units per CU, so the counters are used
     Hk = 32 // G
     return synth.make_case("qwen3next_k3_b64", seed=seed, K=4, Ns=Ns, Hk=Hk, Hv=32,
@@ -67,7 +69,7 @@ def test_vhead_units_ragged_rows():
 
 def test_vhead_units_four_vheads_per_khead():
     # G = 4: four workgroups share a k-head's q/k channels (counts 0..3)
-    case = _k4(420, Ns=64, G=4)
+    case = _k4(420, Ns=96, G=4)
     a = check_spec_case(case)
     _zero_turns(a)
     b = Gpu(case, turns=False)

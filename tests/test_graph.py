@@ -29,11 +29,12 @@ NS_PAD, ND_PAD = 8, 6
 NP_PAD, PF_TOK = 3, 200  # prefill rows (the last one pads) and their token budget
 
 
-def scenario(seed, ns, nd, pf=None, ns_pad=NS_PAD, num_slots=SLOTS, k=K):
+def scenario(seed, ns, nd, pf=None, ns_pad=NS_PAD, num_slots=SLOTS, k=K, heads=(Hk, Hv)):
     """Padded metadata for ns real spec rows of k tokens (of ns_pad), nd real
     decodes and (with pf, a list of at most NP_PAD - 1 lengths) real prefill
     rows, and the unpadded case with the same real rows."""
     NS_PAD, SLOTS, K = ns_pad, num_slots, k  # noqa: N806 (the pads of this scenario)
+    Hk, Hv = heads  # noqa: N806
     rng = np.random.default_rng(seed)
     pf = None if pf is None else list(pf)
     npf, pf_real = (0, 0) if pf is None else (NP_PAD, sum(pf))
@@ -194,13 +195,13 @@ def test_graph_padded_spec_replays():
 
 
 def test_graph_vhead_units_replays():
-    # padded to 104 spec rows of four tokens (plus the decodes) the captured
-    # step runs one workgroup per (row, v-head) with turn counters, replay
-    # after replay; the eager calls on the smaller real batches run the
-    # (row, k-head) form, so the two forms are compared bit for bit as well
-    # as with the oracle
+    # padded to 104 spec rows of four tokens and 32 v-heads (plus the
+    # decodes) the captured step runs one workgroup per (row, v-head) with
+    # turn counters, replay after replay; the eager calls on the smaller real
+    # batches run the (row, k-head) form, so the two forms are compared bit
+    # for bit as well as with the oracle
     _run_graph(True, [(350, 104, 6), (351, 40, 3), (352, 104, 0), (353, 0, 6), (354, 77, 5)],
-               ns_pad=104, num_slots=500, k=4)
+               ns_pad=104, num_slots=500, k=4, heads=(16, 32))
 
 
 def test_graph_padded_decodes_and_spec_replays():
