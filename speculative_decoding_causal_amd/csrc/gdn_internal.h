@@ -56,7 +56,7 @@ struct RowArgs {
   const uint8_t* his;
   const int* tix;
   int stage;
-  // Per (conv slot, k-head) turn counters (num_slots * Hk, 0 between
+  // Per (conv slot, k-head, q/k wave) turn counters (num_slots * Hk * 4, 0 between
   // calls), or null: with them the fused step runs one workgroup per
   // (row, v-head) and the last of a k-head's G workgroups to read the
   // shared q/k ring channels rolls them.
