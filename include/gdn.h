@@ -84,9 +84,10 @@ enum {
   GDN_ERR_HIP = -7,              /* a HIP launch failed */
   GDN_ERR_UNSUPPORTED = -8,      /* shape outside what the kernels support,
                                     launch sizes included: at most 2^22
-                                    (row, k-head) workgroups per row launch,
-                                    65535 64-token prefill units, 2^24
-                                    conv channels */
+                                    workgroups per row launch (rows x
+                                    k-heads, or rows x v-heads with
+                                    conv_turns), 65535 64-token prefill
+                                    units, 2^24 conv channels */
   GDN_ERR_METADATA = -9          /* gdn_check_metadata_host found a violation */
 };
 
@@ -176,8 +177,8 @@ typedef struct gdn_dims {
  * counters, four per (conv slot, k-head), that the caller zeroes once and
  * keeps (any pools with the same dims may share one array; calls on one
  * array are ordered by the caller).  With it the step runs one workgroup
- * per (row, v-head) rather than per (row, k-head) on large batches
- * (dk = dv = 128, Hv > Hk): the G = Hv/Hk workgroups of a k-head each read
+ * per (row, v-head) rather than per (row, k-head) (dk = dv = 128,
+ * Hv > Hk): the G = Hv/Hk workgroups of a k-head each read
  * the shared q/k conv channels, and the last of them to have read its
  * window (told by a wrapping count, 0 .. G-1, per 64 channels) rolls them.
  * Every call leaves every counter at 0, metadata that violates the

@@ -146,11 +146,12 @@ void fill_common(gdn::RowArgs& a, const gdn_dims* d, int num_actual_tokens) {
 }
 
 int rows_launch_ok(const gdn::RowArgs& a, const gdn_dims* d) {
-  const long long wgs =
-      ((long long)a.num_rows + (a.more.num_rows > 0 ? a.more.num_rows : 0)) * a.Hk;
+  // with turn counters the rows may run one workgroup per (row, v-head)
+  const long long wgs = ((long long)a.num_rows + (a.more.num_rows > 0 ? a.more.num_rows : 0)) *
+                        (a.turns ? a.Hv : a.Hk);
   if (wgs > kMaxRowWorkgroups)
-    return fail(GDN_ERR_UNSUPPORTED, "row launch of %lld workgroups (rows x k-heads) exceeds %lld",
-                wgs, kMaxRowWorkgroups);
+    return fail(GDN_ERR_UNSUPPORTED, "row launch of %lld workgroups (rows x %s) exceeds %lld", wgs,
+                a.turns ? "v-heads" : "k-heads", kMaxRowWorkgroups);
   size_t need = gdn::rows_lds_bytes(a, d->head_k_dim, d->head_v_dim);
   if (need > 160 * 1024)
     return fail(GDN_ERR_UNSUPPORTED, "row kernel needs %zu bytes of LDS (max 163840)", need);

@@ -10,8 +10,8 @@
 // With turn counters (RowArgs::turns) the fused step runs one workgroup per
 // (row, v-head) instead: half the state per workgroup at G = 2, twice the
 // workgroups.  The G workgroups of a k-head each read and convolve the
-// shared q and k channels; each rolls its own v channels in place, and the
-// q/k channels are rolled by the last of the G to have consumed its window.
+// shared q and k channels; each rolls its own v channels, and the q/k
+// channels are rolled by the last of the G to have consumed its window.
 // Each of the 2*dk/64 waves that hold q/k channels, once its loads of them
 // have returned, steps its counter of (conv slot, k-head, wave) with a
 // wrapping increment (0, 1, .., G-1, 0); the wave that finds G-1 is the
@@ -22,20 +22,23 @@
 //
 // Phases:
 //   1. conv: stage the ring columns and the row's inputs (gathered through
-//      token_indx) in LDS, convolve, roll the ring (spec rows: window at
-//      n_acc-1, shift n_acc; non-spec rows: ring tail, shift T);
+//      token_indx) in LDS and convolve (spec rows: window at n_acc-1;
+//      non-spec rows: ring tail);
 //   2. gates (read at the same global rows, per the gate-gather fix of
-//      "[Bugfix] Align Qwen GDN gates with speculative tokens"), q/k L2 norms
-//      with wave reductions;
+//      "[Bugfix] Align Qwen GDN gates with speculative tokens");
 //   3. the recurrence, streaming the G*dv state rows of the k-head's v-heads
 //      through VGPRs: each state row of dk floats is spread over dk/16 lanes
 //      (16 floats, four float4 each), so row dot products need dk/16-lane DPP
 //      sums and every global access moves full 128-byte lines (at dk = 128
 //      the waves' rows interleave, so one instruction of the workgroup
-//      covers 64 consecutive rows).  The state of
+//      covers 64 consecutive rows).  The q/k L2 norms and k.q come from the
+//      same lanes' sums over their 16 channels, so no phase of their own
+//      stands between the conv and the first state store.  The state of
 //      each token is stored to its slot (spec) or only the final one
 //      (non-spec).  The initial-state load precedes every store of the row.
-//   4. outputs remapped through token_indx, as bf16.
+//   4. outputs remapped through token_indx, as bf16; then the ring roll
+//      (spec rows: shift n_acc; non-spec rows: shift T), from the pre-state
+//      still staged in LDS, after the state stores it would otherwise delay.
 //
 // The per-token arithmetic is identical for spec and non-spec rows, so a
 // spec row whose history is fully accepted reproduces sequential decodes
@@ -111,7 +114,6 @@ struct Lds {
   int qs, ks;        // float [Tm * DK]
   int vs, ob;        // float [Tm * NR]
   int ga, gb;        // float [Tm * G]
-  int kq;            // float [Tm]
   int total;
 };
 
@@ -129,7 +131,6 @@ __host__ __device__ inline Lds lds_layout(int DK, int DV, int G, int L, int Tm) 
   l.ob = o;     o += align16(Tm * NR * 4);
   l.ga = o;     o += align16(Tm * G * 4);
   l.gb = o;     o += align16(Tm * G * 4);
-  l.kq = o;     o += align16(Tm * 4);
   l.zb = o;     o += align16((L + Tm) * NCH * 2);
   l.total = o;
   return l;
@@ -138,15 +139,15 @@ __host__ __device__ inline Lds lds_layout(int DK, int DV, int G, int L, int Tm) 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // For dk = 128: state rows per lane (R), threads per workgroup (T), the
-// waves per SIMD the registers are fitted to (WPE), rows taken through all
-// tokens at a time (RB), whether snapshots use non-temporal stores, the row
-// order (ORDER: 1 interleaves the waves, so each instruction of the
-// workgroup covers 64 consecutive state rows) and a floor on the dynamic LDS
-// (LDS_MIN: above half of the CU's 160 KiB, so one workgroup runs per CU);
-// all chosen by measurement on MI355X: with more than three (row, k-head)
-// units per CU, one interleaved workgroup per CU moves the state about 2%
-// faster than two banded ones; with fewer, two per CU finish in fewer rounds
-// (5% faster at two units per CU), so the floor applies only above three.
+// waves per SIMD the registers are fitted to (WPE; 2 leaves the 128 KiB
+// (row, k-head) unit room for its registers), rows taken through all tokens
+// at a time (RB), whether snapshots use non-temporal stores, the row order
+// (ORDER: 1 interleaves the waves, so each instruction of the workgroup
+// covers 64 consecutive state rows) and a floor on the dynamic LDS (LDS_MIN:
+// above half of the CU's 160 KiB, so one workgroup runs per CU); all chosen
+// by measurement on MI355X: with more than three (row, k-head) units per CU,
+// one interleaved workgroup per CU moves the state about 2% faster than two
+// banded ones.
 #ifndef GDN_ROWS_R128
 #define GDN_ROWS_R128 4
 #endif
@@ -154,14 +155,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 #define GDN_ROWS_T128 512
 #endif
 #ifndef GDN_ROWS_WPE128
-#define GDN_ROWS_WPE128 4
+#define GDN_ROWS_WPE128 2
 #endif
 #ifndef GDN_ROWS_RB128
 #define GDN_ROWS_RB128 4
-#endif
-// state rows per lane with (row, v-head) units: one pass over dv rows
-#ifndef GDN_ROWS_RV128
-#define GDN_ROWS_RV128 2
 #endif
 #ifndef GDN_NT_STORE
 #define GDN_NT_STORE 1
@@ -172,13 +169,38 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 #ifndef GDN_ROWS_LDS_MIN128
 #define GDN_ROWS_LDS_MIN128 (80 * 1024 + 16)
 #endif
-
-__device__ __forceinline__ void store_row4(float* p, v4f v) {
-#if GDN_NT_STORE
-  __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p));
-#else
-  *reinterpret_cast<v4f*>(p) = v;
+// (row, v-head) units: state rows per lane (one pass over dv rows), waves
+// per SIMD, when the one-per-CU floor applies (rows of at least
+// VH_FLOOR_TOKENS tokens on at least VH_FLOOR_UNITS units per CU; shorter
+// rows and smaller grids run faster with several workgroups per CU), and
+// whether launches that carry decodes and spec rows together take them
+// (VH_MIXED: the one-token decodes repeat the q/k conv per v-head for a
+// single state update, and such a launch measured faster per k-head).
+#ifndef GDN_ROWS_RV128
+#define GDN_ROWS_RV128 2
 #endif
+#ifndef GDN_ROWS_WPE_VH128
+#define GDN_ROWS_WPE_VH128 4
+#endif
+#ifndef GDN_ROWS_VH_FLOOR_TOKENS
+#define GDN_ROWS_VH_FLOOR_TOKENS 3
+#endif
+#ifndef GDN_ROWS_VH_FLOOR_UNITS
+#define GDN_ROWS_VH_FLOOR_UNITS 8
+#endif
+#ifndef GDN_ROWS_VH_MIXED
+#define GDN_ROWS_VH_MIXED 0
+#endif
+
+// State snapshots go through a buffer resource per (token slot, unit): the
+// slot's block is a scalar base and each lane's row a 32-bit offset, so no
+// 64-bit lane addresses stay live across the tokens.
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(float* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void store_row4(__amdgpu_buffer_rsrc_t rs, unsigned off, v4f v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rs, off, 0, GDN_NT_STORE ? 2 : 0);
 }
 
 // Load the R state rows of one lane group: rows rho0 + s*RPW, 16 columns
@@ -193,11 +215,11 @@ __device__ __forceinline__ void load_rows(v4f (&S)[R][4], const float* base, int
 #pragma unroll
   for (int s = 0; s < R; ++s) {
     const int rho = rho0 + s * SS;
-    const int rc = rho < NR ? rho : NR - 1;
+    const unsigned off = static_cast<unsigned>((rho < NR ? rho : NR - 1) * DK + jl * 4) * 4u;  // bytes
+    const float* row = reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + off);
 #pragma unroll
     for (int n = 0; n < 4; ++n)
-      S[s][n] = __builtin_nontemporal_load(
-          reinterpret_cast<const v4f*>(base + (size_t)rc * DK + (n * LPR + jl) * 4));
+      S[s][n] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(row + n * LPR * 4));
   }
 }
 
@@ -411,7 +433,6 @@ gdn_rows_kernel(RowArgs pa) {
   float* ob = reinterpret_cast<float*>(smem + lay.ob);
   float* ga = reinterpret_cast<float*>(smem + lay.ga);
   float* gb = reinterpret_cast<float*>(smem + lay.gb);
-  float* kq = reinterpret_cast<float*>(smem + lay.kq);
   uint16_t* zb = reinterpret_cast<uint16_t*>(smem + lay.zb);
 
   // Global rows of the row's tokens (uniform scalar loads) and, in LDS for
@@ -517,8 +538,8 @@ gdn_rows_kernel(RowArgs pa) {
     // The turn of a q/k wave, once every conv load of the wave has
     // returned: the counter's address carries an opaque zero computed from
     // all of them (a wave's loads return together, lane by lane), so the
-    // step cannot be issued earlier.  Its result is first read at the end of
-    // phase 2, long after it arrives.  (A wrapping increment: an add of a
+    // step cannot be issued earlier.  Its result is first read after the
+    // gates, with the state loads ahead of it.  (A wrapping increment: an add of a
     // uniform value would be rewritten into a wave-wide one that waits for
     // its result at once.)
     if constexpr (VH) {
@@ -540,8 +561,9 @@ gdn_rows_kernel(RowArgs pa) {
   // ---- phase 1: conv (or load of a precomputed conv output) -------------
   for (int pc = tid; pc < NCH; pc += NT) {
     const int c = pc == tid ? c0 : channel_of(pc, ih, hv0, Hk, DK, DV);
-    // with v-head units the shared q/k channels roll later, by one workgroup
-    const bool roll = !VH || pc >= 2 * DK;
+    // the fused step rolls its rings at its end, off the path to the first
+    // state store; the conv-only stage ends here
+    const bool roll = stage == kConvOnly;
     float* dst;
     int dstride;
     if (pc < DK) { dst = qs + pc; dstride = DK; }
@@ -571,7 +593,7 @@ gdn_rows_kernel(RowArgs pa) {
 
 
 
-  // ---- phase 2: gates and q/k norms ---------------------------------------
+  // ---- phase 2: gates -------------------------------------------------------
   if (tid < T * GU) gate_pair(ga[tid], gb[tid], a_log0, dt_bias0, &ga[tid], &gb[tid]);
   for (int idx = tid + NT; idx < T * GU; idx += NT) {
     const int j = idx / GU, g = idx - j * GU, h = hv0 + g;
@@ -582,31 +604,9 @@ gdn_rows_kernel(RowArgs pa) {
   }
   // The phases hand data over through LDS only: every global address a
   // thread writes (its ring channels, its state rows, an output) is read, if
-  // at all, by that same thread, so the barriers order LDS alone and wait
-  // neither for the state loads nor for the ring stores still in flight.
+  // at all, by that same thread, so the barrier orders LDS alone and waits
+  // neither for the state loads nor for stores still in flight.
   lds_barrier();
-  for (int j = wv; j < T; j += NT / 64) {
-    float sq = 0.f, sk = 0.f;
-    for (int c = lane; c < DK; c += 64) {
-      float q = qs[j * DK + c], k = ks[j * DK + c];
-      sq = fmaf(q, q, sq);
-      sk = fmaf(k, k, sk);
-    }
-    sq = wave_sum(sq);
-    sk = wave_sum(sk);
-    float iq = p.l2norm ? 1.f / sqrtf(sq + p.eps) : 1.f;
-    float ik = p.l2norm ? 1.f / sqrtf(sk + p.eps) : 1.f;
-    float dot = 0.f;
-    for (int c = lane; c < DK; c += 64) {
-      float q = qs[j * DK + c] * iq * p.scale;
-      float k = ks[j * DK + c] * ik;
-      qs[j * DK + c] = q;
-      ks[j * DK + c] = k;
-      dot = fmaf(k, q, dot);
-    }
-    dot = wave_sum(dot);
-    if (lane == 0) kq[j] = dot;
-  }
   // the last of the k-head's G waves to take its turn rolls the shared
   // channels; without a ring slot nothing is read, and the wave of one
   // fixed workgroup writes (per-token windows)
@@ -617,7 +617,6 @@ gdn_rows_kernel(RowArgs pa) {
                     ? __builtin_amdgcn_readfirstlane(turn_old) == (unsigned int)(G - 1)
                     : hv0 % G == G - 1;
   }
-  lds_barrier();
   // ---- phase 3: recurrence over the state rows -----------------------------
   // Rows are taken RB at a time through all the row's tokens, so the first
   // snapshots are stored as soon as those rows' loads have arrived.
@@ -629,13 +628,21 @@ gdn_rows_kernel(RowArgs pa) {
 #pragma unroll
     for (int sb = 0; sb < R; sb += RB) {
       for (int j = 0; j < T; ++j) {
+        // S k and S q against the raw conv outputs, and |q|^2, |k|^2 and
+        // k.q: each lane holds 16 channels, the LPR lanes of a row all DK,
+        // so every row group gets the token's norms from its own sums.
         float pk[RB], pq[RB];
 #pragma unroll
         for (int q = 0; q < RB; ++q) { pk[q] = 0.f; pq[q] = 0.f; }
+        float sq = 0.f, sk = 0.f, dkq = 0.f;
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
           const v4f kv = *reinterpret_cast<const v4f*>(ks + j * DK + (n * LPR + jl) * 4);
           const v4f qv = *reinterpret_cast<const v4f*>(qs + j * DK + (n * LPR + jl) * 4);
+          sq = fmaf(qv.x, qv.x, sq); sk = fmaf(kv.x, kv.x, sk); dkq = fmaf(kv.x, qv.x, dkq);
+          sq = fmaf(qv.y, qv.y, sq); sk = fmaf(kv.y, kv.y, sk); dkq = fmaf(kv.y, qv.y, dkq);
+          sq = fmaf(qv.z, qv.z, sq); sk = fmaf(kv.z, kv.z, sk); dkq = fmaf(kv.z, qv.z, dkq);
+          sq = fmaf(qv.w, qv.w, sq); sk = fmaf(kv.w, kv.w, sk); dkq = fmaf(kv.w, qv.w, dkq);
 #pragma unroll
           for (int q = 0; q < RB; ++q) {
             const v4f x = S[sb + q][n];
@@ -645,12 +652,18 @@ gdn_rows_kernel(RowArgs pa) {
             pk[q] = fmaf(x.w, kv.w, pk[q]); pq[q] = fmaf(x.w, qv.w, pq[q]);
           }
         }
+        sq = group_sum<LPR>(sq);
+        sk = group_sum<LPR>(sk);
+        dkq = group_sum<LPR>(dkq);
+        // k^ = k ik, q^ = q iq scale (l2-norm with eps inside the root)
+        const float ik = p.l2norm ? 1.f / sqrtf(sk + p.eps) : 1.f;
+        const float iqs = (p.l2norm ? 1.f / sqrtf(sq + p.eps) : 1.f) * p.scale;
 #pragma unroll
         for (int q = 0; q < RB; ++q) {
-          pk[q] = group_sum<LPR>(pk[q]);
-          pq[q] = group_sum<LPR>(pq[q]);
+          pk[q] = group_sum<LPR>(pk[q]) * ik;
+          pq[q] = group_sum<LPR>(pq[q]) * iqs;
         }
-        const float kqj = kq[j];
+        const float kqj = dkq * ik * iqs;
         float al[RB], u[RB];
         if constexpr (ORDER == 0 && DV % kRowsPerWavePass == 0) {
           // The wave's rows lie in one v-head: its gates are wave-uniform.
@@ -669,6 +682,24 @@ gdn_rows_kernel(RowArgs pa) {
             const float o = fmaf(alw, pq[q], u[q] * kqj);
             if (jl == 0 && rho < NR) ob[j * NR + rho] = o;
           }
+        } else if constexpr (ORDER == 1 && DV % SS == 0) {
+          // Interleaved rows: a lane's row offset within its sub-pass
+          // (wave_row0 + gl) stays below SS, so sub-row sb + q of every lane
+          // lies in the same v-head and its gates are wave-uniform.
+#pragma unroll
+          for (int q = 0; q < RB; ++q) {
+            const int rho = rho0 + (sb + q) * SS;
+            const int gq = (r0 - wave_row0 + (sb + q) * SS) / DV;
+            const int g = gq < GU ? gq : GU - 1;
+            al[q] = __builtin_bit_cast(
+                float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ga[j * GU + g])));
+            const float be = __builtin_bit_cast(
+                float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gb[j * GU + g])));
+            const float vr = vs[j * NR + (rho < NR ? rho : NR - 1)];
+            u[q] = be * (vr - al[q] * pk[q]);
+            const float o = fmaf(al[q], pq[q], u[q] * kqj);
+            if (jl == 0 && rho < NR) ob[j * NR + rho] = o;
+          }
         } else {
 #pragma unroll
           for (int q = 0; q < RB; ++q) {
@@ -683,6 +714,9 @@ gdn_rows_kernel(RowArgs pa) {
             if (jl == 0 && rho < NR) ob[j * NR + rho] = o;
           }
         }
+        // u k^ = (u ik) k
+#pragma unroll
+        for (int q = 0; q < RB; ++q) u[q] *= ik;
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
           const v4f kv = *reinterpret_cast<const v4f*>(ks + j * DK + (n * LPR + jl) * 4);
@@ -695,16 +729,19 @@ gdn_rows_kernel(RowArgs pa) {
             x.w = fmaf(u[q], kv.w, al[q] * x.w);
           }
         }
-        const int st = st_s[j];
+        // the token's store slot is the workgroup's: a scalar base address,
+        // 32-bit lane offsets
+        const int st = __builtin_amdgcn_readfirstlane(st_s[j]);
         if (st > 0) {
-          float* base = p.ssm_pool + (size_t)st * slot_stride + head_off;
+          const __amdgpu_buffer_rsrc_t rs =
+              block_rsrc(p.ssm_pool + (size_t)st * slot_stride + head_off, NR * DK * 4);
 #pragma unroll
           for (int q = 0; q < RB; ++q) {
             const int rho = rho0 + (sb + q) * SS;
             if (full || rho < NR) {
+              const unsigned off = static_cast<unsigned>(rho * DK + jl * 4) * 4u;  // bytes
 #pragma unroll
-              for (int n = 0; n < 4; ++n)
-                store_row4(base + (size_t)rho * DK + (n * LPR + jl) * 4, S[sb + q][n]);
+              for (int n = 0; n < 4; ++n) store_row4(rs, off + n * LPR * 16, S[sb + q][n]);
             }
           }
         }
@@ -713,15 +750,21 @@ gdn_rows_kernel(RowArgs pa) {
   }
   lds_barrier();
 
-  // ---- phase 4: outputs (and the shared q/k roll of the last reader) ------
+  // ---- phase 4: outputs, then the ring rolls -------------------------------
   uint16_t* out = p.out;
   for (int idx = tid; idx < T * NR; idx += NT) {
     int j = idx / NR, rr = idx - j * NR;
     int r = rows_s[j];
     if (r >= 0) out[((size_t)r * p.Hv + hv0) * DV + rr] = f2bf(ob[idx]);
   }
-  if constexpr (VH) {
-    if (roll_qk) roll_chan(p, rp, channel_of(tid, ih, hv0, Hk, DK, DV), tid, NCH, T, zb);
+  // Each thread rolls the channels it staged (their pre-state and inputs
+  // are still in its LDS column); with v-head units the shared q/k channels
+  // only in the wave that was their last reader.
+  if (conv_stage) {
+    for (int pc = tid; pc < NCH; pc += NT) {
+      if (VH && pc < 2 * DK && !roll_qk) continue;
+      roll_chan(p, rp, channel_of(pc, ih, hv0, Hk, DK, DV), pc, NCH, T, zb);
+    }
   }
 }
 
@@ -736,23 +779,27 @@ hipError_t launch_typed(const RowArgs& a, hipStream_t s) {
     hipError_t e = device_cu_count(&cus);
     if (e != hipSuccess) return e;
   }
-  // (row, v-head) units with turn counters, at one workgroup per CU, for
-  // rows of four tokens or more and at least twelve units per CU.
-  // Measured on MI355X (Qwen3-Next heads, one process, alternating): K=4,
-  // 256 rows 476 us against 509 us for (row, k-head) units; K=4, 96 rows
-  // 183 against 192 us; 32 spec rows of K=4 with 32 decodes (64 rows)
-  // 100.8 against 98.4 us; K=3 at 64, 128 and 256 rows 105/104, 200/201
-  // and 400/398 us: there the (row, k-head) form stays.
+  // (row, v-head) units whenever the caller passes turn counters (one row
+  // set per launch): one workgroup per CU for rows of three tokens or more
+  // on grids of at least eight units per CU, several per CU otherwise.
+  // Measured on MI355X (one process, alternating, Qwen3-Next heads; the
+  // (row, k-head) form in brackets): K=3, 64 rows 99.3-101.2 us (102.0);
+  // K=4, 96 rows 181 (185); K=4, 256 rows 470-476 (472); K=2, 64 rows 76.8
+  // (78.5 at one per CU); one token, 256 rows 177 (205).  At 32 rows of
+  // K=3 (four units per CU) both forms take 54 us.
   if constexpr (DK == 128 && DV == 128) {
     const unsigned vunits = rows8 * static_cast<unsigned>(a.Hv);
-    if (a.turns && a.G > 1 && a.stage == kFused && launch_row_tokens(a) >= 4 &&
-        vunits >= 12u * static_cast<unsigned>(cus)) {
+    if (a.turns && a.G > 1 && a.stage == kFused && (GDN_ROWS_VH_MIXED || a.more.num_rows == 0)) {
       constexpr int RV = GDN_ROWS_RV128;
       const Lds lay = lds_layout(DK, DV, 1, a.L, launch_row_tokens(a));
-      const int lds = lay.total < GDN_ROWS_LDS_MIN128 ? GDN_ROWS_LDS_MIN128 : lay.total;
-      auto kern = gdn_rows_kernel<DK, DV, RV, NT, WPE, LM, KT, RV, true, ORDER, true>;
-      hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lds);
-      if (e != hipSuccess) return e;
+      const bool floor = launch_row_tokens(a) >= GDN_ROWS_VH_FLOOR_TOKENS &&
+                         vunits >= GDN_ROWS_VH_FLOOR_UNITS * static_cast<unsigned>(cus);
+      const int lds = floor && lay.total < GDN_ROWS_LDS_MIN128 ? GDN_ROWS_LDS_MIN128 : lay.total;
+      auto kern = gdn_rows_kernel<DK, DV, RV, NT, GDN_ROWS_WPE_VH128, LM, KT, RV, true, ORDER, true>;
+      if (lds > 64 * 1024) {
+        hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lds);
+        if (e != hipSuccess) return e;
+      }
       hipLaunchKernelGGL(kern, dim3(vunits), dim3(NT), lds, s, a);
       return hipGetLastError();
     }

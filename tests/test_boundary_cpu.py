@@ -57,10 +57,10 @@ def dims(**kw):
     return gdn.GdnDims(*[d[f] for f, _ in gdn.GdnDims._fields_])
 
 
-def spec_call(d, Ns=4, T=12, K=3, sqsl=FAKE, ssi=FAKE, nacc=FAKE, qkv=FAKE, nat=12):
+def spec_call(d, Ns=4, T=12, K=3, sqsl=FAKE, ssi=FAKE, nacc=FAKE, qkv=FAKE, nat=12, turns=None):
     return L.gdn_spec_attention(ctypes.byref(d), qkv, FAKE, FAKE, FAKE, None, FAKE, FAKE,
                                 FAKE, FAKE, nat, Ns, T, K, sqsl, None, ssi, nacc, None,
-                                FAKE, None, None)
+                                FAKE, turns, None)
 
 
 def attn_call(d, nat=16, nd=2, npf=1, nns=6, qsl=FAKE, nsi=FAKE, ntix=FAKE, Ns=2, Ts=10,
@@ -135,6 +135,11 @@ def test_launch_sizes_checked_before_any_launch():
     ns = (1 << 22) // 16 + 1        # rows x 16 k-heads just past 2^22 workgroups
     assert spec_call(dims(), Ns=ns, T=ns, K=1, nat=ns) == gdn.GDN_ERR_UNSUPPORTED
     assert "workgroups" in gdn.gdn_last_error()
+    # with turn counters the rows run one workgroup per (row, v-head): 32
+    # v-heads count, not 16 k-heads
+    ns = (1 << 22) // 32 + 1
+    assert spec_call(dims(), Ns=ns, T=ns, K=1, nat=ns, turns=FAKE) == gdn.GDN_ERR_UNSUPPORTED
+    assert "v-heads" in gdn.gdn_last_error()
     d = dims()
     nns = 1 << 22                   # 65536 units of 64 tokens, one prefill row
     need = L.gdn_workspace_bytes(ctypes.byref(d), nns, 1)

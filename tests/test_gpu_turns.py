@@ -1,12 +1,12 @@
 """The row kernel with turn counters: one workgroup per (row, v-head) for
-rows of four or more tokens on batches of at least twelve such units per CU
-(96 rows of 32 v-heads on MI355X's 256 CUs), the last of a k-head's
+launches of one row set (spec rows, or decodes), the last of a k-head's
 workgroups to read the shared q/k conv channels rolling them ("[GDN]
 Spec-decoding-aware attention kernel", "Changes": stage the pre-state, then
-roll).  Compared bit for bit
-with the (row, k-head) form (no counters), which holds one k-head's channels
-in one workgroup, and with the oracle; every counter is back at 0 after
-every call."""
+roll), one workgroup per CU for rows of three tokens or more on at least
+eight units per CU (96 rows of 32 v-heads on MI355X's 256 CUs), several per
+CU otherwise.  Compared bit for bit with the (row, k-head) form (no
+counters), which holds one k-head's channels in one workgroup, and with the
+oracle; every counter is back at 0 after every call."""
 from __future__ import annotations
 
 import dataclasses
@@ -129,10 +129,12 @@ def test_vhead_units_chained_calls():
     assert_states_close(a.host_ssm(slots), ssm[slots])
 
 
-def test_vhead_units_with_decodes():
-    # decodes and spec rows in one row-kernel launch (rows of four tokens
-    # set the form for both)
-    case = synth.make_case("mixed", seed=460, Ns=64, K=4, Nd=32, prefill_lens=())
+@pytest.mark.parametrize("Ns", [64, 0])
+def test_vhead_units_with_decodes(Ns):
+    # decodes and spec rows in one row-kernel launch (per k-head with or
+    # without counters), and decodes alone (one token per row, per v-head
+    # with counters)
+    case = synth.make_case("mixed", seed=460, Ns=Ns, K=4, Nd=32, prefill_lens=())
     ref_out, ref_conv, ref_ssm = helpers.run_case(case)
     a, b = Gpu(case), Gpu(case, turns=False)
     say("decodes + spec rows with counters")
@@ -143,5 +145,7 @@ def test_vhead_units_with_decodes():
     named = synth.referenced_slots(case)
     np.testing.assert_array_equal(a.host_conv(named), ref_conv[named])
     assert_states_close(a.host_ssm(named), ref_ssm[named])
-    rows = np.concatenate([case["spec"]["spec_token_indx"], case["nonspec"]["token_indx"]])
+    rows = case["nonspec"]["token_indx"]
+    if Ns:
+        rows = np.concatenate([case["spec"]["spec_token_indx"], rows])
     assert_out_close(a.host_out(), ref_out, np.sort(rows))
