@@ -350,22 +350,50 @@ __device__ __forceinline__ void conv_chan(const float (&w)[kMaxWidth], float bia
                                           int NCH, int T, const uint16_t* zb, float* dst,
                                           int dstride, const int (&rj)[KT], bool roll) {
   const int L = p.L, W = p.W;
-  for (int j = 0; j < T; ++j) {
-    float acc = bias;
-#pragma unroll
-    for (int m = 0; m < kMaxWidth; ++m) {
-      if (m < W) {
-        const int idx = j + m;
-        const int zi = idx < W - 1 ? rp.off + idx : L + idx - (W - 1);
-        acc = fmaf(w[m], bf2f(zb[zi * NCH + pc]), acc);
-      }
-    }
+  auto emit = [&](int j, float acc) {
     if (p.act) acc = silu(acc);
     if (p.stage == kConvOnly) {
       const int r = pick<KT>(rj, j);
       if (r >= 0) p.y[(size_t)r * p.C + c] = acc;
     } else {
       dst[j * dstride] = acc;
+    }
+  };
+  // Window sample i = j + m of token j is staged row off + i among the
+  // pre-state columns, or input row i - (W-1) after them.
+  if constexpr (KT <= 8) {
+    // short rows: every token's samples read in one batch (a read per loop
+    // step would wait for each in turn); samples the taps never reach
+    // repeat the last staged row
+    constexpr int NS = KT + kMaxWidth - 1;
+    float z[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      int zi = i < W - 1 ? rp.off + i : L + i - (W - 1);
+      zi = zi < L + T ? zi : L + T - 1;
+      z[i] = bf2f(zb[zi * NCH + pc]);
+    }
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      if (j < T) {
+        float acc = bias;
+#pragma unroll
+        for (int m = 0; m < kMaxWidth; ++m) acc = m < W ? fmaf(w[m], z[j + m], acc) : acc;
+        emit(j, acc);
+      }
+    }
+  } else {
+    for (int j = 0; j < T; ++j) {
+      float acc = bias;
+#pragma unroll
+      for (int m = 0; m < kMaxWidth; ++m) {
+        if (m < W) {
+          const int idx = j + m;
+          const int zi = idx < W - 1 ? rp.off + idx : L + idx - (W - 1);
+          acc = fmaf(w[m], bf2f(zb[zi * NCH + pc]), acc);
+        }
+      }
+      emit(j, acc);
     }
   }
   if (roll) roll_chan(p, rp, c, pc, NCH, T, zb);
