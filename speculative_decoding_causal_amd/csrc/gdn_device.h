@@ -23,8 +23,7 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF,
-                                      0xF, false));
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over groups of LPR consecutive lanes (LPR in 1,2,4,8,16); every lane

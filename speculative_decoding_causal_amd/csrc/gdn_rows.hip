@@ -684,8 +684,8 @@ gdn_rows_kernel(RowArgs pa) {
         sk = group_sum<LPR>(sk);
         dkq = group_sum<LPR>(dkq);
         // k^ = k ik, q^ = q iq scale (l2-norm with eps inside the root)
-        const float ik = p.l2norm ? 1.f / sqrtf(sk + p.eps) : 1.f;
-        const float iqs = (p.l2norm ? 1.f / sqrtf(sq + p.eps) : 1.f) * p.scale;
+        const float ik = p.l2norm ? __builtin_amdgcn_rsqf(sk + p.eps) : 1.f;
+        const float iqs = (p.l2norm ? __builtin_amdgcn_rsqf(sq + p.eps) : 1.f) * p.scale;
 #pragma unroll
         for (int q = 0; q < RB; ++q) {
           pk[q] = group_sum<LPR>(pk[q]) * ik;
