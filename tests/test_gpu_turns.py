@@ -38,7 +38,7 @@ def _zero_turns(g):
 
 def _k4(seed, Ns=96, G=2, **kw):
     # Qwen3-Next-like heads, rows of up to four tokens, 96 rows: twelve
-    # (row, v-head) units per CU, so the counters are used
+    # (row, v-head) units per CU, one workgroup per CU
     Hk = 32 // G
     return synth.make_case("qwen3next_k3_b64", seed=seed, K=4, Ns=Ns, Hk=Hk, Hv=32,
                            num_slots=4 * Ns + 16, permute_tokens=True, **kw)
