@@ -57,9 +57,9 @@ struct RowArgs {
   const int* tix;
   int stage;
   // Per (conv slot, k-head, q/k wave) turn counters (num_slots * Hk * 4, 0 between
-  // calls), or null: with them the fused step runs one workgroup per
-  // (row, v-head) and the last of a k-head's G workgroups to read the
-  // shared q/k ring channels rolls them.
+  // calls), or null: with them the fused step of one row set (dk = dv = 128,
+  // G > 1) runs one workgroup per (row, v-head), and the last of a k-head's
+  // G workgroups to read the shared q/k ring channels rolls them.
   unsigned int* turns;
   // A second set of rows in the same launch (none when num_rows is 0): its
   // rows follow the first set's in the grid, with their own kind and metadata.
