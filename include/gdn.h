@@ -223,7 +223,8 @@ size_t gdn_conv_turns_count(const gdn_dims* dims);
  * Spec rows: exactly as gdn_spec_attention.  spec_state_indices and
  * num_accepted_tokens must be given together or not at all (GDN_ERR_SPEC_PAIR).
  * conv_turns (NULL or as for gdn_spec_attention) serves the spec rows and
- * the decodes.
+ * the decodes; a row launch that carries both (decodes and spec rows in one
+ * call) runs per k-head either way, the counters untouched.
  *
  * Checks: num_non_spec_tokens + num_spec_tokens == num_actual_tokens
  * (GDN_ERR_CONSERVATION); when both streams are non-empty both token_indx
