@@ -149,3 +149,34 @@ def test_vhead_units_with_decodes(Ns):
     if Ns:
         rows = np.concatenate([case["spec"]["spec_token_indx"], rows])
     assert_out_close(a.host_out(), ref_out, np.sort(rows))
+
+
+def test_vhead_units_decodes_null_slots_no_initial_state():
+    # A decode-only launch (one row set, so per v-head with counters) whose
+    # rows include NULL cache slots (no ring, no state read or store) and
+    # rows without an initial state (ring and state read as zeros, then
+    # written): against the (row, k-head) form bit for bit and the oracle.
+    nd = 96
+    case = helpers.small_case(seed=470, Hk=16, Hv=32, dk=128, dv=128, K=1, T=nd, L=3,
+                              num_slots=2 * nd + 8)
+    rng = np.random.default_rng(471)
+    slots = rng.choice(np.arange(1, case["dims"]["num_slots"]), nd, replace=False)
+    slots[rng.random(nd) < 0.15] = 0
+    his = (rng.random(nd) < 0.7).astype(np.uint8)
+    tix = rng.permutation(nd).astype(np.int32)
+    case["nonspec"] = helpers.nonspec_meta([1] * nd, slots, his=his, tix=tix, num_decodes=nd)
+    case["spec"] = None
+    case["name"] = "nonspec"
+    out_ref, conv_ref, ssm_ref, _ = helpers.run_nonspec(case)
+    a, b = Gpu(case), Gpu(case, turns=False)
+    say("decodes with NULL slots and no initial state, with and without counters")
+    a.attention()
+    b.attention()
+    _zero_turns(a)
+    _same(a, b)
+    assert_out_close(a.host_out(), out_ref)
+    named = np.unique(slots[slots > 0])
+    np.testing.assert_array_equal(a.host_conv(named), conv_ref[named])
+    assert_states_close(a.host_ssm(named), ssm_ref[named])
+    free = np.setdiff1d(np.arange(1, case["dims"]["num_slots"]), named)[:8]
+    np.testing.assert_array_equal(a.host_ssm(free), case["ssm_state"][free])
