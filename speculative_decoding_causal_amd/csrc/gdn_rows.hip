@@ -7,9 +7,9 @@
 // "[GDN] Spec-decoding-aware attention kernel" ("Changes") holds inside one
 // workgroup, with the pre-state staged in LDS before the ring is rewritten.
 //
-// With turn counters (RowArgs::turns) the fused step runs one workgroup per
-// (row, v-head) instead: half the state per workgroup at G = 2, twice the
-// workgroups.  The G workgroups of a k-head each read and convolve the
+// With turn counters (RowArgs::turns) the fused step of a launch with one
+// row set runs one workgroup per (row, v-head) instead (dk = dv = 128,
+// G > 1): half the state per workgroup at G = 2, twice the workgroups.  The G workgroups of a k-head each read and convolve the
 // shared q and k channels; each rolls its own v channels, and the q/k
 // channels are rolled by the last of the G to have consumed its window.
 // Each of the 2*dk/64 waves that hold q/k channels, once its loads of them
@@ -683,7 +683,8 @@ gdn_rows_kernel(RowArgs pa) {
         sq = group_sum<LPR>(sq);
         sk = group_sum<LPR>(sk);
         dkq = group_sum<LPR>(dkq);
-        // k^ = k ik, q^ = q iq scale (l2-norm with eps inside the root)
+        // k^ = k ik, q^ = q iq scale: l2 norms with eps inside the root, by the
+        // hardware reciprocal square root (within 1 ulp)
         const float ik = p.l2norm ? __builtin_amdgcn_rsqf(sk + p.eps) : 1.f;
         const float iqs = (p.l2norm ? __builtin_amdgcn_rsqf(sq + p.eps) : 1.f) * p.scale;
 #pragma unroll
