@@ -10,6 +10,12 @@ have), so no step finds the previous step's states in the last-level cache.
 Prints one JSON line: tokens/s, us per layer, achieved HBM bandwidth of the
 kernel against the 8 TB/s MI355X peak, and the CPU oracle timed on a bounded
 sample of the same workload (one thread, then all the host's threads).
+Each timed region starts behind a short GPU spin queued after the
+synchronisation: the host launches the first steps while the GPU spins, so
+the region holds the steps' GPU time and not the host's latency to launch
+the first one onto an idle stream (on a 20-step region that latency adds
+about 1.5 us to every step).  The same steps timed from an idle stream are
+reported beside it.
 Beside the headline mean over the timed region: the median, p10 and p90 of
 one series of the same steps (an event between consecutive calls), a
 labelled "hot" series (one layer back to back), and a measured same-GPU
@@ -37,6 +43,9 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_gdn_rows_qwen3next_k3_
 
 
 DEFAULT_WORKLOAD = "qwen3next_k3_b64"
+# Spin queued ahead of a timed region's first event (GPU clock cycles; about
+# 0.4 ms at 2.4 GHz, far longer than the host needs to launch one step).
+LEAD_CYCLES = 1_000_000
 
 
 def algorithmic_bytes(case) -> int:
@@ -255,6 +264,32 @@ def state_fanout_ceiling(case, layers, meta, stream, steps, achieved_gbs):
             "frac_of_peak": gbs / HBM_PEAK_GBS, "frac_of_ceiling": achieved_gbs / gbs}
 
 
+def lead(stream):
+    """Queue a GPU spin on ``stream`` ahead of a timed region's first event,
+    so that the host has launched the region's first steps by the time the
+    spin ends and the events see no launch gap."""
+    import torch
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(LEAD_CYCLES)
+
+
+def time_region(fn, n, stream, start=0, led=True):
+    """Mean time per call of ``n`` calls back to back, bracketed by one pair
+    of events and synchronised on both sides."""
+    import torch
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    if led:
+        lead(stream)
+    t_begin.record(stream)
+    for i in range(n):
+        fn(start + i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    return t_begin.elapsed_time(t_end) / n
+
+
 def time_series(fn, n, stream, start=0, block=8):
     """n calls back to back in blocks of ``block`` calls with one event
     between consecutive blocks: each sample is a block's time per call (the
@@ -264,6 +299,8 @@ def time_series(fn, n, stream, start=0, block=8):
     import torch
     nb = max(n // block, 1)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+    torch.cuda.synchronize()
+    lead(stream)
     ev[0].record(stream)
     for i in range(nb):
         for j in range(block):
@@ -409,16 +446,12 @@ def main():
         def step(i):  # noqa: F811 (the timed step replays the layer's graph)
             graphs[i % len(graphs)].replay()
         del eager_step
-    # Timed region: exactly `steps` layer steps, synchronised on both sides.
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_begin.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_begin.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
+    # Timed region: exactly `steps` layer steps, synchronised on both sides,
+    # behind the lead spin.
+    ms_per_step = time_region(step, args.steps, stream, start=args.warmup)
+    # The same steps from an idle stream (no lead): the host's latency to
+    # launch the first step counted in.
+    idle_ms = time_region(step, args.steps, stream, start=args.warmup, led=False)
     # The same steps again with an event after every block of `layers` calls
     # (layers cycled: cold states): median, p10 and p90 of one series.
     cold = time_series(step, args.steps, stream, start=args.warmup, block=args.layers)
@@ -462,6 +495,7 @@ def main():
                      "kernel": "gdn_rows_kernel (dk=dv=128)",
                      "algorithmic_bytes_per_launch": nbytes,
                      "avg_launch_us": avg_launch_s * 1e6,
+                     "idle_start_us": idle_ms * 1e3,
                      "series_us": cold, "hot_series_us": hot},
     }
     if ns is None:
