@@ -61,6 +61,12 @@ struct RowArgs {
   // G > 1) runs one workgroup per (row, v-head), and the last of a k-head's
   // G workgroups to read the shared q/k ring channels rolls them.
   unsigned int* turns;
+  // Dynamic tail of a (row, v-head) launch (tail_units 0: none).  The grid
+  // covers units [0, tail_first) one per workgroup; its last tail_takers
+  // workgroups then claim units tail_first + c, c = 0 .. tail_units-1, from
+  // a wrapping count in turns[0] (the cell of the NULL conv slot, which the
+  // turn protocol never uses) until a claim comes back past the tail.
+  int tail_units = 0, tail_takers = 0, tail_first = 0;
   // A second set of rows in the same launch (none when num_rows is 0): its
   // rows follow the first set's in the grid, with their own kind and metadata.
   struct RowSet {

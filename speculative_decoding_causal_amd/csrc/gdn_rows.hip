@@ -9,16 +9,23 @@
 //
 // With turn counters (RowArgs::turns) the fused step of a launch with one
 // row set runs one workgroup per (row, v-head) instead (dk = dv = 128,
-// G > 1): half the state per workgroup at G = 2, twice the workgroups.  The G workgroups of a k-head each read and convolve the
-// shared q and k channels; each rolls its own v channels, and the q/k
-// channels are rolled by the last of the G to have consumed its window.
-// Each of the 2*dk/64 waves that hold q/k channels, once its loads of them
-// have returned, steps its counter of (conv slot, k-head, wave) with a
-// wrapping increment (0, 1, .., G-1, 0); the wave that finds G-1 is the
-// last reader of those 64 channels and rewrites them at its end.  Every
-// row steps a counter 0 or G times, so the counters are back at 0 after
-// every call (graph replays included), and no workgroup ever waits for
-// another.
+// G > 1): half the state per workgroup at G = 2, twice the workgroups.  The
+// G workgroups of a k-head each read and convolve the shared q and k
+// channels; each rolls its own v channels, and the q/k channels are rolled
+// by the last of the G to have consumed its window.  Each of the 2*dk/64
+// waves that hold q/k channels, once its loads of them have returned, steps
+// its counter of (conv slot, k-head, wave) with a wrapping increment (0, 1,
+// .., G-1, 0); the wave that finds G-1 is the last reader of those 64
+// channels and rewrites them at its end.  Every row steps a counter 0 or G
+// times, so the counters are back at 0 after every call (graph replays
+// included), and no workgroup ever waits for another.
+//
+// When such a launch runs one workgroup per CU, its last units form a
+// dynamic tail: the last workgroup of each CU claims them one at a time
+// from a wrapping count in the counter cell of the NULL conv slot (slot 0,
+// which the turns never use), so the CUs of a faster XCD take more of them.
+// (On MI355X one XCD's workgroups can take up to 10% longer than another's
+// for the same work, and the same XCDs are the slower ones from run to run.)
 //
 // Phases:
 //   1. conv: stage the ring columns and the row's inputs (gathered through
@@ -60,14 +67,23 @@ struct RowPlan {
   const int* save; // per-token conv slots (spec rows, per-token layout), else null
 };
 
+// Read-only inputs that no kernel of the step writes (metadata, A_log,
+// dt_bias), read through the constant address space: a uniform address then
+// takes a scalar load even after the unit's own stores (a workgroup that
+// goes on to a claimed unit reads its metadata after storing states).
+template <class T>
+__device__ __forceinline__ T ldc(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
 __device__ __forceinline__ int slot_or_null(int s, int num_slots) {
   return (s > 0 && s < num_slots) ? s : 0;
 }
 
 __device__ RowPlan plan_row(const RowArgs& p, int row) {
   RowPlan r;
-  int j0 = clampi(p.qsl[row], 0, p.num_tokens);
-  int j1 = clampi(p.qsl[row + 1], j0, p.num_tokens);
+  int j0 = clampi(ldc(p.qsl + row), 0, p.num_tokens);
+  int j1 = clampi(ldc(p.qsl + row + 1), j0, p.num_tokens);
   r.j0 = j0;
   r.T = min(j1 - j0, p.max_row_tokens);
   const int L = p.L, W = p.W;
@@ -77,7 +93,7 @@ __device__ RowPlan plan_row(const RowArgs& p, int row) {
     // saved after every token to that token's slot
     const int* ssi = p.ssi + (size_t)row * p.row_stride;
     const int T = r.T > 0 ? r.T : 1;
-    r.load_slot = slot_or_null(ssi[clampi(p.nacc[row], 1, T) - 1], p.num_slots);
+    r.load_slot = slot_or_null(ldc(ssi + clampi(ldc(p.nacc + row), 1, T) - 1), p.num_slots);
     r.conv_slot = r.load_slot;
     r.read_hist = true;
     r.off = 0;
@@ -88,16 +104,16 @@ __device__ RowPlan plan_row(const RowArgs& p, int row) {
     int T = r.T > 0 ? r.T : 1;
     // n_acc outside [1, min(T, L-W+2)] is a precondition violation; clamp so
     // every access stays inside the slot.
-    const int nacc = p.nacc[row];
+    const int nacc = ldc(p.nacc + row);
     const int n = clampi(nacc, 1, min(T, L - W + 2));
-    r.conv_slot = slot_or_null(p.cache_idx ? p.cache_idx[row] : ssi[0], p.num_slots);
+    r.conv_slot = slot_or_null(p.cache_idx ? ldc(p.cache_idx + row) : ldc(ssi), p.num_slots);
     r.read_hist = true;
     r.off = n - 1;
     r.shift = n;
-    r.load_slot = slot_or_null(ssi[clampi(nacc, 1, T) - 1], p.num_slots);
+    r.load_slot = slot_or_null(ldc(ssi + clampi(nacc, 1, T) - 1), p.num_slots);
   } else {
-    int c = slot_or_null(p.cache_idx[row], p.num_slots);
-    bool init = (p.his ? p.his[row] != 0 : true) && c > 0;
+    int c = slot_or_null(ldc(p.cache_idx + row), p.num_slots);
+    bool init = (p.his ? ldc(p.his + row) != 0 : true) && c > 0;
     r.conv_slot = c;
     r.read_hist = init;
     r.off = L - W + 1;
@@ -190,6 +206,17 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 #endif
 #ifndef GDN_ROWS_VH_MIXED
 #define GDN_ROWS_VH_MIXED 0
+#endif
+// Dynamic tail of (row, v-head) launches that run one workgroup per CU:
+// 1/TAIL_DIV of the units (0: off), at most TAIL_ROUNDS units per CU, taken
+// by the last workgroup of each CU.  Measured on MI355X (one process,
+// alternating): K=3, 64 rows 96.9 us (97.9 without); K=4, 96 rows 175.9
+// (179.0); K=4, 256 rows 459.5 with two units per CU (470.3).
+#ifndef GDN_ROWS_TAIL_DIV
+#define GDN_ROWS_TAIL_DIV 8
+#endif
+#ifndef GDN_ROWS_TAIL_ROUNDS
+#define GDN_ROWS_TAIL_ROUNDS 2
 #endif
 
 // State snapshots go through a buffer resource per (token slot, unit): the
@@ -402,10 +429,14 @@ __device__ __forceinline__ void conv_chan(const float (&w)[kMaxWidth], float bia
 // NT threads per workgroup, R state rows per lane; WPE waves per SIMD is the
 // occupancy the register budget is fitted to.  LM / KT bound state_len and
 // the tokens per row for the register gathers of the conv phase.
+// One unit of the launch: virtual workgroup index vb, mapped to (row, head)
+// as below.  A claim of the dynamic tail, when `post`, is written to *tail_sh
+// by thread 0 before the phase-2 barrier (its result is back by then, the
+// state loads being younger).  Returns whether it got that far.
 template <int DK, int DV, int R, int NT, int WPE, int LM, int KT, int RB, bool FUSED, int ORDER,
           bool VH>
-__global__ void __launch_bounds__(NT, WPE)
-gdn_rows_kernel(RowArgs pa) {
+__device__ __forceinline__ bool rows_unit(const RowArgs& pa, const int vb, const bool post,
+                                          const unsigned int claim, unsigned int* tail_sh) {
   static_assert(R % RB == 0, "row batch");
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int LPR = DK / 16;    // lanes per state row
@@ -422,12 +453,12 @@ gdn_rows_kernel(RowArgs pa) {
   // Workgroup i runs on XCD i % 8: the units of a row share i % 8, so
   // each XCD's L2 fetches a row's metadata and gate rows once.  The grid is
   // padded to whole groups of 8 rows.
-  const int q8 = blockIdx.x >> 3;
+  const int q8 = vb >> 3;
   const int hu = q8 % NU;
   const int ih = VH ? hu / G : hu;
   const int hv0 = VH ? hu : hu * G;
-  int row = (q8 / NU) * 8 + (blockIdx.x & 7);
-  if (row >= pa.num_rows + (pa.more.num_rows > 0 ? pa.more.num_rows : 0)) return;
+  int row = (q8 / NU) * 8 + (vb & 7);
+  if (row >= pa.num_rows + (pa.more.num_rows > 0 ? pa.more.num_rows : 0)) return false;
   const int NCH = 2 * DK + GU * DV;
   const int NR = GU * DV;
   const int Tm = launch_row_tokens(pa);
@@ -450,7 +481,7 @@ gdn_rows_kernel(RowArgs pa) {
 
   const RowPlan rp = plan_row(p, row);
   const int T = rp.T;
-  if (T <= 0) return;
+  if (T <= 0) return false;
 
   const Lds lay = lds_layout(DK, DV, GU, L, Tm);
   int* rows_s = reinterpret_cast<int*>(smem + lay.rows);
@@ -470,7 +501,7 @@ gdn_rows_kernel(RowArgs pa) {
   for (int j = 0; j < KT; ++j) {
     int r = -1;
     if (j < T) {
-      r = p.tix ? p.tix[rp.j0 + j] : rp.j0 + j;
+      r = p.tix ? ldc(p.tix + rp.j0 + j) : rp.j0 + j;
       if (r < 0 || r >= p.num_actual_tokens) r = -1;
     }
     rj[j] = r;
@@ -536,8 +567,8 @@ gdn_rows_kernel(RowArgs pa) {
     // stage, which has no gates), so phase 2 issues no load behind the state
     const float* gsrc_l = stage != kConvOnly ? p.A_log : reinterpret_cast<const float*>(p.conv_w);
     const float* gsrc_d = stage != kConvOnly ? p.dt_bias : gsrc_l;
-    a_log0 = gsrc_l[gh];
-    dt_bias0 = gsrc_d[gh];
+    a_log0 = ldc(gsrc_l + gh);
+    dt_bias0 = ldc(gsrc_d + gh);
     // Every thread loads a channel (threads past the last one repeat it) so
     // that no load waits behind a per-thread branch.
     ChanIn<LM, KT> in0;
@@ -615,7 +646,7 @@ gdn_rows_kernel(RowArgs pa) {
       conv_chan<KT>(w, bias, p, rp, c, pc, NCH, T, zb, dst, dstride, rj, roll);
     }
   }
-  if (stage == kConvOnly) return;
+  if (stage == kConvOnly) return false;
   if constexpr (!kEarlyRows)
     load_rows<DK, R, LPR, SS>(S, load_base, wave_row0 + gl, jl, NR);
 
@@ -634,6 +665,9 @@ gdn_rows_kernel(RowArgs pa) {
   // thread writes (its ring channels, its state rows, an output) is read, if
   // at all, by that same thread, so the barrier orders LDS alone and waits
   // neither for the state loads nor for stores still in flight.
+  if constexpr (VH) {
+    if (post && tid == 0) *tail_sh = claim;
+  }
   lds_barrier();
   // the last of the k-head's G waves to take its turn rolls the shared
   // channels; without a ring slot nothing is read, and the wave of one
@@ -795,6 +829,67 @@ gdn_rows_kernel(RowArgs pa) {
       roll_chan(p, rp, channel_of(pc, ih, hv0, Hk, DK, DV), pc, NCH, T, zb);
     }
   }
+  return true;
+}
+
+// Workgroup i takes unit i.  With a dynamic tail, the last tail_takers
+// workgroups (the last to start on each CU) go on to claim the tail's units
+// one at a time, each claim issued a whole unit ahead of its use, so a CU
+// that finishes early takes more of the tail than one on a slower XCD.  The
+// count wraps at tail_units + tail_takers - 1: every taker claims until its
+// first claim past the tail, so exactly that many claims are made per launch
+// and the count is back at 0 after every launch.
+template <int DK, int DV, int R, int NT, int WPE, int LM, int KT, int RB, bool FUSED, int ORDER,
+          bool VH>
+__global__ void __launch_bounds__(NT, WPE)
+gdn_rows_kernel(RowArgs pa) {
+  if constexpr (VH) {
+    // the claim in hand, double-buffered: a wave still reading one
+    // iteration's entry never meets the next iteration's write
+    __shared__ unsigned int tail_sh[2];
+    const bool taker = pa.tail_units > 0 &&
+                       static_cast<int>(blockIdx.x) >= static_cast<int>(gridDim.x) - pa.tail_takers;
+    if (!taker) {
+      // every workgroup but the takers: one unit, no loop around it
+      rows_unit<DK, DV, R, NT, WPE, LM, KT, RB, FUSED, ORDER, VH>(pa, blockIdx.x, false, 0u, nullptr);
+      return;
+    }
+    const unsigned int wrap = static_cast<unsigned int>(pa.tail_units + pa.tail_takers - 1);
+    unsigned int claim = 0;
+    if (threadIdx.x == 0) claim = atomicInc(pa.turns, wrap);
+#if defined(__HIP_DEVICE_COMPILE__)
+    // the kernel's one explicit argument opens its argument segment
+    typedef const __attribute__((address_space(4))) RowArgs* KArgs;
+    KArgs kp = (KArgs)__builtin_amdgcn_kernarg_segment_ptr();
+#endif
+    int vb = blockIdx.x;
+    for (int it = 0;; ++it) {
+      // each unit reads the arguments afresh (scalar loads of the kernel
+      // argument block): nothing is hoisted across units and kept live
+      // through the loop (the host pass generates no code for this body)
+#if defined(__HIP_DEVICE_COMPILE__)
+      asm volatile("" : "+s"(kp));
+      const RowArgs a = *kp;
+#else
+      const RowArgs& a = pa;
+#endif
+      // the unit is the workgroup's (an SGPR), whatever the compiler makes
+      // of the loop around it
+      vb = __builtin_amdgcn_readfirstlane(vb);
+      const int ib = __builtin_amdgcn_readfirstlane(it) & 1;
+      const bool posted = rows_unit<DK, DV, R, NT, WPE, LM, KT, RB, FUSED, ORDER, VH>(
+          a, vb, true, claim, &tail_sh[ib]);
+      if (!posted && threadIdx.x == 0) tail_sh[ib] = claim;
+      // the claim is visible, and the unit's LDS free for the next one
+      lds_barrier();
+      const unsigned int c = __builtin_amdgcn_readfirstlane(tail_sh[ib]);
+      if (c >= static_cast<unsigned int>(pa.tail_units)) return;
+      vb = pa.tail_first + static_cast<int>(c);
+      if (threadIdx.x == 0) claim = atomicInc(pa.turns, wrap);
+    }
+  } else {
+    rows_unit<DK, DV, R, NT, WPE, LM, KT, RB, FUSED, ORDER, VH>(pa, blockIdx.x, false, 0u, nullptr);
+  }
 }
 
 template <int DK, int DV, int R, int NT, int WPE, int LM, int KT>
@@ -829,7 +924,18 @@ hipError_t launch_typed(const RowArgs& a, hipStream_t s) {
         hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lds);
         if (e != hipSuccess) return e;
       }
-      hipLaunchKernelGGL(kern, dim3(vunits), dim3(NT), lds, s, a);
+      // dynamic tail: the last workgroup of each CU (the grid's last
+      // `takers`) goes on to claim the last `tail` units at run time
+      RowArgs b = a;
+      const unsigned takers = static_cast<unsigned>(cus) & ~7u;
+      unsigned tail = GDN_ROWS_TAIL_DIV > 0 ? vunits / (GDN_ROWS_TAIL_DIV > 0 ? GDN_ROWS_TAIL_DIV : 1) : 0u;
+      tail = (tail < GDN_ROWS_TAIL_ROUNDS * takers ? tail : GDN_ROWS_TAIL_ROUNDS * takers) & ~7u;
+      if (floor && tail > 0 && takers > 0 && vunits - tail >= takers) {
+        b.tail_units = static_cast<int>(tail);
+        b.tail_takers = static_cast<int>(takers);
+        b.tail_first = static_cast<int>(vunits - tail);
+      }
+      hipLaunchKernelGGL(kern, dim3(vunits - static_cast<unsigned>(b.tail_units)), dim3(NT), lds, s, b);
       return hipGetLastError();
     }
   }

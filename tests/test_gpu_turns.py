@@ -4,9 +4,12 @@ workgroups to read the shared q/k conv channels rolling them ("[GDN]
 Spec-decoding-aware attention kernel", "Changes": stage the pre-state, then
 roll), one workgroup per CU for rows of three tokens or more on at least
 eight units per CU (96 rows of 32 v-heads on MI355X's 256 CUs), several per
-CU otherwise.  Compared bit for bit with the (row, k-head) form (no
-counters), which holds one k-head's channels in one workgroup, and with the
-oracle; every counter is back at 0 after every call."""
+CU otherwise.  On grids of at least two units per CU the last eighth of the
+units is claimed at run time by the last workgroup of each CU (a wrapping
+count in the NULL slot's counter cell).  Compared bit for bit with the
+(row, k-head) form (no counters), which holds one k-head's channels in one
+workgroup, and with the oracle; every counter is back at 0 after every
+call."""
 from __future__ import annotations
 
 import dataclasses
@@ -65,6 +68,34 @@ def test_vhead_units_ragged_rows():
     b = Gpu(case, turns=False)
     b.spec()
     _same(a, b)
+
+
+def test_vhead_units_dynamic_tail_padded_rows():
+    # 93 rows: the grid is padded to 96 rows, and the padded units sit in
+    # the dynamically claimed tail (its last units), beside one-token rows
+    # and NULL slots; two chained calls, so the second starts from the
+    # count the first left (it must be back at 0)
+    rng = np.random.default_rng(415)
+    lens = rng.integers(1, 5, 93)
+    lens[0] = 4
+    lens[-3:] = 1
+    case = _k4(415, Ns=93, lens=lens, null_p=0.15)
+    a, b = Gpu(case), Gpu(case, turns=False)
+    for step in range(2):
+        say(f"dynamic tail, 93 ragged rows, call {step}")
+        a.spec()
+        b.spec()
+        _zero_turns(a)
+        _same(a, b)
+    c = helpers.clone(case)
+    for step in range(2):
+        out, conv, ssm, _ = helpers.run_spec(c)
+        c["conv_state"], c["ssm_state"] = conv, ssm
+    sp = case["spec"]
+    glob, slots = spec_rows_of(sp, range(sp["num_spec_decodes"]))
+    assert_out_close(a.host_out(), out, glob)
+    np.testing.assert_array_equal(a.host_conv(slots), conv[slots])
+    assert_states_close(a.host_ssm(slots), ssm[slots])
 
 
 def test_vhead_units_four_vheads_per_khead():
