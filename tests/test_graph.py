@@ -166,6 +166,8 @@ def _run_graph(with_decodes, plan, **pads):
             f"(padded to {padded['ns_pad']}, {ND_PAD})")
         graph.replay()
         torch.cuda.synchronize()
+        if st.g.turns is not None:
+            assert int(st.g.turns.abs().sum().item()) == 0, "turn counters not back at 0"
         eager = Gpu(real)
         if with_decodes:
             eager.attention()
@@ -195,12 +197,21 @@ def test_graph_padded_spec_replays():
 
 
 def test_graph_vhead_units_replays():
-    # padded to 104 spec rows of four tokens and 32 v-heads (plus the
-    # decodes) the captured step runs one workgroup per (row, v-head) with
-    # turn counters, replay after replay; the eager calls on the smaller real
-    # batches run the (row, k-head) form, so the two forms are compared bit
-    # for bit as well as with the oracle
+    # padded to 104 spec rows of four tokens and 32 v-heads plus the decodes:
+    # a launch that carries both runs one workgroup per (row, k-head), with
+    # the turn counters passed and left untouched, replay after replay
     _run_graph(True, [(350, 104, 6), (351, 40, 3), (352, 104, 0), (353, 0, 6), (354, 77, 5)],
+               ns_pad=104, num_slots=500, k=4, heads=(16, 32))
+
+
+def test_graph_vhead_tail_replays():
+    # spec rows alone, padded to 104 rows of four tokens and 32 v-heads: the
+    # captured step runs one workgroup per (row, v-head) and per CU, its last
+    # units claimed at run time through the turn array's NULL-slot cell, so
+    # every replay must find that count back at 0; the eager calls on the
+    # real batches take the same form with a tail (104 and 77 rows) or
+    # several workgroups per CU and no tail (40 rows, 8 rows)
+    _run_graph(False, [(360, 104, 0), (361, 40, 0), (362, 104, 0), (363, 8, 0), (364, 77, 0)],
                ns_pad=104, num_slots=500, k=4, heads=(16, 32))
 
 
