@@ -182,7 +182,7 @@ typedef struct gdn_dims {
  * the shared q/k conv channels, and the last of them to have read its
  * window (told by a wrapping count, 0 .. G-1, per 64 channels) rolls them.
  * The first counter (slot 0, which names no ring) also counts, in large
- * launches (rows of three or more tokens, eight or more (row, v-head) units
+ * launches (rows of two or more tokens, four or more (row, v-head) units
  * per CU), the units handed out at run time to the CUs that finish first.
  * Every call leaves every counter at 0,
  * metadata that violates the preconditions included.  The results are the

@@ -186,9 +186,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 #define GDN_ROWS_LDS_MIN128 (80 * 1024 + 16)
 #endif
 // (row, v-head) units: state rows per lane (one pass over dv rows), waves
-// per SIMD, when the one-per-CU floor applies (rows of at least
-// VH_FLOOR_TOKENS tokens on at least VH_FLOOR_UNITS units per CU; shorter
-// rows and smaller grids run faster with several workgroups per CU), and
+// per SIMD, when the one-per-CU floor (and with it the dynamic tail)
+// applies (rows of at least VH_FLOOR_TOKENS tokens on at least
+// VH_FLOOR_UNITS units per CU; one-token rows and smaller grids run faster
+// with several workgroups per CU), and
 // whether launches that carry decodes and spec rows together take them
 // (VH_MIXED: the one-token decodes repeat the q/k conv per v-head for a
 // single state update, and such a launch measured faster per k-head).
@@ -199,10 +200,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 #define GDN_ROWS_WPE_VH128 4
 #endif
 #ifndef GDN_ROWS_VH_FLOOR_TOKENS
-#define GDN_ROWS_VH_FLOOR_TOKENS 3
+#define GDN_ROWS_VH_FLOOR_TOKENS 2
 #endif
 #ifndef GDN_ROWS_VH_FLOOR_UNITS
-#define GDN_ROWS_VH_FLOOR_UNITS 8
+#define GDN_ROWS_VH_FLOOR_UNITS 4
 #endif
 #ifndef GDN_ROWS_VH_MIXED
 #define GDN_ROWS_VH_MIXED 0
@@ -904,13 +905,12 @@ hipError_t launch_typed(const RowArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   // (row, v-head) units whenever the caller passes turn counters (one row
-  // set per launch): one workgroup per CU for rows of three tokens or more
-  // on grids of at least eight units per CU, several per CU otherwise.
-  // Measured on MI355X (one process, alternating, Qwen3-Next heads; the
-  // (row, k-head) form in brackets): K=3, 64 rows 99.3-101.2 us (102.0);
-  // K=4, 96 rows 181 (185); K=4, 256 rows 470-476 (472); K=2, 64 rows 76.8
-  // (78.5 at one per CU); one token, 256 rows 177 (205).  At 32 rows of
-  // K=3 (four units per CU) both forms take 54 us.
+  // set per launch): one workgroup per CU, with the dynamic tail, for rows
+  // of two tokens or more on grids of at least four units per CU, several
+  // per CU otherwise.  Measured on MI355X (one process, alternating,
+  // Qwen3-Next heads; several per CU, no tail, in brackets): K=3, 48 rows
+  // 75.9 us (78.8); K=2, 64 rows 74.9 (77.1); K=2, 128 rows 141.3 (144.9);
+  // K=3, 32 rows 53.9 (53.8); one token, 256 rows 202.4 (177.1).
   if constexpr (DK == 128 && DV == 128) {
     const unsigned vunits = rows8 * static_cast<unsigned>(a.Hv);
     if (a.turns && a.G > 1 && a.stage == kFused && (GDN_ROWS_VH_MIXED || a.more.num_rows == 0)) {

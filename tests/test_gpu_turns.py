@@ -2,8 +2,8 @@
 launches of one row set (spec rows, or decodes), the last of a k-head's
 workgroups to read the shared q/k conv channels rolling them ("[GDN]
 Spec-decoding-aware attention kernel", "Changes": stage the pre-state, then
-roll), one workgroup per CU for rows of three tokens or more on at least
-eight units per CU (96 rows of 32 v-heads on MI355X's 256 CUs), several per
+roll), one workgroup per CU for rows of two tokens or more on at least
+four units per CU (32 rows of 32 v-heads on MI355X's 256 CUs), several per
 CU otherwise.  On grids of at least two units per CU the last eighth of the
 units is claimed at run time by the last workgroup of each CU (a wrapping
 count in the NULL slot's counter cell).  Compared bit for bit with the

@@ -209,8 +209,8 @@ def test_graph_vhead_tail_replays():
     # captured step runs one workgroup per (row, v-head) and per CU, its last
     # units claimed at run time through the turn array's NULL-slot cell, so
     # every replay must find that count back at 0; the eager calls on the
-    # real batches take the same form with a tail (104 and 77 rows) or
-    # several workgroups per CU and no tail (40 rows, 8 rows)
+    # real batches take the same form with a tail (104, 77 and 40 rows) or
+    # several workgroups per CU and no tail (8 rows)
     _run_graph(False, [(360, 104, 0), (361, 40, 0), (362, 104, 0), (363, 8, 0), (364, 77, 0)],
                ns_pad=104, num_slots=500, k=4, heads=(16, 32))
 
