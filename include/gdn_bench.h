@@ -32,7 +32,11 @@ extern "C" {
  * XCD, one workgroup per CU; each wave instruction moves 1 KiB of
  * consecutive bytes with non-temporal loads and stores (measured on MI355X
  * the fastest of the layouts tried for this traffic: 95.6 us at K=3,
- * batch 64, against 103.4 us with 128 KiB (row, k-head) blocks).  Supports
+ * batch 64, against 103.4 us with 128 KiB (row, k-head) blocks).  On grids
+ * of at least two units per CU the last eighth of the units (at most two
+ * per CU) is claimed at run time by the last workgroup of each CU, as in
+ * the row kernel, from a wrapping count in the library's own device memory
+ * (0 again after every call; calls on one GPU must be ordered).  Supports
  * dv*dk == 16384 (dk = dv = 128).  num_k_heads only checks the shape.
  * Slots, n_acc and T_b are clamped to stay inside the pool.  Returns 0, -1
  * for an unsupported shape or NULL pointer, -7 when the launch fails.
